@@ -1,0 +1,333 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each ``pin_*`` takes an :class:`oracle.oracle.Oracle` and raises AssertionError when the
+oracle disagrees with what the mathematics or a hand derivation fixes:
+  * hand-derived reduction-order values (tests/golden/tree_order.json);
+  * a dense float64 brute force of the gated delta rule (norm-wise relative error 1e-5);
+  * exact closed forms with one-hot keys and queries, a in {1, 1/2}, b in {0, 1};
+  * invariants: b=0 and a=1 leave S unchanged; unit k with b=1 makes S k = v;
+  * an exact-rational binary32 emulator of the stated operation order (bitwise);
+  * structural identities of the three cases (resume, chunk states, decode, packing).
+The same pins run against deliberately broken builds of the oracle (test_oracle_mutants),
+which must each fail at least one of them.
+"""
+
+import json
+import os
+
+import numpy as np
+
+import brute_f64
+import exact_fp32
+from bitwise_consistent_linear_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+REL_TOL_F64 = 1e-5
+
+
+def _bits(x):
+    return np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+
+
+def same_bits(x, y) -> bool:
+    x, y = np.asarray(x, np.float32), np.asarray(y, np.float32)
+    return x.shape == y.shape and np.array_equal(_bits(x), _bits(y))
+
+
+def _hexf(h):
+    return np.uint32(int(h, 16)).view(np.float32)
+
+
+def _vec(spec, d):
+    if spec == "ones":
+        return np.ones(d, np.float32)
+    if spec == "zeros":
+        return np.zeros(d, np.float32)
+    if isinstance(spec, str) and spec.startswith("all "):
+        return np.full(d, _hexf(spec[4:]), np.float32)
+    out = np.zeros(d, np.float32)
+    for i, h in spec.items():
+        out[int(i)] = _hexf(h)
+    return out
+
+
+def _normwise(err_num, ref):
+    den = np.abs(ref).max()
+    return np.abs(err_num).max() / (den if den > 0 else 1.0)
+
+
+def _check_f64(o, cs, fs, o64, cs64, fs64, cu, label):
+    N = len(cu) - 1
+    Hv = o.shape[1]
+    for n in range(N):
+        sl = slice(int(cu[n]), int(cu[n + 1]))
+        for h in range(Hv):
+            if sl.stop > sl.start:
+                e = _normwise(o[sl, h] - o64[sl, h], o64[sl, h])
+                assert e <= REL_TOL_F64, f"{label}: o rel err {e:.3g} at n={n} h={h}"
+            e = _normwise(fs[n, h] - fs64[n, h], fs64[n, h])
+            assert e <= REL_TOL_F64, f"{label}: final state rel err {e:.3g} at n={n} h={h}"
+    assert cs.shape == cs64.shape, f"{label}: chunk state count {cs.shape} vs {cs64.shape}"
+    for c in range(cs.shape[0]):
+        e = _normwise(cs[c] - cs64[c], cs64[c])
+        assert e <= REL_TOL_F64, f"{label}: chunk state {c} rel err {e:.3g}"
+
+
+def small_case(seed, lengths, Hk, Hv, d, chunk, bf16=False, a_lo=0.9, with_s0=False):
+    w = W.make_packed(f"small{seed}", lengths, Hk=Hk, Hv=Hv, d=d, chunk=chunk, bf16=bf16,
+                      seed=1000 + seed, a_lo=a_lo)
+    s0 = None
+    if with_s0:
+        g = np.random.default_rng(2000 + seed)
+        s0 = (0.1 * g.standard_normal((w.num_seqs, Hv, d, d))).astype(np.float32)
+    return w, s0
+
+
+# ------------------------------------------------------------------------------ pins
+
+def pin_tree_golden(orc):
+    with open(os.path.join(GOLDEN, "tree_order.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        x, y = _vec(c["x"], c["d"]), _vec(c["y"], c["d"])
+        got = orc.dot(x, y)
+        want = _hexf(c["expect"])
+        assert same_bits(got, want), f"{c['name']}: got {got!r} want {want!r}"
+
+
+def pin_dot_exact_emulator(orc):
+    g = np.random.default_rng(11)
+    for d in (16, 32, 64, 128):
+        for _ in range(25):
+            x = g.standard_normal(d).astype(np.float32) * np.float32(g.uniform(1e-3, 1e3))
+            y = g.standard_normal(d).astype(np.float32)
+            want = exact_fp32.dot([float(v) for v in x], [float(v) for v in y])
+            got = orc.dot(x, y)
+            assert same_bits(got, np.float32(want)), f"dot d={d}: {got!r} vs {want!r}"
+
+
+def pin_tiny_vs_f64(orc):
+    w = W.tiny()
+    o, cs, fs = orc.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=w.chunk,
+                         want_chunk_states=True, want_final_state=True)
+    o64, cs64, fs64 = brute_f64.scan_f64(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, w.chunk)
+    _check_f64(o, cs, fs, o64, cs64, fs64, w.cu_seqlens, "tiny")
+
+
+def pin_shapes_vs_f64(orc):
+    cases = [
+        dict(seed=1, lengths=[5, 0, 37, 16], Hk=1, Hv=2, d=16, chunk=16),
+        dict(seed=2, lengths=[23, 40], Hk=2, Hv=4, d=32, chunk=8, bf16=True),
+        dict(seed=3, lengths=[33], Hk=2, Hv=2, d=64, chunk=16, with_s0=True),
+        dict(seed=4, lengths=[7, 9, 18], Hk=1, Hv=4, d=16, chunk=4, bf16=True, with_s0=True),
+    ]
+    for c in cases:
+        w, s0 = small_case(**c)
+        o, cs, fs = orc.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=w.chunk,
+                             initial_state=s0, want_chunk_states=True, want_final_state=True)
+        o64, cs64, fs64 = brute_f64.scan_f64(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, w.chunk, s0)
+        _check_f64(o, cs, fs, o64, cs64, fs64, w.cu_seqlens, f"case{c['seed']}")
+
+
+def onehot_case(T=12, Hk=2, Hv=4, d=16, seed=5):
+    g = np.random.default_rng(seed)
+    kap = g.integers(0, d, (T, Hk))
+    rho = g.integers(0, d, (T, Hk))
+    q = np.zeros((T, Hk, d), np.float32)
+    k = np.zeros((T, Hk, d), np.float32)
+    for t in range(T):
+        for j in range(Hk):
+            k[t, j, kap[t, j]] = 1.0
+            q[t, j, rho[t, j]] = 1.0
+    v = g.integers(-8, 9, (T, Hv, d)).astype(np.float32)
+    a = g.choice(np.float32([1.0, 0.5]), (T, Hv))
+    b = g.choice(np.float32([0.0, 1.0]), (T, Hv))
+    s0 = g.integers(-4, 5, (1, Hv, d, d)).astype(np.float32)
+    return np.array([0, T], np.int32), q, k, v, a, b, s0, kap, rho
+
+
+def pin_onehot_closed_form(orc):
+    cu, q, k, v, a, b, s0, kap, rho = onehot_case()
+    T, Hk, d = k.shape
+    Hv = v.shape[1]
+    G = Hv // Hk
+    o, cs, fs = orc.scan(cu, q, k, v, a, b, chunk=4, initial_state=s0,
+                         want_chunk_states=True, want_final_state=True)
+    # closed form: column kappa of S becomes b*v + (1-b)*a*S[:, kappa]; other columns a*S
+    S = s0[0].astype(np.float64).copy()
+    for t in range(T):
+        for h in range(Hv):
+            kc, rc = kap[t, h // G], rho[t, h // G]
+            S[h] *= float(a[t, h])
+            if b[t, h] == 1.0:
+                S[h][:, kc] = v[t, h]
+            want_o = S[h][:, rc]
+            assert np.array_equal(o[t, h].astype(np.float64), want_o), f"onehot o t={t} h={h}"
+        if (t + 1) % 4 == 0:
+            assert np.array_equal(cs[(t + 1) // 4 - 1].astype(np.float64), S), f"onehot chunk t={t}"
+    assert np.array_equal(fs[0].astype(np.float64), S), "onehot final state"
+
+
+def pin_b0_a1_identity(orc):
+    w, _ = small_case(6, [20], Hk=2, Hv=2, d=32, chunk=4)
+    g = np.random.default_rng(6)
+    s0 = g.standard_normal((1, 2, 32, 32)).astype(np.float32)
+    a = np.ones_like(w.a)
+    b = np.zeros_like(w.b)
+    o, cs, fs = orc.scan(w.cu_seqlens, w.q, w.k, w.v, a, b, chunk=4, initial_state=s0,
+                         want_chunk_states=True, want_final_state=True)
+    assert np.array_equal(fs, s0), "b=0, a=1 must leave the state unchanged"
+    assert all(np.array_equal(cs[c], s0[0]) for c in range(cs.shape[0])), "chunk states changed"
+    for t in range(20):
+        for h in range(2):
+            for i in range(32):
+                want = exact_fp32.dot([float(x) for x in s0[0, h, i]],
+                                      [float(x) for x in w.q[t, h]])
+                assert same_bits(o[t, h, i], np.float32(want)), f"readout t={t} h={h} i={i}"
+
+
+def pin_unit_k_overwrite(orc):
+    # random unit k, b = 1: after every token S_t k_t = v_t up to rounding
+    w, s0 = small_case(7, [16], Hk=1, Hv=2, d=64, chunk=16, with_s0=True)
+    b = np.ones_like(w.b)
+    k = w.k.astype(np.float64)
+    for T in range(1, 17):
+        cu = np.array([0, T], np.int32)
+        _, _, fs = orc.scan(cu, w.q[:T], w.k[:T], w.v[:T], w.a[:T], b[:T], chunk=16,
+                            initial_state=s0, want_o=False, want_final_state=True)
+        for h in range(2):
+            sk = fs[0, h].astype(np.float64) @ k[T - 1, 0]
+            vt = w.v[T - 1, h].astype(np.float64)
+            err = np.abs(sk - vt).max() / np.abs(vt).max()
+            assert err <= 64 * 2.0 ** -22, f"unit k overwrite T={T} h={h}: rel {err:.3g}"
+
+
+def pin_exact_emulator_tiny(orc):
+    w = W.tiny()
+    T = 24
+    cu = np.array([0, T], np.int32)
+    o, _, fs = orc.scan(cu, w.q[:T], w.k[:T], w.v[:T], w.a[:T], w.b[:T], chunk=16,
+                        want_final_state=True)
+    for h in range(w.num_v_heads):
+        for i in range(0, w.d_v, 3):
+            s = [0.0] * w.d_k
+            for t in range(T):
+                s, oi = exact_fp32.token(s, float(w.a[t, h]), float(w.b[t, h]),
+                                         float(w.v[t, h, i]), [float(x) for x in w.k[t, h]],
+                                         [float(x) for x in w.q[t, h]])
+                assert same_bits(o[t, h, i], np.float32(oi)), f"emulator o t={t} h={h} i={i}"
+            assert same_bits(fs[0, h, i], np.float32(s)), f"emulator state h={h} i={i}"
+
+
+def pin_chunk_invariance(orc):
+    w, s0 = small_case(8, [70, 33], Hk=1, Hv=2, d=16, chunk=16, with_s0=True)
+    ref = None
+    for C in (1, 4, 16, 64):
+        o, _, fs = orc.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=C, initial_state=s0,
+                            want_final_state=True)
+        if ref is None:
+            ref = (o, fs)
+        assert same_bits(o, ref[0]) and same_bits(fs, ref[1]), f"C={C} changed o or state"
+
+
+def pin_split_resume(orc):
+    w, s0 = small_case(9, [50], Hk=2, Hv=2, d=32, chunk=8, bf16=True, with_s0=True)
+    o, _, fs = orc.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=8, initial_state=s0,
+                        want_final_state=True)
+    for m in (1, 8, 21, 49):
+        c1 = np.array([0, m], np.int32)
+        c2 = np.array([0, 50 - m], np.int32)
+        o1, _, f1 = orc.scan(c1, w.q[:m], w.k[:m], w.v[:m], w.a[:m], w.b[:m], chunk=8,
+                             initial_state=s0, want_final_state=True)
+        o2, _, f2 = orc.scan(c2, w.q[m:], w.k[m:], w.v[m:], w.a[m:], w.b[m:], chunk=8,
+                             initial_state=f1, want_final_state=True)
+        assert same_bits(np.concatenate([o1, o2]), o), f"split at {m}: o differs"
+        assert same_bits(f2, fs), f"split at {m}: state differs"
+
+
+def pin_chunk_states_are_prefix_finals(orc):
+    w, s0 = small_case(10, [37, 16, 3], Hk=1, Hv=2, d=16, chunk=8, with_s0=True)
+    _, cs, _ = orc.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=8, initial_state=s0,
+                        want_o=False, want_chunk_states=True)
+    c = 0
+    for n, L in enumerate(w.lengths):
+        bos = int(w.cu_seqlens[n])
+        for j in range(8, int(L) + 1, 8):
+            cu = np.array([0, j], np.int32)
+            sl = slice(bos, bos + j)
+            _, _, f = orc.scan(cu, w.q[sl], w.k[sl], w.v[sl], w.a[sl], w.b[sl], chunk=8,
+                               initial_state=s0[n:n + 1], want_o=False, want_final_state=True)
+            assert same_bits(cs[c], f[0]), f"chunk state {c} (n={n}, j={j})"
+            c += 1
+    assert c == cs.shape[0]
+
+
+def pin_decode_equals_scan(orc):
+    w, s0 = small_case(12, [40, 40, 40], Hk=2, Hv=4, d=32, chunk=8, bf16=True, with_s0=True)
+    o, cs, fs = orc.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=8, initial_state=s0,
+                         want_chunk_states=True, want_final_state=True)
+    pre, steps = W.split_for_decode(w, 13)
+    _, _, state = orc.scan(pre.cu_seqlens, pre.q, pre.k, pre.v, pre.a, pre.b, chunk=8,
+                           initial_state=s0, want_o=False, want_final_state=True)
+    o_seq = o.reshape(3, 40, 4, 32)
+    cs_seq = cs.reshape(3, 5, 4, 32, 32)
+    for s in range(27):
+        od, rs = orc.decode_step(steps["pos"][s], steps["q"][s], steps["k"][s], steps["v"][s],
+                                 steps["a"][s], steps["b"][s], state, chunk=8)
+        assert same_bits(od, o_seq[:, 13 + s]), f"decode o at step {s}"
+        if (13 + s + 1) % 8 == 0:
+            assert same_bits(rs, cs_seq[:, (13 + s + 1) // 8 - 1]), f"resync at step {s}"
+        else:
+            assert not rs.any(), f"resync written off-boundary at step {s}"
+    assert same_bits(state, fs), "decode end state"
+
+
+def pin_permutation(orc):
+    w, s0 = small_case(13, [9, 30, 17, 1], Hk=1, Hv=2, d=16, chunk=4, with_s0=True)
+    o, cs, fs = orc.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=4, initial_state=s0,
+                         want_chunk_states=True, want_final_state=True)
+    perm = [2, 0, 3, 1]
+    L = w.lengths
+    idx = np.concatenate([np.arange(w.cu_seqlens[n], w.cu_seqlens[n + 1]) for n in perm])
+    cu2 = np.concatenate([[0], np.cumsum(L[perm])]).astype(np.int32)
+    o2, cs2, fs2 = orc.scan(cu2, w.q[idx], w.k[idx], w.v[idx], w.a[idx], w.b[idx], chunk=4,
+                            initial_state=s0[perm], want_chunk_states=True,
+                            want_final_state=True)
+    assert same_bits(o2, o[idx]), "permuted pack: o"
+    assert same_bits(fs2, fs[perm]), "permuted pack: final states"
+    coff = np.concatenate([[0], np.cumsum(L // 4)])
+    cidx = np.concatenate([np.arange(coff[n], coff[n + 1]) for n in perm]).astype(int)
+    assert same_bits(cs2, cs[cidx]), "permuted pack: chunk states"
+
+
+def pin_pairs_equals_full(orc):
+    w, s0 = small_case(14, [19, 45], Hk=2, Hv=4, d=32, chunk=8, bf16=True, with_s0=True)
+    o, cs, fs = orc.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=8, initial_state=s0,
+                         want_chunk_states=True, want_final_state=True)
+    pairs = [(1, 3), (0, 0), (1, 1)]
+    res = orc.scan_pairs(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, pairs, chunk=8,
+                         initial_state=s0)
+    coff = np.concatenate([[0], np.cumsum(w.lengths // 8)])
+    for (n, h), r in zip(pairs, res):
+        sl = slice(int(w.cu_seqlens[n]), int(w.cu_seqlens[n + 1]))
+        assert same_bits(r["o"], o[sl, h]), f"pair ({n},{h}) o"
+        assert same_bits(r["chunk_states"], cs[coff[n]:coff[n + 1], h]), f"pair ({n},{h}) chunks"
+        assert same_bits(r["final_state"], fs[n, h]), f"pair ({n},{h}) final"
+
+
+def pin_idle_slot(orc):
+    w, s0 = small_case(15, [4, 4], Hk=1, Hv=2, d=16, chunk=4, with_s0=True)
+    state = s0.copy()
+    pos = np.array([-1, 3], np.int32)
+    q = w.q.reshape(2, 4, 1, 16)[:, 0]
+    k = w.k.reshape(2, 4, 1, 16)[:, 0]
+    v = w.v.reshape(2, 4, 2, 16)[:, 0]
+    a = w.a.reshape(2, 4, 2)[:, 0]
+    b = w.b.reshape(2, 4, 2)[:, 0]
+    o, rs = orc.decode_step(pos, q, k, v, a, b, state, chunk=4)
+    assert same_bits(state[0], s0[0]), "idle slot state changed"
+    assert not o[0].any() and not rs[0].any(), "idle slot wrote outputs"
+    assert not same_bits(state[1], s0[1]) and same_bits(rs[1], state[1]), "active slot resync"
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

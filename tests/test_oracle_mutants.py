@@ -1,0 +1,73 @@
+"""Planted mistakes in the CPU oracle must be caught by its pins.
+
+Each mutant is a copy of oracle/gdn_oracle.c with one plausible mistake (a dropped term, a
+wrong sign, a swapped operand or index, another reduction order), built with gcc into a
+temporary directory. Every mutant must fail at least one pin in tests/oracle_pins.py; a
+mutant that passes them all would mean the pins cannot tell that mistake from the contract.
+Mutations only change arithmetic or in-bounds indices, so no mutant writes out of bounds.
+"""
+
+import os
+
+import pytest
+
+import oracle_pins
+from oracle import oracle as O
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
+                   "gdn_oracle.c")
+
+MUTANTS = {
+    "decay_dropped": [("x[e] = a * s[e];", "x[e] = s[e];")],
+    "delta_sign_flipped": [("float diff = v_i - u;", "float diff = u - v_i;")],
+    "beta_dropped": [("float delta = b * diff;", "float delta = diff;")],
+    "readout_before_update": [("return contract_dot(s, q, dk);", "return contract_dot(x, q, dk);")],
+    "key_dot_uses_query": [("float u = contract_dot(x, k, dk);", "float u = contract_dot(x, q, dk);")],
+    "decay_folded_into_dot": [("float u = contract_dot(x, k, dk);",
+                               "float u = a * contract_dot(s, k, dk);")],
+    "update_from_undecayed_state": [("s[e] = fmaf(delta, k[e], x[e]);",
+                                     "s[e] = fmaf(delta, k[e], s[e]);")],
+    "update_unfused": [("s[e] = fmaf(delta, k[e], x[e]);", "s[e] = delta * k[e] + x[e];")],
+    "gqa_modulo_mapping": [("int hk = h / group;\n  int dk = J->dk;",
+                            "int hk = h % J->Hk;\n  int dk = J->dk;"),
+                           ("      int hk = h / group;", "      int hk = h % Hk;")],
+    "leaf_chain_unfused": [("acc = fmaf(xl[e], yl[e], acc);", "acc = acc + xl[e] * yl[e];")],
+    "leaf_start_fma_from_zero": [("float acc = xl[0] * yl[0];", "float acc = fmaf(xl[0], yl[0], 0.0f);")],
+    "serial_leaf_sum": [("leaf[l] = leaf[l] + leaf[l + width];",
+                         "leaf[0] = leaf[0] + leaf[l + width];")],
+    "strided_leaves": [("const float *xl = x + l * m, *yl = y + l * m;",
+                        "const float *xl = x + l, *yl = y + l;"),
+                       ("float acc = xl[0] * yl[0];", "float acc = xl[0] * yl[0]; (void)xl;"),
+                       ("acc = fmaf(xl[e], yl[e], acc);",
+                        "acc = fmaf(xl[e * ORACLE_LEAVES], yl[e * ORACLE_LEAVES], acc);")],
+    "value_row_reversed": [("(t * J->Hv + h) * (int64_t)J->dv + i, J->dtype)",
+                            "(t * J->Hv + h) * (int64_t)J->dv + (J->dv - 1 - i), J->dtype)")],
+    "initial_state_ignored": [("s[e] = J->S0 ? J->S0[", "s[e] = J->S0 ? 0.0f * J->S0[")],
+    "chunk_states_all_in_slot_0": [("((j + 1) / J->C - 1) * J->cs_stride", "0 * J->cs_stride")],
+    "resync_off_by_one": [("((int64_t)pos[n] + 1) % C == 0", "((int64_t)pos[n]) % C == 0")],
+    "bf16_widening_wrong_half": [("(uint32_t)((const uint16_t *)base)[index] << 16",
+                                  "(uint32_t)((const uint16_t *)base)[index] << 15")],
+}
+
+
+def _apply(src, edits):
+    for old, new in edits:
+        assert old in src, f"mutation anchor not found: {old!r}"
+        src = src.replace(old, new)
+    return src
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = open(SRC).read()
+    mutant_src = tmp_path / f"{name}.c"
+    mutant_src.write_text(_apply(src, MUTANTS[name]))
+    lib = O.build(force=True, src=str(mutant_src), out=str(tmp_path / f"lib{name}.so"))
+    orc = O.Oracle(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
