@@ -1,0 +1,259 @@
+"""ctypes binding of libgdn_cpr.so (the C ABI declared in include/gdn_cpr.h).
+
+Argument marshalling only: the functions check torch tensor dtypes, devices and
+contiguity, allocate outputs that the caller did not pass, and call the C entry point of
+the same name on the current stream. Every step of the recurrence runs in the library's
+HIP kernels; there is no other code path, and a missing library is an error.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from functools import lru_cache
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdn_cpr.so")
+
+GDN_OK, GDN_E_NULL, GDN_E_SHAPE, GDN_E_UNSUPPORTED, GDN_E_IDENTITY, GDN_E_DEVICE = range(6)
+GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
+STATUS_NAMES = {0: "GDN_OK", 1: "GDN_E_NULL", 2: "GDN_E_SHAPE", 3: "GDN_E_UNSUPPORTED",
+                4: "GDN_E_IDENTITY", 5: "GDN_E_DEVICE"}
+
+
+class GdnShape(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_qk_heads", ctypes.c_int32),
+                ("num_v_heads", ctypes.c_int32), ("d_k", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("qkv_dtype", ctypes.c_int32)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.gdn_abi_version.restype = I32
+        L.gdn_abi_version.argtypes = []
+        L.gdn_contract_string.restype = I32
+        L.gdn_contract_string.argtypes = [I32, I32, ctypes.c_char_p, ctypes.c_size_t,
+                                          ctypes.POINTER(ctypes.c_size_t)]
+        L.gdn_sha256.restype = I32
+        L.gdn_sha256.argtypes = [ctypes.c_char_p, ctypes.c_size_t, ctypes.c_char_p]
+        L.gdn_contract_identity.restype = I32
+        L.gdn_contract_identity.argtypes = [I32, I32, ctypes.c_char_p]
+        L.gdn_cpr_trainer_fwd.restype = I32
+        L.gdn_cpr_trainer_fwd.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_char_p, P, I64,
+                                          P, P, P, P, P, P, P, P, I64, P]
+        L.gdn_cpr_prefill.restype = I32
+        L.gdn_cpr_prefill.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_char_p, P, I64,
+                                      P, P, P, P, P, P, P, P, P]
+        L.gdn_cpr_decode_step.restype = I32
+        L.gdn_cpr_decode_step.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_char_p, P,
+                                          P, P, P, P, P, P, P, P, P]
+        L.gdn_last_error.restype = ctypes.c_char_p
+        L.gdn_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        raise GdnError(status, lib().gdn_last_error().decode())
+
+
+def abi_version() -> int:
+    return lib().gdn_abi_version()
+
+
+def contract_string(chunk: int, d_k: int) -> str:
+    n = ctypes.c_size_t(0)
+    st = lib().gdn_contract_string(chunk, d_k, None, 0, ctypes.byref(n))
+    if st not in (GDN_OK, GDN_E_SHAPE):
+        _check(st)
+    buf = ctypes.create_string_buffer(n.value + 1)
+    _check(lib().gdn_contract_string(chunk, d_k, buf, n.value + 1, ctypes.byref(n)))
+    return buf.value.decode()
+
+
+def sha256(data: bytes) -> bytes:
+    out = ctypes.create_string_buffer(32)
+    _check(lib().gdn_sha256(data, len(data), out))
+    return out.raw
+
+
+@lru_cache(maxsize=None)
+def contract_identity(chunk: int, d_k: int) -> bytes:
+    out = ctypes.create_string_buffer(32)
+    _check(lib().gdn_contract_identity(chunk, d_k, out))
+    return out.raw
+
+
+# ------------------------------------------------------------------------ tensor helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need(t, name, dtypes, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+    return t
+
+
+def _qkv(q, k, v):
+    torch = _torch()
+    dt = (torch.float32, torch.bfloat16)
+    _need(q, "q", dt, 3)
+    _need(k, "k", dt, 3)
+    _need(v, "v", dt, 3)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if q.shape != k.shape:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} differ")
+    return GDN_DTYPE_BF16 if q.dtype == torch.bfloat16 else GDN_DTYPE_F32
+
+
+def _shape(N, q, v, chunk, dtype_code):
+    return GdnShape(N, q.shape[1], v.shape[1], q.shape[2], v.shape[2], chunk, dtype_code)
+
+
+def _ab(a, b, T, Hv):
+    torch = _torch()
+    _need(a, "a", (torch.float32,), 2)
+    _need(b, "b", (torch.float32,), 2)
+    if tuple(a.shape) != (T, Hv) or tuple(b.shape) != (T, Hv):
+        raise ValueError(f"a and b must be [{T}, {Hv}]")
+
+
+def _state(t, name, N, Hv, dv, dk):
+    torch = _torch()
+    if t is None:
+        return None
+    _need(t, name, (torch.float32,), 4)
+    if tuple(t.shape) != (N, Hv, dv, dk):
+        raise ValueError(f"{name} must be [{N}, {Hv}, {dv}, {dk}], got {tuple(t.shape)}")
+    return t
+
+
+def count_chunks(cu_seqlens, chunk: int) -> int:
+    """sum_n floor(T_n / C) from cu_seqlens (reads it back to the host)."""
+    c = cu_seqlens.detach().to("cpu").to(_torch().int64)
+    return int(((c[1:] - c[:-1]) // chunk).sum())
+
+
+# ----------------------------------------------------------------------------- entry points
+
+def trainer_fwd(cu_seqlens, q, k, v, a, b, *, chunk, initial_state=None, o=None,
+                chunk_states=None, total_chunks=None, identity=None, stream=None):
+    """gdn_cpr_trainer_fwd. Returns (o [T, Hv, dv] fp32, chunk_states [total_chunks, Hv, dv, dk])."""
+    torch = _torch()
+    dt = _qkv(q, k, v)
+    _need(cu_seqlens, "cu_seqlens", (torch.int32,), 1)
+    N = cu_seqlens.shape[0] - 1
+    T, Hv, dv, dk = q.shape[0], v.shape[1], v.shape[2], q.shape[2]
+    _ab(a, b, T, Hv)
+    _state(initial_state, "initial_state", N, Hv, dv, dk)
+    if total_chunks is None:
+        total_chunks = count_chunks(cu_seqlens, chunk)
+    if o is None:
+        o = torch.empty((T, Hv, dv), dtype=torch.float32, device=q.device)
+    _need(o, "o", (torch.float32,), 3)
+    if chunk_states is None:
+        chunk_states = torch.empty((total_chunks, Hv, dv, dk), dtype=torch.float32,
+                                   device=q.device)
+    _need(chunk_states, "chunk_states", (torch.float32,), 4)
+    if chunk_states.shape[0] < total_chunks:
+        raise ValueError("chunk_states has fewer rows than total_chunks")
+    shape = _shape(N, q, v, chunk, dt)
+    ident = identity if identity is not None else contract_identity(chunk, dk)
+    _check(lib().gdn_cpr_trainer_fwd(ctypes.byref(shape), ident, _ptr(cu_seqlens), T,
+                                     _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                     _ptr(initial_state), _ptr(o),
+                                     _ptr(chunk_states) if total_chunks else None,
+                                     total_chunks, _stream(stream)))
+    return o, chunk_states
+
+
+def prefill(cu_seqlens, q, k, v, a, b, *, chunk, initial_state=None, o=None, final_state=None,
+            identity=None, stream=None):
+    """gdn_cpr_prefill. Returns (o [T, Hv, dv] fp32, final_state [N, Hv, dv, dk])."""
+    torch = _torch()
+    dt = _qkv(q, k, v)
+    _need(cu_seqlens, "cu_seqlens", (torch.int32,), 1)
+    N = cu_seqlens.shape[0] - 1
+    T, Hv, dv, dk = q.shape[0], v.shape[1], v.shape[2], q.shape[2]
+    _ab(a, b, T, Hv)
+    _state(initial_state, "initial_state", N, Hv, dv, dk)
+    if o is None:
+        o = torch.empty((T, Hv, dv), dtype=torch.float32, device=q.device)
+    _need(o, "o", (torch.float32,), 3)
+    if final_state is None:
+        final_state = torch.empty((N, Hv, dv, dk), dtype=torch.float32, device=q.device)
+    _state(final_state, "final_state", N, Hv, dv, dk)
+    shape = _shape(N, q, v, chunk, dt)
+    ident = identity if identity is not None else contract_identity(chunk, dk)
+    _check(lib().gdn_cpr_prefill(ctypes.byref(shape), ident, _ptr(cu_seqlens), T, _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(initial_state),
+                                 _ptr(o), _ptr(final_state), _stream(stream)))
+    return o, final_state
+
+
+def decode_step(pos, q, k, v, a, b, state, *, chunk, o=None, resync_states=None,
+                identity=None, stream=None):
+    """gdn_cpr_decode_step: one token per sequence; ``state`` is updated in place.
+
+    pos int32 [N]; q, k [N, Hk, dk]; v [N, Hv, dv]; a, b [N, Hv]; state [N, Hv, dv, dk].
+    Returns o [N, Hv, dv] fp32.
+    """
+    torch = _torch()
+    dt = _qkv(q, k, v)
+    _need(pos, "pos", (torch.int32,), 1)
+    N, Hv, dv, dk = q.shape[0], v.shape[1], v.shape[2], q.shape[2]
+    if pos.shape[0] != N or v.shape[0] != N:
+        raise ValueError("pos, q, k and v must have one row per sequence")
+    _ab(a, b, N, Hv)
+    _state(state, "state", N, Hv, dv, dk)
+    _state(resync_states, "resync_states", N, Hv, dv, dk)
+    if o is None:
+        o = torch.empty((N, Hv, dv), dtype=torch.float32, device=q.device)
+    _need(o, "o", (torch.float32,), 3)
+    shape = _shape(N, q, v, chunk, dt)
+    ident = identity if identity is not None else contract_identity(chunk, dk)
+    _check(lib().gdn_cpr_decode_step(ctypes.byref(shape), ident, _ptr(pos), _ptr(q), _ptr(k),
+                                     _ptr(v), _ptr(a), _ptr(b), _ptr(state), _ptr(o),
+                                     _ptr(resync_states), _stream(stream)))
+    return o

@@ -1,0 +1,67 @@
+"""Build libgdn_cpr.so in-tree with hipcc for gfx950 (cross-compiles without a GPU).
+
+Flags that the contract depends on:
+  -ffp-contract=off                  no fusion other than the explicit fmaf
+  -fno-gpu-flush-denormals-to-zero   binary32 denormals kept on the GPU
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                                     no packed fp32 (v_pk_*) instructions in the kernels
+No -ffast-math anywhere.
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libgdn_cpr.so")
+
+SOURCES = ["cpr_kernels.hip", "api.cpp", "contract.cpp"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-fvisibility=hidden",
+    "-ffp-contract=off",
+    "-fno-fast-math",
+    "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into bitwise_consistent_linear_amd/libgdn_cpr.so; return its path."""
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp,
+           *[os.path.join(CSRC, s) for s in SOURCES]]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed to build libgdn_cpr.so")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def device_asm(out_path: str) -> str:
+    """Write the gfx950 assembly of the kernels (for instruction-mix checks)."""
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
+           "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "--cuda-device-only", "-S", "-I", INCLUDE, "-I", CSRC, "-o", out_path,
+           os.path.join(CSRC, "cpr_kernels.hip")]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out_path
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,232 @@
+// C ABI entry points: host-side claims, identity check, dispatch to the HIP kernels.
+//
+// Every argument claim is checked here, before anything is enqueued, so that a refused
+// call leaves all buffers untouched. IsoExec checks its claims and identities at run time
+// (IsoExec, aihirek.info, section on the contract and common model; agentlenshq.com,
+// section on contract structure: claims and identities).
+
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+
+namespace gdn {
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int64_t kMaxInt32 = 2147483647;
+
+bool aligned(const void *p, size_t bytes) {
+  return (reinterpret_cast<uintptr_t>(p) % bytes) == 0;
+}
+
+// Lanes per state row: GDN_CPR_LANES_PER_ROW overrides the automatic choice.
+int lanes_per_row(int fallback) {
+  const char *env = std::getenv("GDN_CPR_LANES_PER_ROW");
+  if (env && *env) {
+    const int v = std::atoi(env);
+    if (v == 16 || v == 8 || v == 4) return v;
+  }
+  return fallback;
+}
+
+gdn_status_t check_shape(const char *fn, const gdn_shape_t *sh, const uint8_t *identity) {
+  if (!sh) return fail(GDN_E_NULL, std::string(fn) + ": shape is NULL");
+  if (!identity) return fail(GDN_E_NULL, std::string(fn) + ": expected_identity is NULL");
+  if (sh->num_seqs < 0 || sh->num_qk_heads < 1 || sh->num_v_heads < 1)
+    return fail(GDN_E_SHAPE, std::string(fn) + ": need num_seqs >= 0 and head counts >= 1");
+  if (sh->num_v_heads % sh->num_qk_heads != 0)
+    return fail(GDN_E_SHAPE, std::string(fn) + ": num_v_heads must be a multiple of num_qk_heads");
+  if (!admitted_dk(sh->d_k))
+    return fail(GDN_E_UNSUPPORTED, std::string(fn) + ": d_k must be 16, 32, 64 or 128");
+  if (sh->d_v < 1 || sh->d_v > 1024)
+    return fail(GDN_E_UNSUPPORTED, std::string(fn) + ": d_v must be in [1, 1024]");
+  if (!admitted_chunk(sh->chunk))
+    return fail(GDN_E_UNSUPPORTED, std::string(fn) + ": chunk must be 16, 32, 64, 128 or 256");
+  if (sh->qkv_dtype != GDN_DTYPE_F32 && sh->qkv_dtype != GDN_DTYPE_BF16)
+    return fail(GDN_E_UNSUPPORTED, std::string(fn) + ": qkv_dtype must be F32 or BF16");
+  uint8_t mine[32];
+  const std::string text = contract_text(sh->chunk, sh->d_k);
+  sha256(reinterpret_cast<const uint8_t *>(text.data()), text.size(), mine);
+  if (std::memcmp(mine, identity, 32) != 0)
+    return fail(GDN_E_IDENTITY, std::string(fn) + ": expected_identity differs from this "
+                                "library's contract for (chunk, d_k)");
+  return GDN_OK;
+}
+
+gdn_status_t check_inputs(const char *fn, const gdn_shape_t *sh, const void *q, const void *k,
+                          const void *v, const float *a, const float *b) {
+  if (!q || !k || !v || !a || !b)
+    return fail(GDN_E_NULL, std::string(fn) + ": q, k, v, a and b are required");
+  const size_t vec = sh->qkv_dtype == GDN_DTYPE_BF16 ? 8 : 16;
+  if (!aligned(q, vec) || !aligned(k, vec) || !aligned(v, sh->qkv_dtype == GDN_DTYPE_BF16 ? 2 : 4) ||
+      !aligned(a, 4) || !aligned(b, 4))
+    return fail(GDN_E_SHAPE, std::string(fn) + ": q and k must be " + std::to_string(vec) +
+                                 "-byte aligned, v, a and b element aligned");
+  return GDN_OK;
+}
+
+gdn_status_t check_state(const char *fn, const char *name, const float *p) {
+  if (p && !aligned(p, 16))
+    return fail(GDN_E_SHAPE, std::string(fn) + ": " + name + " must be 16-byte aligned");
+  return GDN_OK;
+}
+
+gdn_status_t scan_common(const char *fn, const gdn_shape_t *sh, const uint8_t *identity,
+                         const int32_t *cu, int64_t T, const void *q, const void *k,
+                         const void *v, const float *a, const float *b, const float *s0,
+                         float *o, ScanArgs &args) {
+  gdn_status_t st = check_shape(fn, sh, identity);
+  if (st != GDN_OK) return st;
+  if (T < 0 || T > kMaxInt32)
+    return fail(GDN_E_SHAPE, std::string(fn) + ": total_tokens must be in [0, 2^31)");
+  if (sh->num_seqs > 0 && !cu) return fail(GDN_E_NULL, std::string(fn) + ": cu_seqlens is NULL");
+  if (cu && !aligned(cu, 4)) return fail(GDN_E_SHAPE, std::string(fn) + ": cu_seqlens misaligned");
+  if (T > 0) {
+    st = check_inputs(fn, sh, q, k, v, a, b);
+    if (st != GDN_OK) return st;
+    if (!o) return fail(GDN_E_NULL, std::string(fn) + ": o is required");
+    if (!aligned(o, 4)) return fail(GDN_E_SHAPE, std::string(fn) + ": o misaligned");
+  }
+  if ((st = check_state(fn, "initial_state", s0)) != GDN_OK) return st;
+  args = ScanArgs{};
+  args.num_seqs = sh->num_seqs;
+  args.num_qk_heads = sh->num_qk_heads;
+  args.num_v_heads = sh->num_v_heads;
+  args.d_k = sh->d_k;
+  args.d_v = sh->d_v;
+  args.chunk = sh->chunk;
+  args.bf16 = sh->qkv_dtype == GDN_DTYPE_BF16;
+  args.total_tokens = T;
+  args.cu_seqlens = cu;
+  args.q = q;
+  args.k = k;
+  args.v = v;
+  args.a = a;
+  args.b = b;
+  args.initial_state = s0;
+  args.o = o;
+  return GDN_OK;
+}
+
+gdn_status_t run_scan(const char *fn, ScanArgs &args, void *stream) {
+  const int L = lanes_per_row(16);
+  if (scan_grid(args, L) > kMaxInt32)
+    return fail(GDN_E_SHAPE, std::string(fn) + ": num_seqs * num_v_heads * row blocks too large");
+  const hipError_t e = launch_scan(args, L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(GDN_E_DEVICE, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+gdn_status_t fail(gdn_status_t status, const std::string &message) {
+  g_last_error = message;
+  return status;
+}
+
+gdn_status_t ok() {
+  g_last_error.clear();
+  return GDN_OK;
+}
+
+}  // namespace gdn
+
+extern "C" {
+
+GDN_EXPORT const char *gdn_last_error(void) { return gdn::g_last_error.c_str(); }
+
+GDN_EXPORT gdn_status_t gdn_cpr_trainer_fwd(const gdn_shape_t *shape,
+                                            const uint8_t *expected_identity,
+                                            const int32_t *cu_seqlens, int64_t total_tokens,
+                                            const void *q, const void *k, const void *v,
+                                            const float *a, const float *b,
+                                            const float *initial_state, float *o,
+                                            float *chunk_states, int64_t total_chunks,
+                                            void *stream) {
+  const char *fn = "gdn_cpr_trainer_fwd";
+  gdn::ScanArgs args;
+  gdn_status_t st = gdn::scan_common(fn, shape, expected_identity, cu_seqlens, total_tokens, q,
+                                     k, v, a, b, initial_state, o, args);
+  if (st != GDN_OK) return st;
+  if (total_chunks < 0 || total_chunks > gdn::kMaxInt32)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": total_chunks must be in [0, 2^31)");
+  if (total_chunks > total_tokens / shape->chunk)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": total_chunks exceeds total_tokens / chunk");
+  if (total_chunks > 0 && !chunk_states)
+    return gdn::fail(GDN_E_NULL, std::string(fn) + ": chunk_states is required");
+  if ((st = gdn::check_state(fn, "chunk_states", chunk_states)) != GDN_OK) return st;
+  args.mode = gdn::kTrainer;
+  args.total_chunks = total_chunks;
+  args.chunk_states = chunk_states;
+  return gdn::run_scan(fn, args, stream);
+}
+
+GDN_EXPORT gdn_status_t gdn_cpr_prefill(const gdn_shape_t *shape,
+                                        const uint8_t *expected_identity,
+                                        const int32_t *cu_seqlens, int64_t total_tokens,
+                                        const void *q, const void *k, const void *v,
+                                        const float *a, const float *b,
+                                        const float *initial_state, float *o,
+                                        float *final_state, void *stream) {
+  const char *fn = "gdn_cpr_prefill";
+  gdn::ScanArgs args;
+  gdn_status_t st = gdn::scan_common(fn, shape, expected_identity, cu_seqlens, total_tokens, q,
+                                     k, v, a, b, initial_state, o, args);
+  if (st != GDN_OK) return st;
+  if (shape->num_seqs > 0 && !final_state)
+    return gdn::fail(GDN_E_NULL, std::string(fn) + ": final_state is required");
+  if ((st = gdn::check_state(fn, "final_state", final_state)) != GDN_OK) return st;
+  args.mode = gdn::kPrefill;
+  args.final_state = final_state;
+  return gdn::run_scan(fn, args, stream);
+}
+
+GDN_EXPORT gdn_status_t gdn_cpr_decode_step(const gdn_shape_t *shape,
+                                            const uint8_t *expected_identity,
+                                            const int32_t *pos, const void *q, const void *k,
+                                            const void *v, const float *a, const float *b,
+                                            float *state, float *o, float *resync_states,
+                                            void *stream) {
+  const char *fn = "gdn_cpr_decode_step";
+  gdn_status_t st = gdn::check_shape(fn, shape, expected_identity);
+  if (st != GDN_OK) return st;
+  if (shape->num_seqs > 0) {
+    if (!pos) return gdn::fail(GDN_E_NULL, std::string(fn) + ": pos is NULL");
+    if ((st = gdn::check_inputs(fn, shape, q, k, v, a, b)) != GDN_OK) return st;
+    if (!state || !o) return gdn::fail(GDN_E_NULL, std::string(fn) + ": state and o are required");
+    if (!gdn::aligned(pos, 4) || !gdn::aligned(o, 4))
+      return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": pos or o misaligned");
+  }
+  if ((st = gdn::check_state(fn, "state", state)) != GDN_OK) return st;
+  if ((st = gdn::check_state(fn, "resync_states", resync_states)) != GDN_OK) return st;
+  gdn::DecodeArgs args{};
+  args.num_seqs = shape->num_seqs;
+  args.num_qk_heads = shape->num_qk_heads;
+  args.num_v_heads = shape->num_v_heads;
+  args.d_k = shape->d_k;
+  args.d_v = shape->d_v;
+  args.chunk = shape->chunk;
+  args.bf16 = shape->qkv_dtype == GDN_DTYPE_BF16;
+  args.pos = pos;
+  args.q = q;
+  args.k = k;
+  args.v = v;
+  args.a = a;
+  args.b = b;
+  args.state = state;
+  args.o = o;
+  args.resync_states = resync_states;
+  const int L = gdn::lanes_per_row(16);
+  if (gdn::decode_grid(args, L) > gdn::kMaxInt32)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": num_seqs * num_v_heads * row blocks too large");
+  const hipError_t e = gdn::launch_decode(args, L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return gdn::fail(GDN_E_DEVICE, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
+  return gdn::ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Declarations shared by the library's own sources (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "gdn_cpr.h"
+
+#define GDN_EXPORT __attribute__((visibility("default")))
+
+namespace gdn {
+
+// Thread-local error text behind gdn_last_error().
+gdn_status_t fail(gdn_status_t status, const std::string &message);
+gdn_status_t ok();
+
+void sha256(const uint8_t *msg, size_t len, uint8_t out[32]);
+bool admitted_chunk(int32_t chunk);
+bool admitted_dk(int32_t d_k);
+std::string contract_text(int32_t chunk, int32_t d_k);
+
+enum ScanMode : int32_t { kTrainer = 0, kPrefill = 1 };
+
+// Arguments of one scan launch (trainer_fwd or prefill); validated on the host.
+struct ScanArgs {
+  int32_t num_seqs, num_qk_heads, num_v_heads, d_k, d_v, chunk;
+  int32_t bf16;
+  int32_t mode;
+  int64_t total_tokens;
+  int64_t total_chunks;
+  const int32_t *cu_seqlens;
+  const void *q, *k, *v;
+  const float *a, *b, *initial_state;
+  float *o, *chunk_states, *final_state;
+};
+
+// Arguments of one decode-step launch; validated on the host.
+struct DecodeArgs {
+  int32_t num_seqs, num_qk_heads, num_v_heads, d_k, d_v, chunk;
+  int32_t bf16;
+  const int32_t *pos;
+  const void *q, *k, *v;
+  const float *a, *b;
+  float *state, *o, *resync_states;
+};
+
+// Enqueue the kernels. lanes_per_row is 16, 8 or 4. Return the HIP launch status.
+hipError_t launch_scan(const ScanArgs &args, int lanes_per_row, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &args, int lanes_per_row, hipStream_t stream);
+
+// Number of workgroups a scan or decode launch uses (for the host-side size claims).
+int64_t scan_grid(const ScanArgs &args, int lanes_per_row);
+int64_t decode_grid(const DecodeArgs &args, int lanes_per_row);
+
+}  // namespace gdn

@@ -1,0 +1,179 @@
+/*
+ * gdn_cpr.h - C ABI of libgdn_cpr.so: Chunkwise-Parallel Recurrent (CPR) Gated DeltaNet
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The library computes the gated delta rule, per sequence n, value head h and state row i:
+ *     S_t = a_t * S_{t-1} * (I - b_t k_t k_t^T) + b_t v_t k_t^T,      o_t = S_t q_t
+ * (Yang, Kautz & Hatamizadeh, "Gated Delta Networks", ICLR 2025), through the three cases
+ * that the IsoExec pages name - trainer forward, engine prefill and decode - which must
+ * give bitwise identical results (IsoExec, agentlenshq.com: section on the contract
+ * structure, cases and regions; section "Chunkwise-Parallel Recurrent (CPR) Gated
+ * DeltaNet", including its table where all three CPR stages are bitwise exact).
+ *
+ * EXECUTION CONTRACT (hashed by gdn_contract_identity; see gdn_contract_string).
+ * Each row s = S[i, :] (d_k binary32 values) absorbs token t in this exact order:
+ *     x_e = a * s_e                      binary32 multiply, round to nearest even
+ *     u   = dot(x, k)                    contract dot product, below
+ *     d   = b * (v_i - u)                subtract, then multiply
+ *     s_e = fmaf(d, k_e, x_e)            one fused multiply-add per element
+ *     o_i = dot(s, q)                    read out from the updated state
+ * dot(x, y): GDN_CPR_LEAVES = 16 leaves of d_k/16 contiguous elements; a leaf starts with
+ * the rounded product of its first pair and adds the others with fmaf in ascending index;
+ * the 16 leaf sums are added pairwise in natural order ((0+1),(2+3),...; then pairs of
+ * those; four levels). Binary32 throughout, denormals kept, no fusion other than these
+ * fmaf. The fixed binary tree with fp32 accumulation follows the IsoExec page's section on
+ * achieving parallel invariance; the per-(region, case) pinning of accumulation dtype and
+ * reduction decomposition follows its section on contract structure. The update order,
+ * leaf width and pairing are this library's reading of the rule and are part of the
+ * identity. q/k head of value head h is h / (Hv / Hk). bf16 inputs are widened exactly.
+ * The chunk size C selects only which states are emitted; it changes no output bits.
+ *
+ * LAYOUTS (row-major, element offsets; all device pointers unless stated otherwise):
+ *   cu_seqlens  int32 [N+1], cu_seqlens[0] = 0, nondecreasing, cu_seqlens[N] = T
+ *   q, k        [T, Hk, d_k]   binary32 or bfloat16 (gdn_shape_t.qkv_dtype)
+ *   v           [T, Hv, d_v]   same dtype as q and k
+ *   a, b        float [T, Hv]  decay and write strength, used as given
+ *   o           float [T, Hv, d_v]
+ *   states      float [.., Hv, d_v, d_k]  (row i of S is d_k contiguous floats)
+ * Sequence n owns tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of the packed batch.
+ *
+ * OWNERSHIP, STREAMS, ERRORS. The caller allocates every buffer; the library allocates
+ * and frees no device memory and keeps no state between calls. Work is enqueued on the
+ * hipStream_t passed as `stream` (NULL = the null stream) of the current HIP device; the
+ * calls return before the work finishes. All argument checks run on the host before
+ * anything is enqueued, so a non-GDN_OK status means nothing was launched, except
+ * GDN_E_DEVICE (a launch error reported by HIP). Device-side values (cu_seqlens contents,
+ * pos) cannot be checked on the host: kernels clamp token ranges to [0, T) and skip
+ * chunk-state writes past total_chunks, so bad contents give wrong numbers, never
+ * out-of-bounds accesses. Outputs must not alias inputs (except the documented in/out
+ * state of decode). gdn_last_error() returns text for the calling thread's last error.
+ * All functions are thread-safe.
+ *
+ * TUNING. The environment variable GDN_CPR_LANES_PER_ROW (16, 8 or 4) overrides how many
+ * lanes of a wavefront share one state row; the contract makes every admitted value give
+ * the same bits, which the tests check.
+ */
+#ifndef GDN_CPR_H
+#define GDN_CPR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_CPR_ABI_VERSION 1
+#define GDN_CPR_LEAVES 16
+#define GDN_CPR_IDENTITY_BYTES 32
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_E_NULL = 1,        /* a required pointer is NULL                                */
+  GDN_E_SHAPE = 2,       /* sizes are negative, inconsistent or too large             */
+  GDN_E_UNSUPPORTED = 3, /* chunk, d_k, d_v or dtype outside the admitted values      */
+  GDN_E_IDENTITY = 4,    /* expected_identity differs from this library's contract    */
+  GDN_E_DEVICE = 5       /* HIP reported an error when launching                      */
+} gdn_status_t;
+
+typedef enum gdn_dtype { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype_t;
+
+/* Host struct. Admitted values (claims checked on every call):
+ *   num_seqs >= 0; num_qk_heads >= 1; num_v_heads a multiple of num_qk_heads;
+ *   d_k in {16, 32, 64, 128}; 1 <= d_v <= 1024; chunk in {16, 32, 64, 128, 256};
+ *   qkv_dtype GDN_DTYPE_F32 or GDN_DTYPE_BF16. */
+typedef struct gdn_shape {
+  int32_t num_seqs;     /* N  */
+  int32_t num_qk_heads; /* Hk */
+  int32_t num_v_heads;  /* Hv */
+  int32_t d_k;
+  int32_t d_v;
+  int32_t chunk; /* C  */
+  int32_t qkv_dtype;
+} gdn_shape_t;
+
+/* ABI version of the loaded library (GDN_CPR_ABI_VERSION). Host only. */
+int32_t gdn_abi_version(void);
+
+/* Canonical contract text for (chunk, d_k): ASCII lines "key=value\n" fixing the rule,
+ * operation order, reduction tree, dtypes, rounding, head mapping, chunk boundaries and
+ * resync rule. Writes at most buf_len bytes (NUL-terminated when it fits) and the full
+ * length, without the NUL, to *out_len. buf may be NULL when buf_len is 0.
+ * Host only. Errors: GDN_E_NULL (out_len NULL), GDN_E_UNSUPPORTED (chunk or d_k not
+ * admitted), GDN_E_SHAPE (buffer too small; *out_len still set).
+ * Identity by content digest follows IsoExec (aihirek.info, section on the contract and
+ * common model; agentlenshq.com, section on contract structure: SHA-256 identities). */
+gdn_status_t gdn_contract_string(int32_t chunk, int32_t d_k, char *buf, size_t buf_len,
+                                 size_t *out_len);
+
+/* SHA-256 (FIPS 180-4) of gdn_contract_string(chunk, d_k) into digest[32] (host memory).
+ * Every compute entry point takes this digest as expected_identity and refuses to run
+ * when it differs. Host only. Errors: GDN_E_NULL, GDN_E_UNSUPPORTED. */
+gdn_status_t gdn_contract_identity(int32_t chunk, int32_t d_k, uint8_t digest[32]);
+
+/* SHA-256 (FIPS 180-4) of len bytes at msg (host memory) into digest[32] (host memory);
+ * the routine behind gdn_contract_identity, for callers that derive identities of their
+ * own texts. Host only. Errors: GDN_E_NULL (digest NULL, or msg NULL with len > 0). */
+gdn_status_t gdn_sha256(const void *msg, size_t len, uint8_t digest[32]);
+
+/* trainer_fwd: the recurrence over a packed batch, writing o for every token and the state
+ * at every C-token chunk boundary (IsoExec, agentlenshq.com, section "Chunkwise-Parallel
+ * Recurrent (CPR) Gated DeltaNet"; the trainer-forward case of the contract).
+ *   shape, expected_identity : host pointers, required (identity: 32 bytes)
+ *   cu_seqlens [N+1], total_tokens T (0 <= T < 2^31)
+ *   q, k, v, a, b            : inputs, layouts above
+ *   initial_state            : [N, Hv, d_v, d_k] or NULL for zeros
+ *   o                        : [T, Hv, d_v] output
+ *   chunk_states             : [total_chunks, Hv, d_v, d_k] output; the state after
+ *                              in-sequence token j with (j+1) % C == 0, boundary by
+ *                              boundary, sequence by sequence: sequence n writes
+ *                              floor(T_n / C) states starting at sum_{m<n} floor(T_m / C).
+ *                              May be NULL only when total_chunks == 0.
+ *   total_chunks             : sum_n floor(T_n / C), 0 <= total_chunks < 2^31
+ *   stream                   : hipStream_t or NULL. */
+gdn_status_t gdn_cpr_trainer_fwd(const gdn_shape_t *shape, const uint8_t *expected_identity,
+                                 const int32_t *cu_seqlens, int64_t total_tokens,
+                                 const void *q, const void *k, const void *v, const float *a,
+                                 const float *b, const float *initial_state, float *o,
+                                 float *chunk_states, int64_t total_chunks, void *stream);
+
+/* engine_prefill: the same recurrence over a packed batch of prompts, writing o for every
+ * token and the final state of every sequence (IsoExec, agentlenshq.com, section
+ * "Chunkwise-Parallel Recurrent (CPR) Gated DeltaNet"; the engine-prefill case).
+ *   initial_state [N, Hv, d_v, d_k] or NULL for zeros; o [T, Hv, d_v];
+ *   final_state [N, Hv, d_v, d_k] (required; may be the same buffer as initial_state, which
+ *   is then updated in place). Other arguments as for gdn_cpr_trainer_fwd. */
+gdn_status_t gdn_cpr_prefill(const gdn_shape_t *shape, const uint8_t *expected_identity,
+                             const int32_t *cu_seqlens, int64_t total_tokens, const void *q,
+                             const void *k, const void *v, const float *a, const float *b,
+                             const float *initial_state, float *o, float *final_state,
+                             void *stream);
+
+/* engine_decode: one token for each of N sequences, streaming the binary32 state through
+ * HBM; at every C-token boundary the new state is also written as the resync checkpoint,
+ * equal bit for bit to the trainer's chunk state at that boundary (IsoExec,
+ * agentlenshq.com, section "Chunkwise-Parallel Recurrent (CPR) Gated DeltaNet": decode
+ * resynchronises the hidden state every C tokens).
+ *   pos            int32 [N]: tokens already absorbed by state[n]; the step applies token
+ *                  pos[n]; pos[n] < 0 marks an idle slot, whose state, o and resync rows
+ *                  are left untouched
+ *   q, k [N, Hk, d_k]; v [N, Hv, d_v]; a, b float [N, Hv]
+ *   state          float [N, Hv, d_v, d_k], in/out
+ *   o              float [N, Hv, d_v] output
+ *   resync_states  float [N, Hv, d_v, d_k] or NULL; row block n is written iff
+ *                  (pos[n] + 1) % C == 0
+ * Other arguments as for gdn_cpr_trainer_fwd. */
+gdn_status_t gdn_cpr_decode_step(const gdn_shape_t *shape, const uint8_t *expected_identity,
+                                 const int32_t *pos, const void *q, const void *k,
+                                 const void *v, const float *a, const float *b, float *state,
+                                 float *o, float *resync_states, void *stream);
+
+/* Text describing the calling thread's last non-GDN_OK status ("" if none). The pointer
+ * stays valid until the thread's next call into the library. Host only. */
+const char *gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_CPR_H */

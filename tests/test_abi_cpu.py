@@ -1,0 +1,196 @@
+"""The C ABI on the host: exports, identity, claims. No GPU is touched: every call here is
+refused by a host-side check before anything is enqueued (fake pointers are never read)."""
+
+import ctypes
+import hashlib
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+from bitwise_consistent_linear_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn_cpr.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+CHUNKS = (16, 32, 64, 128, 256)
+DKS = (16, 32, 64, 128)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return api.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) == 8, names
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(gdn_\w+)$", out, flags=re.M))
+    assert set(names) <= exported, set(names) - exported
+    assert exported <= set(names), f"undeclared exports: {exported - set(names)}"
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_abi_version_matches_header(L):
+    m = re.search(r"#define GDN_CPR_ABI_VERSION (\d+)", open(HEADER).read())
+    assert api.abi_version() == int(m.group(1))
+
+
+@pytest.mark.parametrize("n", [0, 1, 3, 55, 56, 57, 63, 64, 65, 119, 120, 127, 128, 129, 1000])
+def test_sha256_matches_hashlib(n):
+    data = bytes((i * 131 + 7) % 256 for i in range(n))
+    assert api.sha256(data) == hashlib.sha256(data).digest()
+
+
+@pytest.mark.parametrize("chunk", CHUNKS)
+@pytest.mark.parametrize("d_k", DKS)
+def test_identity_is_sha256_of_contract_text(chunk, d_k):
+    text = api.contract_string(chunk, d_k)
+    assert f"chunk={chunk}\n" in text and f"d_k={d_k}\n" in text
+    assert "leaves:16" in text and "fusion=explicit fma only" in text
+    assert api.contract_identity(chunk, d_k) == hashlib.sha256(text.encode()).digest()
+
+
+def test_identities_are_distinct():
+    ids = {api.contract_identity(c, d) for c in CHUNKS for d in DKS}
+    assert len(ids) == len(CHUNKS) * len(DKS)
+
+
+def test_identity_matches_committed_digest():
+    with open(os.path.join(GOLDEN, "contract_identity.json")) as f:
+        want = json.load(f)
+    for key, hexdigest in want["identities"].items():
+        c, d = (int(x) for x in key.split(","))
+        assert api.contract_identity(c, d).hex() == hexdigest, key
+
+
+@pytest.mark.parametrize("chunk,d_k", [(48, 128), (0, 128), (64, 48), (64, 256), (-16, 16)])
+def test_unadmitted_contract_refused(L, chunk, d_k):
+    buf = ctypes.create_string_buffer(32)
+    assert L.gdn_contract_identity(chunk, d_k, buf) == api.GDN_E_UNSUPPORTED
+    n = ctypes.c_size_t(0)
+    assert L.gdn_contract_string(chunk, d_k, None, 0, ctypes.byref(n)) == api.GDN_E_UNSUPPORTED
+
+
+def test_contract_string_small_buffer(L):
+    n = ctypes.c_size_t(0)
+    assert L.gdn_contract_string(64, 128, None, 0, ctypes.byref(n)) == api.GDN_E_SHAPE
+    assert n.value == len(api.contract_string(64, 128))
+    assert L.gdn_contract_string(64, 128, None, 0, None) == api.GDN_E_NULL
+
+
+# ------------------------------------------------------------------- refused compute calls
+
+FAKE = 0x100000  # never dereferenced: every call below is refused on the host
+
+
+def shape(**kw):
+    base = dict(num_seqs=2, num_qk_heads=2, num_v_heads=4, d_k=64, d_v=64, chunk=64,
+                qkv_dtype=api.GDN_DTYPE_BF16)
+    base.update(kw)
+    return api.GdnShape(**base)
+
+
+def ident(sh):
+    if sh is None or sh.chunk not in CHUNKS or sh.d_k not in DKS:
+        return bytes(32)
+    return api.contract_identity(sh.chunk, sh.d_k)
+
+
+def trainer(L, sh, identity=None, T=128, total_chunks=2, **ptrs):
+    p = dict(cu=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s0=None, o=FAKE, cs=FAKE)
+    p.update(ptrs)
+    idb = ident(sh) if identity is None else identity
+    return L.gdn_cpr_trainer_fwd(ctypes.byref(sh) if sh is not None else None, idb, p["cu"], T,
+                                 p["q"], p["k"], p["v"], p["a"], p["b"], p["s0"], p["o"],
+                                 p["cs"], total_chunks, None)
+
+
+def prefill(L, sh, identity=None, T=128, **ptrs):
+    p = dict(cu=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s0=None, o=FAKE, fs=FAKE)
+    p.update(ptrs)
+    idb = ident(sh) if identity is None else identity
+    return L.gdn_cpr_prefill(ctypes.byref(sh), idb, p["cu"], T, p["q"], p["k"], p["v"],
+                             p["a"], p["b"], p["s0"], p["o"], p["fs"], None)
+
+
+def decode(L, sh, identity=None, **ptrs):
+    p = dict(pos=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, state=FAKE, o=FAKE, rs=None)
+    p.update(ptrs)
+    idb = ident(sh) if identity is None else identity
+    return L.gdn_cpr_decode_step(ctypes.byref(sh), idb, p["pos"], p["q"], p["k"], p["v"],
+                                 p["a"], p["b"], p["state"], p["o"], p["rs"], None)
+
+
+REFUSALS = [
+    ("null shape", lambda L: trainer(L, None), api.GDN_E_NULL),
+    ("null identity", lambda L: L.gdn_cpr_trainer_fwd(ctypes.byref(shape()), None, FAKE, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 2, None), api.GDN_E_NULL),
+    ("wrong identity", lambda L: trainer(L, shape(), identity=bytes(32)), api.GDN_E_IDENTITY),
+    ("identity of other chunk", lambda L: trainer(L, shape(), identity=api.contract_identity(16, 64)), api.GDN_E_IDENTITY),
+    ("identity of other d_k", lambda L: prefill(L, shape(), identity=api.contract_identity(64, 128)), api.GDN_E_IDENTITY),
+    ("heads not a multiple", lambda L: trainer(L, shape(num_qk_heads=3, num_v_heads=4)), api.GDN_E_SHAPE),
+    ("zero qk heads", lambda L: trainer(L, shape(num_qk_heads=0)), api.GDN_E_SHAPE),
+    ("negative seqs", lambda L: trainer(L, shape(num_seqs=-1)), api.GDN_E_SHAPE),
+    ("d_k not admitted", lambda L: trainer(L, shape(d_k=48)), api.GDN_E_UNSUPPORTED),
+    ("d_v zero", lambda L: trainer(L, shape(d_v=0)), api.GDN_E_UNSUPPORTED),
+    ("d_v too large", lambda L: trainer(L, shape(d_v=1025)), api.GDN_E_UNSUPPORTED),
+    ("chunk not admitted", lambda L: trainer(L, shape(chunk=48)), api.GDN_E_UNSUPPORTED),
+    ("dtype not admitted", lambda L: trainer(L, shape(qkv_dtype=7)), api.GDN_E_UNSUPPORTED),
+    ("negative tokens", lambda L: trainer(L, shape(), T=-1), api.GDN_E_SHAPE),
+    ("tokens >= 2^31", lambda L: trainer(L, shape(), T=2**31), api.GDN_E_SHAPE),
+    ("negative chunks", lambda L: trainer(L, shape(), total_chunks=-1), api.GDN_E_SHAPE),
+    ("more chunks than T/C", lambda L: trainer(L, shape(), total_chunks=3), api.GDN_E_SHAPE),
+    ("null cu_seqlens", lambda L: trainer(L, shape(), cu=None), api.GDN_E_NULL),
+    ("null q", lambda L: trainer(L, shape(), q=None), api.GDN_E_NULL),
+    ("null b", lambda L: prefill(L, shape(), b=None), api.GDN_E_NULL),
+    ("null o", lambda L: trainer(L, shape(), o=None), api.GDN_E_NULL),
+    ("null chunk_states", lambda L: trainer(L, shape(), cs=None), api.GDN_E_NULL),
+    ("null final_state", lambda L: prefill(L, shape(), fs=None), api.GDN_E_NULL),
+    ("misaligned q (bf16 needs 8 B)", lambda L: trainer(L, shape(), q=FAKE + 4), api.GDN_E_SHAPE),
+    ("misaligned k (f32 needs 16 B)", lambda L: trainer(L, shape(qkv_dtype=api.GDN_DTYPE_F32), k=FAKE + 8), api.GDN_E_SHAPE),
+    ("misaligned initial state", lambda L: prefill(L, shape(), s0=FAKE + 4), api.GDN_E_SHAPE),
+    ("misaligned chunk states", lambda L: trainer(L, shape(), cs=FAKE + 8), api.GDN_E_SHAPE),
+    ("decode null pos", lambda L: decode(L, shape(), pos=None), api.GDN_E_NULL),
+    ("decode null state", lambda L: decode(L, shape(), state=None), api.GDN_E_NULL),
+    ("decode null v", lambda L: decode(L, shape(), v=None), api.GDN_E_NULL),
+    ("decode misaligned state", lambda L: decode(L, shape(), state=FAKE + 4), api.GDN_E_SHAPE),
+    ("decode misaligned resync", lambda L: decode(L, shape(), rs=FAKE + 4), api.GDN_E_SHAPE),
+    ("decode wrong identity", lambda L: decode(L, shape(), identity=b"\x01" * 32), api.GDN_E_IDENTITY),
+    ("decode chunk not admitted", lambda L: decode(L, shape(chunk=100)), api.GDN_E_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,call,status", REFUSALS, ids=[r[0] for r in REFUSALS])
+def test_refused_before_launch(L, name, call, status):
+    assert call(L) == status
+    msg = L.gdn_last_error().decode()
+    assert msg.startswith("gdn_cpr_"), msg
+
+
+def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
+    monkeypatch.setattr(api, "_lib", None)
+    monkeypatch.setattr(api, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        api.lib()
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "bitwise_consistent_linear_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, flags=re.M), f
+                assert "gdn_oracle" not in text and "liboracle" not in text, f

@@ -1,0 +1,50 @@
+"""The gfx950 code of the kernels obeys the contract's arithmetic rules (CPU only: hipcc -S).
+
+* binary32 denormals kept (kernel descriptor float_denorm_mode_32 = 3);
+* no packed fp32 instructions and no unfused multiply-add (v_mad/v_mac) forms;
+* every fused multiply-add is a v_fma/v_fmac, every DPP reduction step an add;
+* no register spills in any kernel.
+"""
+
+import re
+
+import pytest
+
+from bitwise_consistent_linear_amd import build
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    path = tmp_path_factory.mktemp("isa") / "kernels.s"
+    return build.device_asm(str(path)) and open(path).read()
+
+
+def kernels(asm):
+    return re.findall(r"^\s+\.amdhsa_kernel (\S+)$", asm, flags=re.M)
+
+
+def test_all_kernels_present(asm):
+    names = kernels(asm)
+    assert sum("cpr_scan_kernel" in n for n in names) == 4 * 3 * 2 * 2
+    assert sum("cpr_decode_kernel" in n for n in names) == 4 * 3 * 2
+
+
+def test_denormals_kept(asm):
+    modes = re.findall(r"\.amdhsa_float_denorm_mode_32 (\d)", asm)
+    assert modes and all(m == "3" for m in modes)
+
+
+def test_no_packed_or_unfused_fp32(asm):
+    assert not re.search(r"^\s+v_pk_\w+", asm, flags=re.M)
+    assert not re.search(r"^\s+v_ma[cd]_(f32|legacy)", asm, flags=re.M)
+    assert not re.search(r"^\s+v_fma_legacy", asm, flags=re.M)
+
+
+def test_dpp_steps_are_adds(asm):
+    dpp = re.findall(r"^\s+(v_\w+_dpp)\b", asm, flags=re.M)
+    assert dpp and set(dpp) <= {"v_add_f32_dpp", "v_mov_b32_dpp"}
+
+
+def test_no_spills(asm):
+    sizes = re.findall(r"\.private_segment_fixed_size: (\d+)", asm)
+    assert sizes and all(s == "0" for s in sizes)
