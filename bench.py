@@ -1,0 +1,337 @@
+"""Benchmark of the CPR Gated DeltaNet hot path on one MI355X.
+
+Prints ONE JSON line on stdout (progress goes to stderr). The headline step is one
+trainer_fwd call (gdn_cpr_trainer_fwd: every token's o plus the state at every 64-token
+boundary) over the trainer workload: 4 sequences x 4096 tokens, 16 heads, d_k = d_v = 128,
+C = 64, bf16 q/k/v, fp32 a/b/state/o. `value` is tokens/s of that step with inputs already
+in HBM. The same line also reports, under "cases", engine_prefill tokens/s (64 varlen
+sequences, 262144 tokens, 16 q/k / 32 v heads), the engine_decode step time (256
+sequences after a 1000-token prefill, 512 steps) and the long-context runs, each with its
+fraction of the relevant peak, plus the CPU oracle timed on the host as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cases all|main]
+                       [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, spec sheet
+FP32_FMA_PEAK_TFLOPS = 78.6       # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (no packed fp32)
+FP32_PACKED_PEAK_TFLOPS = 157.3   # spec-sheet figure with packed fp32 (not used by these kernels)
+METRIC = "GDN-CPR tokens/s (trainer_fwd, prefill), decode-step us, % of HBM peak"
+KERNEL_SOURCES = ["cpr_kernels.hip", "cpr_row.hpp"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bitwise_consistent_linear_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def flops_per_token_head(dk, dv):
+    # per row and token: decay d_k mul; two contract dots of 16 mul + (d_k-16) fma + 15 add
+    # = 2 d_k - 1 flop each; delta 2; rank-1 update d_k fma = 2 d_k  ->  7 d_k flop
+    return 7 * dk * dv
+
+
+def scan_bytes(w, with_o=True, chunk_states=0, final_states=0, initial_states=0):
+    """Algorithmic HBM bytes of one scan call: each input read once, each output written once."""
+    el = 2 if w.bf16 else 4
+    T, Hk, Hv, dk, dv = w.total_tokens, w.num_qk_heads, w.num_v_heads, w.d_k, w.d_v
+    b = T * Hk * dk * el * 2 + T * Hv * dv * el + T * Hv * 4 * 2 + (w.num_seqs + 1) * 4
+    if with_o:
+        b += T * Hv * dv * 4
+    b += (chunk_states + final_states + initial_states) * Hv * dv * dk * 4
+    return b
+
+
+def decode_step_bytes(N, Hk, Hv, dk, dv, el, C):
+    state = N * Hv * dv * dk * 4
+    return (2 * state + N * Hk * dk * el * 2 + N * Hv * dv * el + N * Hv * 4 * 2 + N * 4
+            + N * Hv * dv * 4 + state / C)
+
+
+def up(x):
+    import numpy as np
+    import torch
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(x).cuda()
+
+
+def timed(fn, steps, warmup):
+    """Run fn warmup times, then time `steps` calls: wall clock of the whole region and HIP
+    events around each call on the current stream. Returns (wall_s, per_call_ms list)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in evs:
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [s.elapsed_time(e) for s, e in evs]
+
+
+def roofline_alu(flops, ms):
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"bound": "alu", "achieved": round(achieved, 3), "peak": FP32_FMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / FP32_FMA_PEAK_TFLOPS, 4)}
+
+
+def hbm(bytes_, ms):
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    return {"algorithmic_bytes": int(bytes_), "achieved_GBs": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def traffic_for(name, launches_bytes_fn=None):
+    """Measured HBM bytes per launch from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return int(t["hbm_bytes_per_launch"])
+
+
+# ------------------------------------------------------------------------------ cases
+
+def bench_trainer(steps, warmup):
+    import torch
+    from bitwise_consistent_linear_amd import api
+    from bitwise_consistent_linear_amd import workloads as W
+    w = W.trainer_fwd()
+    log(f"trainer_fwd: N={w.num_seqs} T={w.lengths[0]} H={w.num_v_heads} d={w.d_k} C={w.chunk}")
+    cu, q, k, v, a, b = (up(x) for x in (w.cu_seqlens, w.q, w.k, w.v, w.a, w.b))
+    o = torch.empty((w.total_tokens, w.num_v_heads, w.d_v), dtype=torch.float32, device="cuda")
+    cs = torch.empty((w.total_chunks, w.num_v_heads, w.d_v, w.d_k), dtype=torch.float32,
+                     device="cuda")
+    tc = w.total_chunks
+
+    def step():
+        api.trainer_fwd(cu, q, k, v, a, b, chunk=w.chunk, o=o, chunk_states=cs, total_chunks=tc)
+
+    wall, per = timed(step, steps, warmup)
+    kernel_ms = sum(per) / len(per)
+    flops = flops_per_token_head(w.d_k, w.d_v) * w.total_tokens * w.num_v_heads
+    nbytes = scan_bytes(w, chunk_states=tc)
+    return w, wall, kernel_ms, flops, nbytes
+
+
+def bench_prefill(steps, warmup):
+    import torch
+    from bitwise_consistent_linear_amd import api
+    from bitwise_consistent_linear_amd import workloads as W
+    w = W.engine_prefill()
+    L = w.lengths
+    log(f"engine_prefill: N={w.num_seqs} lengths {L.min()}..{L.max()} sum {L.sum()}")
+    cu, q, k, v, a, b = (up(x) for x in (w.cu_seqlens, w.q, w.k, w.v, w.a, w.b))
+    o = torch.empty((w.total_tokens, w.num_v_heads, w.d_v), dtype=torch.float32, device="cuda")
+    fs = torch.empty((w.num_seqs, w.num_v_heads, w.d_v, w.d_k), dtype=torch.float32,
+                     device="cuda")
+
+    def step():
+        api.prefill(cu, q, k, v, a, b, chunk=w.chunk, o=o, final_state=fs)
+
+    wall, per = timed(step, steps, warmup)
+    ms = sum(per) / len(per)
+    flops = flops_per_token_head(w.d_k, w.d_v) * w.total_tokens * w.num_v_heads
+    nbytes = scan_bytes(w, final_states=w.num_seqs)
+    del q, k, v, o
+    return {"workload": f"engine_prefill: 64 varlen sequences (lognormal, {L.min()}..{L.max()} "
+                        f"tokens), {L.sum()} tokens, 16 q/k / 32 v heads, d=128, C=64, bf16 q/k/v",
+            "tokens_per_s": round(w.total_tokens / (wall / steps), 1),
+            "ms_per_call": round(wall / steps * 1e3, 4), "kernel_ms": round(ms, 4),
+            "steps": steps, "roofline": roofline_alu(flops, ms), "hbm": hbm(nbytes, ms)}
+
+
+def bench_decode_after_prefill(w, prefix, nsteps, warmup_steps, label):
+    """Prefill `prefix` tokens of every sequence, then time decode steps one by one."""
+    import torch
+    from bitwise_consistent_linear_amd import api
+    from bitwise_consistent_linear_amd import workloads as W
+    pre, steps = W.split_for_decode(w, prefix)
+    dp = {k: up(getattr(pre, k)) for k in ("q", "k", "v", "a", "b")}
+    _, state = api.prefill(up(pre.cu_seqlens), dp["q"], dp["k"], dp["v"], dp["a"], dp["b"],
+                           chunk=w.chunk)
+    del dp
+    ds = {k: up(x) for k, x in steps.items()}
+    N = w.num_seqs
+    rs = torch.empty_like(state)
+    o = torch.empty((N, w.num_v_heads, w.d_v), dtype=torch.float32, device="cuda")
+    S = ds["q"].shape[0]
+    assert warmup_steps + nsteps <= S
+    it = iter(range(S))
+
+    def step():
+        s = next(it)
+        api.decode_step(ds["pos"][s], ds["q"][s], ds["k"][s], ds["v"][s], ds["a"][s],
+                        ds["b"][s], state, chunk=w.chunk, o=o, resync_states=rs)
+
+    wall, per = timed(step, nsteps, warmup_steps)
+    ms = sum(per) / len(per)
+    nbytes = decode_step_bytes(N, w.num_qk_heads, w.num_v_heads, w.d_k, w.d_v,
+                               2 if w.bf16 else 4, w.chunk)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"{label}: {nsteps} decode steps, {ms * 1e3:.1f} us/step (events)")
+    return {"us_per_step_kernel": round(ms * 1e3, 2),
+            "us_per_step_wall": round(wall / nsteps * 1e6, 2), "steps": nsteps,
+            "warmup_steps": warmup_steps,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "algorithmic_bytes_per_step": int(nbytes)}
+
+
+def bench_decode():
+    from bitwise_consistent_linear_amd import workloads as W
+    w = W.engine_decode()
+    log("engine_decode: N=256, 1000-token prefill, 512 decode steps, 16/32 heads, d=128")
+    r = bench_decode_after_prefill(w, 1000, 504, 8, "engine_decode")
+    r["workload"] = ("engine_decode: 256 sequences, 16 q/k / 32 v heads, d=128, C=64, fp32 "
+                     "state in HBM, prefill 1000 tokens then 512 steps (8 untimed)")
+    return r
+
+
+def bench_long(steps):
+    import numpy as np
+    import torch
+    from bitwise_consistent_linear_amd import api
+    from bitwise_consistent_linear_amd import workloads as W
+    w = W.long_context()
+    log("long_context: T=131072, 16/32 heads, d=128")
+    cu, q, k, v, a, b = (up(x) for x in (w.cu_seqlens, w.q, w.k, w.v, w.a, w.b))
+    o = torch.empty((w.total_tokens, w.num_v_heads, w.d_v), dtype=torch.float32, device="cuda")
+    cs = torch.empty((w.total_chunks, w.num_v_heads, w.d_v, w.d_k), dtype=torch.float32,
+                     device="cuda")
+    fs = torch.empty((1, w.num_v_heads, w.d_v, w.d_k), dtype=torch.float32, device="cuda")
+    wall_t, per_t = timed(lambda: api.trainer_fwd(cu, q, k, v, a, b, chunk=64, o=o,
+                                                  chunk_states=cs, total_chunks=w.total_chunks),
+                          steps, 1)
+    wall_p, per_p = timed(lambda: api.prefill(cu, q, k, v, a, b, chunk=64, o=o, final_state=fs),
+                          steps, 1)
+    del q, k, v, o, cs
+    torch.cuda.empty_cache()
+    flops = flops_per_token_head(w.d_k, w.d_v) * w.total_tokens * w.num_v_heads
+    mt, mp = sum(per_t) / len(per_t), sum(per_p) / len(per_p)
+    P, S = w.extra["prefix"], w.extra["steps"]
+    cut = W.Workload("long_context_decode", np.array([0, P + S], np.int32), w.q[:P + S],
+                     w.k[:P + S], w.v[:P + S], w.a[:P + S], w.b[:P + S], w.chunk, w.bf16)
+    dec = bench_decode_after_prefill(cut, P, S - 8, 8, "long_context decode")
+    return {"workload": "long_context: 1 x 131072 tokens, 16 q/k / 32 v heads, d=128, C=64, "
+                        "bf16 q/k/v, a ~ U(0.95, 1)",
+            "trainer_fwd_tokens_per_s": round(w.total_tokens / (wall_t / steps), 1),
+            "trainer_fwd_kernel_ms": round(mt, 3),
+            "trainer_fwd_roofline": roofline_alu(flops, mt),
+            "trainer_fwd_hbm": hbm(scan_bytes(w, chunk_states=w.total_chunks), mt),
+            "prefill_tokens_per_s": round(w.total_tokens / (wall_p / steps), 1),
+            "prefill_kernel_ms": round(mp, 3),
+            "decode_after_65536": dec}
+
+
+def cpu_baseline(w):
+    """The CPU oracle on the whole trainer_fwd workload (all outputs), on the host's cores."""
+    from oracle import oracle as O
+    threads = min(16, O.default_threads())
+    t0 = time.perf_counter()
+    O.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=w.chunk, want_chunk_states=True,
+           nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(w.total_tokens / dt, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole trainer_fwd workload (4 x 4096 tokens, 16 heads, o and "
+                      f"chunk states), {dt:.2f} s on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cases", choices=["all", "main"], default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (every state "
+              "row is independent; see DESIGN.md for how the work would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from bitwise_consistent_linear_amd import api
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    api.lib()
+    log(f"device: {torch.cuda.get_device_name(0)}")
+
+    w, wall, kernel_ms, flops, nbytes = bench_trainer(args.steps, args.warmup)
+    ms_per_step = wall / args.steps * 1e3
+    roof = roofline_alu(flops, kernel_ms)
+    traffic = traffic_for("cpr_scan_trainer_fwd")
+    roof["traffic"] = traffic
+    log(f"trainer_fwd: {ms_per_step:.3f} ms/step, kernel {kernel_ms:.3f} ms, "
+        f"{roof['achieved']} TFLOP/s")
+    out = {
+        "metric": METRIC,
+        "value": round(w.total_tokens / (wall / args.steps), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "trainer_fwd: 4 sequences x 4096 tokens, 16 q/k = 16 v heads, "
+                               "d_k=d_v=128, C=64, bf16 q/k/v, fp32 a/b/state/o; writes o and "
+                               "the 256 chunk-boundary states",
+                   "global_batch": 4, "seq_len": 4096, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "hbm": hbm(nbytes, kernel_ms),
+        "frac_of_packed_fp32_spec_peak": round(roof["achieved"] / FP32_PACKED_PEAK_TFLOPS, 4),
+        "kernel_ms": round(kernel_ms, 4),
+        "contract_identity": api.contract_identity(64, 128).hex(),
+    }
+    if args.cases == "all":
+        cases = {}
+        cases["engine_prefill"] = bench_prefill(max(3, args.steps // 4), 1)
+        torch.cuda.empty_cache()
+        cases["engine_decode"] = bench_decode()
+        torch.cuda.empty_cache()
+        cases["long_context"] = bench_long(max(2, args.steps // 10))
+        torch.cuda.empty_cache()
+        out["cases"] = cases
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on the trainer_fwd workload")
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

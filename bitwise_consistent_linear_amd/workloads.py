@@ -5,8 +5,8 @@ and the CPU oracle consume the same stored bytes, so the generator's own roundin
 L2 normalisation of k, the cast to bfloat16) never shows up as a difference between them.
 
 Recipe: numpy PCG64 streams from ``SeedSequence(seed).spawn(6)``, one per drawn quantity in
-the order lengths, q, k, v, a, b; each tensor is drawn in fixed blocks of 2**22 elements,
-block j from the j-th child of its stream, so the values do not depend on thread count.
+the order lengths, q, k, v, a, b; each tensor is drawn in fixed blocks of whole rows (2**22
+elements when the row length divides it), block j from the j-th child of its stream, so the values do not depend on thread count.
   q, k ~ N(0, 1) per element, k scaled to unit L2 norm per (token, q/k head) in float32;
   v ~ N(0, 1); a ~ U(a_lo, 1); b ~ U(0, 1); initial state zero unless a test says otherwise.
   bfloat16 storage is float32 rounded to nearest even, kept as uint16 bit patterns.
@@ -133,15 +133,15 @@ def _draw(seq: np.random.SeedSequence, shape, kind: str, bf16: bool = False,
 
     size = int(np.prod(shape))
     row = shape[-1]
-    assert _BLOCK % row == 0
+    blk = _BLOCK - _BLOCK % row  # whole rows per block
     out = np.empty(shape, np.uint16 if bf16 else np.float32)
     flat = out.reshape(-1)
-    nblk = (size + _BLOCK - 1) // _BLOCK
+    nblk = (size + blk - 1) // blk
     kids = seq.spawn(nblk)
 
     def fill(j):
         g = np.random.Generator(np.random.PCG64(kids[j]))
-        m = min(_BLOCK, size - j * _BLOCK)
+        m = min(blk, size - j * blk)
         if kind == "normal":
             x = g.standard_normal(m, dtype=np.float32)
             if unit_rows:
@@ -149,7 +149,7 @@ def _draw(seq: np.random.SeedSequence, shape, kind: str, bf16: bool = False,
                 r /= np.sqrt(np.sum(r * r, axis=1, dtype=np.float32), dtype=np.float32)[:, None]
         else:
             x = g.uniform(lo, hi, m).astype(np.float32)
-        flat[j * _BLOCK:j * _BLOCK + m] = f32_to_bf16_bits(x) if bf16 else x
+        flat[j * blk:j * blk + m] = f32_to_bf16_bits(x) if bf16 else x
 
     if nblk == 1:
         fill(0)
