@@ -5,6 +5,7 @@
 // (IsoExec, aihirek.info, section on the contract and common model; agentlenshq.com,
 // section on contract structure: claims and identities).
 
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -23,13 +24,50 @@ bool aligned(const void *p, size_t bytes) {
 }
 
 // Lanes per state row: GDN_CPR_LANES_PER_ROW overrides the automatic choice.
-int lanes_per_row(int fallback) {
+int lanes_override() {
   const char *env = std::getenv("GDN_CPR_LANES_PER_ROW");
   if (env && *env) {
     const int v = std::atoi(env);
     if (v == 16 || v == 8 || v == 4) return v;
   }
-  return fallback;
+  return 0;
+}
+
+// SIMDs of the current device (4 per compute unit), read once per device.
+int64_t device_simds() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    v = 4 * cus;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Scan: the fewer the rows, the more lanes per row. A row on 16 lanes needs the most
+// instructions but gives 4x the waves of 4 lanes per row; the recurrence is serial along
+// the tokens, so with at most one wave per SIMD latency dominates and more lanes win, while
+// with many waves per SIMD issue dominates and fewer lanes (fewer reduction steps) win.
+int scan_lanes(const ScanArgs &a) {
+  if (const int o = lanes_override()) return o;
+  const int64_t rows = (int64_t)a.num_seqs * a.num_v_heads * a.d_v;
+  const int64_t simds = device_simds();
+  if (rows / 4 <= simds) return 16;  // <= 1 wave per SIMD with 16 lanes per row
+  if (rows / 8 <= simds) return 8;   // <= 1 wave per SIMD with 8 lanes per row
+  return 4;
+}
+
+// Decode streams every row once per step; 16 lanes per row keeps each lane's slice of the
+// 512-byte row at 32 bytes and gives the most loads in flight.
+int decode_lanes() {
+  if (const int o = lanes_override()) return o;
+  return 16;
 }
 
 gdn_status_t check_shape(const char *fn, const gdn_shape_t *sh, const uint8_t *identity) {
@@ -112,7 +150,7 @@ gdn_status_t scan_common(const char *fn, const gdn_shape_t *sh, const uint8_t *i
 }
 
 gdn_status_t run_scan(const char *fn, ScanArgs &args, void *stream) {
-  const int L = lanes_per_row(16);
+  const int L = scan_lanes(args);
   if (scan_grid(args, L) > kMaxInt32)
     return fail(GDN_E_SHAPE, std::string(fn) + ": num_seqs * num_v_heads * row blocks too large");
   const hipError_t e = launch_scan(args, L, static_cast<hipStream_t>(stream));
@@ -220,7 +258,7 @@ GDN_EXPORT gdn_status_t gdn_cpr_decode_step(const gdn_shape_t *shape,
   args.state = state;
   args.o = o;
   args.resync_states = resync_states;
-  const int L = gdn::lanes_per_row(16);
+  const int L = gdn::decode_lanes();
   if (gdn::decode_grid(args, L) > gdn::kMaxInt32)
     return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": num_seqs * num_v_heads * row blocks too large");
   const hipError_t e = gdn::launch_decode(args, L, static_cast<hipStream_t>(stream));

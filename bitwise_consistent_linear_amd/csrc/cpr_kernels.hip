@@ -28,7 +28,12 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kStageTokens = 16;
+// Tokens staged in LDS at a time: 32 where few waves share a SIMD (lanes per row >= 8),
+// which halves the per-stage barrier and pipeline restart; 16 where occupancy matters.
+// Both divide every admitted chunk size's multiples of 16: a chunk boundary falls on
+// token 15 or 31 of a stage.
+template <int L>
+constexpr int stage_tokens() { return L >= 8 ? 32 : 16; }
 constexpr int kMaxRankedSeqs = 1024;
 
 // ---------------------------------------------------------------------- loads and stores
@@ -178,17 +183,66 @@ __device__ int64_t first_chunk_slot(const int32_t *cu, int n, int64_t T, int C, 
 
 // ----------------------------------------------------------------------------- kernels
 
+// Raw register copy of four input elements: bf16 stays packed until it is written to LDS.
+template <bool BF16>
+struct Raw4 {
+  using type = float4;
+};
+template <>
+struct Raw4<true> {
+  using type = uint2;
+};
+
+template <bool BF16>
+__device__ __forceinline__ typename Raw4<BF16>::type load_raw4(const void *base, int64_t idx) {
+  if constexpr (BF16)
+    return *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(base) + idx);
+  else
+    return *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + idx);
+}
+
+// One input element kept raw (bf16 bits or binary32 bits) until it is written to LDS, so
+// that no arithmetic on it forces the prefetch loads to complete early.
+template <bool BF16>
+__device__ __forceinline__ uint32_t load_raw1(const void *base, int64_t idx) {
+  if constexpr (BF16)
+    return static_cast<const uint16_t *>(base)[idx];
+  else
+    return __float_as_uint(static_cast<const float *>(base)[idx]);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float widen1(uint32_t r) {
+  return __uint_as_float(BF16 ? r << 16 : r);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float4 widen4(typename Raw4<BF16>::type r) {
+  if constexpr (BF16)
+    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u),
+                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xFFFF0000u));
+  else
+    return r;
+}
+
 template <int D, int L, bool BF16, int MODE>
 __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
   constexpr int ROWS = kThreads / L;
   constexpr int M = D / L;
-  constexpr int TS = kStageTokens;
+  constexpr int TS = stage_tokens<L>();
   constexpr int GROUPS = D / 4;  // float4 groups per staged k or q vector
-  __shared__ __align__(16) float sk[TS * D];
-  __shared__ __align__(16) float sq[TS * D];
-  __shared__ float sv[TS * ROWS];
-  __shared__ float so[TS * ROWS];
-  __shared__ float sa[TS], sb[TS];
+  constexpr int KQ_ITEMS = TS * GROUPS, V_ITEMS = TS * ROWS;
+  constexpr int KQ_PER = (KQ_ITEMS + kThreads - 1) / kThreads;
+  constexpr int V_PER = (V_ITEMS + kThreads - 1) / kThreads;
+  using raw_t = typename Raw4<BF16>::type;
+
+  // Two stage buffers: stage s is computed from buffer s&1 while stage s+1 is deposited
+  // into the other, so one barrier per stage suffices.
+  __shared__ __align__(16) float sk[2][TS * D];
+  __shared__ __align__(16) float sq[2][TS * D];
+  __shared__ float sv[2][V_ITEMS];
+  __shared__ float so[2][V_ITEMS];
+  __shared__ float sa[2][TS], sb[2][TS];
   __shared__ int s_len[kMaxRankedSeqs];
   __shared__ int s_pick, s_acc;
 
@@ -221,68 +275,171 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
 #pragma unroll
     for (int e = 0; e < M; ++e) s[e] = 0.0f;
   }
-
-  auto stage = [&](int64_t t0, int nt) {
-    for (int g = tid; g < nt * GROUPS; g += kThreads) {
-      const int tt = g / GROUPS, c = g % GROUPS;
-      const int64_t src = ((bos + t0 + tt) * Hk + hk) * D + 4 * c;
-      *reinterpret_cast<float4 *>(sk + tt * D + stage_slot<D, L>(c)) = load4<BF16>(p.k, src);
-      *reinterpret_cast<float4 *>(sq + tt * D + stage_slot<D, L>(c)) = load4<BF16>(p.q, src);
-    }
-    for (int e = tid; e < nt * ROWS; e += kThreads) {
-      const int tt = e / ROWS, r = e % ROWS;
-      sv[e] = (r0 + r < dv) ? load1<BF16>(p.v, (bos + t0 + tt) * vstride + (int64_t)h * dv + r0 + r)
-                            : 0.0f;
-    }
-    for (int tt = tid; tt < nt; tt += kThreads) {
-      const int64_t ab = (bos + t0 + tt) * Hv + h;
-      sa[tt] = p.a[ab];
-      sb[tt] = p.b[ab];
-    }
-  };
-
-  auto write_o = [&](int64_t t0, int nt) {
-    for (int e = tid; e < nt * ROWS; e += kThreads) {
-      const int tt = e / ROWS, r = e % ROWS;
-      if (r0 + r < dv) p.o[(bos + t0 + tt) * vstride + (int64_t)h * dv + r0 + r] = so[e];
-    }
-  };
-
-  auto step = [&](int tt) {
-    float kr[M], qr[M];
-    lds_slice<D, L>(sk + tt * D, lane, kr);
-    lds_slice<D, L>(sq + tt * D, lane, qr);
-    const float oi = row_token<D, L>(s, sa[tt], sb[tt], sv[tt * ROWS + row], kr, qr);
-    if (lane == 0) so[tt * ROWS + row] = oi;
-  };
-
-  // Every admitted C is a multiple of the stage length and stages start at in-sequence
-  // index 0, so a chunk boundary (j + 1) % C == 0 can only be the last token of a full stage.
-  static_assert(16 % TS == 0, "stage length must divide every admitted chunk size");
-  const int chunk_shift = __builtin_ctz((unsigned)p.chunk);
-
-  if (Tn > 0) stage(0, (int)(Tn < TS ? Tn : TS));
-  __syncthreads();
-  for (int64_t t0 = 0; t0 < Tn; t0 += TS) {
-    const int nt = (int)(Tn - t0 < TS ? Tn - t0 : TS);
-    if (nt == TS) {
+  // Complete the state loads here, once: otherwise the first use of s inside the stage
+  // loop waits on the in-order load counter and with it on that stage's prefetch loads.
 #pragma unroll
-      for (int tt = 0; tt < TS; ++tt) step(tt);
-      if constexpr (MODE == kTrainer) {
-        const int64_t done = t0 + TS;  // tokens absorbed
-        if ((done & (p.chunk - 1)) == 0) {
-          const int64_t c = cbase + (done >> chunk_shift) - 1;
-          if (valid && c < p.total_chunks)
-            store_row<M>(p.chunk_states + ((c * Hv + h) * dv + i) * D + lane * M, s);
-        }
-      }
-    } else {
-      for (int tt = 0; tt < nt; ++tt) step(tt);
+  for (int e = 0; e < M; ++e) asm volatile("" ::"v"(s[e]));
+
+  // Staged inputs in registers, between their global load and their LDS deposit. Token and
+  // row indices are clamped to valid addresses so the loads need no branches; the extra
+  // values land in LDS slots that the token loop never reads.
+  raw_t rk[KQ_PER], rq[KQ_PER];
+  uint32_t rv[V_PER];
+  float ra, rb;
+  auto fetch = [&](int64_t t0) {
+    const int64_t last = Tn - 1;
+#pragma unroll
+    for (int j = 0; j < KQ_PER; ++j) {
+      const int g = (tid + j * kThreads) % KQ_ITEMS;
+      const int64_t t = t0 + g / GROUPS < last ? t0 + g / GROUPS : last;
+      const int64_t src = ((bos + t) * Hk + hk) * D + 4 * (g % GROUPS);
+      rk[j] = load_raw4<BF16>(p.k, src);
+      rq[j] = load_raw4<BF16>(p.q, src);
     }
+#pragma unroll
+    for (int j = 0; j < V_PER; ++j) {
+      const int e = (tid + j * kThreads) % V_ITEMS;
+      const int64_t t = t0 + e / ROWS < last ? t0 + e / ROWS : last;
+      const int r = r0 + e % ROWS < dv ? r0 + e % ROWS : dv - 1;
+      rv[j] = load_raw1<BF16>(p.v, (bos + t) * vstride + (int64_t)h * dv + r);
+    }
+    const int64_t t = t0 + tid % TS < last ? t0 + tid % TS : last;
+    ra = p.a[(bos + t) * Hv + h];
+    rb = p.b[(bos + t) * Hv + h];
+  };
+  auto deposit = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < KQ_PER; ++j) {
+      const int g = tid + j * kThreads;
+      if (KQ_ITEMS % kThreads == 0 || g < KQ_ITEMS) {
+        const int off = (g / GROUPS) * D + stage_slot<D, L>(g % GROUPS);
+        *reinterpret_cast<float4 *>(&sk[buf][off]) = widen4<BF16>(rk[j]);
+        *reinterpret_cast<float4 *>(&sq[buf][off]) = widen4<BF16>(rq[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < V_PER; ++j) {
+      const int e = tid + j * kThreads;
+      if (V_ITEMS % kThreads == 0 || e < V_ITEMS) sv[buf][e] = widen1<BF16>(rv[j]);
+    }
+    if (tid < TS) {
+      sa[buf][tid] = ra;
+      sb[buf][tid] = rb;
+    }
+  };
+  auto write_o = [&](int64_t t0, int nt, int buf) {
+#pragma unroll
+    for (int j = 0; j < V_PER; ++j) {
+      const int e = tid + j * kThreads;
+      const int tt = e / ROWS, r = e % ROWS;
+      if ((V_ITEMS % kThreads == 0 || e < V_ITEMS) && tt < nt && r0 + r < dv)
+        p.o[(bos + t0 + tt) * vstride + (int64_t)h * dv + r0 + r] = so[buf][e];
+    }
+  };
+  // One token of a stage, in row_token's plain order. Every lane of a row holds the same
+  // o_i and stores it (no branch), which keeps an unrolled stage in one basic block.
+  auto run_token = [&](int buf, int tt) {
+    float kr[M], qr[M];
+    lds_slice<D, L>(&sk[buf][tt * D], lane, kr);
+    lds_slice<D, L>(&sq[buf][tt * D], lane, qr);
+    so[buf][tt * ROWS + row] =
+        row_token<D, L>(s, sa[buf][tt], sb[buf][tt], sv[buf][tt * ROWS + row], kr, qr);
+  };
+
+  // A full stage, software-pipelined: the inputs of token t+2 are read from LDS while token
+  // t computes (a three-slot register ring), and token t's readout dot runs side by side
+  // with token t+1's key dot (both read only the state after token t). Every operation is
+  // one that row_token performs, on the same operands; only independent operations are
+  // interleaved, so the bits are the same. Used where few waves share a SIMD and latency,
+  // not issue, bounds the stage.
+  auto run_stage_pipelined = [&](int buf, float (&snap)[M]) {
+    float rk_[3][M], rq_[3][M], ra_[3], rb_[3], rv_[3], x[M];
+    auto load_token = [&](int tt, int slot) {
+      lds_slice<D, L>(&sk[buf][tt * D], lane, rk_[slot]);
+      lds_slice<D, L>(&sq[buf][tt * D], lane, rq_[slot]);
+      ra_[slot] = sa[buf][tt];
+      rb_[slot] = sb[buf][tt];
+      rv_[slot] = sv[buf][tt * ROWS + row];
+    };
+    load_token(0, 0);
+    load_token(1, 1);
+    row_decay<D, L>(s, ra_[0], x);
+    float u = contract_dot<D, L>(x, rk_[0]);
+#pragma unroll
+    for (int tt = 0; tt < TS; ++tt) {
+      const int cur = tt % 3, nxt = (tt + 1) % 3;
+      if (tt + 2 < TS) load_token(tt + 2, (tt + 2) % 3);
+      row_update<D, L>(s, row_delta(rb_[cur], rv_[cur], u), rk_[cur], x);
+      if (tt == 15 && TS == 32) {  // state after the stage's 16th token (a C = 16 boundary)
+#pragma unroll
+        for (int e = 0; e < M; ++e) snap[e] = s[e];
+      }
+      float o;
+      if (tt + 1 < TS) {
+        row_decay<D, L>(s, ra_[nxt], x);
+        float xs[2][M], ys[2][M], r[2];
+#pragma unroll
+        for (int e = 0; e < M; ++e) {
+          xs[0][e] = s[e];
+          ys[0][e] = rq_[cur][e];
+          xs[1][e] = x[e];
+          ys[1][e] = rk_[nxt][e];
+        }
+        contract_dots<D, L, 2>(xs, ys, r);
+        o = r[0];
+        u = r[1];
+      } else {
+        o = contract_dot<D, L>(s, rq_[cur]);
+      }
+      so[buf][tt * ROWS + row] = o;
+    }
+  };
+
+  // Stages start at in-sequence index 0 and every admitted C is a multiple of 16, so a chunk
+  // boundary (j + 1) % C == 0 falls on token 15 or 31 of a stage. `done` = tokens absorbed.
+  const int chunk_shift = __builtin_ctz((unsigned)p.chunk);
+  auto store_chunk_state = [&](int64_t done, const float (&st)[M]) {
+    if constexpr (MODE == kTrainer) {
+      if ((done & (p.chunk - 1)) == 0) {
+        const int64_t c = cbase + (done >> chunk_shift) - 1;
+        if (valid && c < p.total_chunks)
+          store_row<M>(p.chunk_states + ((c * Hv + h) * dv + i) * D + lane * M, st);
+      }
+    }
+  };
+  const int64_t nstages = (Tn + TS - 1) / TS;
+
+  if (Tn > 0) {
+    fetch(0);
+    deposit(0);
+  }
+  __syncthreads();
+  for (int64_t st = 0; st < nstages; ++st) {
+    const int buf = (int)(st & 1);
+    const int64_t t0 = st * TS;
+    const int nt = (int)(Tn - t0 < TS ? Tn - t0 : TS);
+    const bool more = st + 1 < nstages;
+    if (more) fetch(t0 + TS);  // global loads in flight while this stage computes
+    if (nt == TS) {
+      if constexpr (L >= 8) {
+        float snap[M];
+        run_stage_pipelined(buf, snap);
+        if constexpr (TS == 32) store_chunk_state(t0 + 16, snap);
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < TS; ++tt) run_token(buf, tt);
+      }
+      store_chunk_state(t0 + TS, s);
+    } else {
+#pragma unroll 1
+      for (int tt = 0; tt < nt; ++tt) {
+        run_token(buf, tt);
+        store_chunk_state(t0 + tt + 1, s);
+      }
+    }
+    if (more) deposit(buf ^ 1);
     __syncthreads();
-    write_o(t0, nt);
-    if (t0 + TS < Tn) stage(t0 + TS, (int)(Tn - t0 - TS < TS ? Tn - t0 - TS : TS));
-    __syncthreads();
+    write_o(t0, nt, buf);
   }
   if constexpr (MODE == kPrefill) {
     if (valid) store_row<M>(p.final_state + row_off, s);

@@ -43,28 +43,82 @@ struct RowShape {
   static constexpr int W = D / 16;  // leaf width
 };
 
-// Contract dot product of the row slice x with the matching slice y of k or q.
-template <int D, int L>
-__device__ __forceinline__ float contract_dot(const float (&x)[D / L], const float (&y)[D / L]) {
+// N contract dot products computed side by side: dot n of the row slice x[n] with the
+// matching slice y[n] of k or q. Each dot performs exactly the contract's sequence of
+// operations (the same for every N); computing several together only lets independent
+// instructions fill each other's latencies and DPP wait states.
+template <int D, int L, int N>
+__device__ __forceinline__ void contract_dots(const float (&x)[N][D / L],
+                                              const float (&y)[N][D / L], float (&r)[N]) {
   constexpr int P = RowShape<D, L>::P, W = RowShape<D, L>::W;
-  float leaf[P];
+  float leaf[N][P];
 #pragma unroll
-  for (int p = 0; p < P; ++p) {
-    float acc = x[p * W] * y[p * W];
+  for (int p = 0; p < P; ++p)
 #pragma unroll
-    for (int e = 1; e < W; ++e) acc = __builtin_fmaf(x[p * W + e], y[p * W + e], acc);
-    leaf[p] = acc;
-  }
+    for (int n = 0; n < N; ++n) leaf[n][p] = x[n][p * W] * y[n][p * W];
+#pragma unroll
+  for (int e = 1; e < W; ++e)
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int n = 0; n < N; ++n)
+        leaf[n][p] = __builtin_fmaf(x[n][p * W + e], y[n][p * W + e], leaf[n][p]);
 #pragma unroll
   for (int w = 1; w < P; w *= 2)
 #pragma unroll
-    for (int p = 0; p < P; p += 2 * w) leaf[p] = leaf[p] + leaf[p + w];
-  float r = leaf[0];
-  if constexpr (L >= 2) r = r + dpp_partner<kDppQuadXor1>(r);
-  if constexpr (L >= 4) r = r + dpp_partner<kDppQuadXor2>(r);
-  if constexpr (L >= 8) r = r + dpp_partner<kDppRowHalfMirror>(r);
-  if constexpr (L >= 16) r = r + dpp_partner<kDppRowMirror>(r);
-  return r;
+    for (int p = 0; p < P; p += 2 * w)
+#pragma unroll
+      for (int n = 0; n < N; ++n) leaf[n][p] = leaf[n][p] + leaf[n][p + w];
+#pragma unroll
+  for (int n = 0; n < N; ++n) r[n] = leaf[n][0];
+  if constexpr (L >= 2) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) r[n] = r[n] + dpp_partner<kDppQuadXor1>(r[n]);
+  }
+  if constexpr (L >= 4) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) r[n] = r[n] + dpp_partner<kDppQuadXor2>(r[n]);
+  }
+  if constexpr (L >= 8) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) r[n] = r[n] + dpp_partner<kDppRowHalfMirror>(r[n]);
+  }
+  if constexpr (L >= 16) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) r[n] = r[n] + dpp_partner<kDppRowMirror>(r[n]);
+  }
+}
+
+template <int D, int L>
+__device__ __forceinline__ float contract_dot(const float (&x)[D / L], const float (&y)[D / L]) {
+  constexpr int M = RowShape<D, L>::M;
+  float xs[1][M], ys[1][M], r[1];
+#pragma unroll
+  for (int e = 0; e < M; ++e) {
+    xs[0][e] = x[e];
+    ys[0][e] = y[e];
+  }
+  contract_dots<D, L, 1>(xs, ys, r);
+  return r[0];
+}
+
+// The steps of one token on one row (s: the row's slice in this lane).
+template <int D, int L>
+__device__ __forceinline__ void row_decay(const float (&s)[D / L], float a, float (&x)[D / L]) {
+#pragma unroll
+  for (int e = 0; e < RowShape<D, L>::M; ++e) x[e] = a * s[e];
+}
+
+__device__ __forceinline__ float row_delta(float b, float v_i, float u) {
+  const float diff = v_i - u;
+  return b * diff;
+}
+
+template <int D, int L>
+__device__ __forceinline__ void row_update(float (&s)[D / L], float delta, const float (&k)[D / L],
+                                           const float (&x)[D / L]) {
+#pragma unroll
+  for (int e = 0; e < RowShape<D, L>::M; ++e) s[e] = __builtin_fmaf(delta, k[e], x[e]);
 }
 
 // One token on one row: decay, key dot, delta, fused rank-1 update, query readout.
@@ -72,15 +126,10 @@ __device__ __forceinline__ float contract_dot(const float (&x)[D / L], const flo
 template <int D, int L>
 __device__ __forceinline__ float row_token(float (&s)[D / L], float a, float b, float v_i,
                                            const float (&k)[D / L], const float (&q)[D / L]) {
-  constexpr int M = RowShape<D, L>::M;
-  float x[M];
-#pragma unroll
-  for (int e = 0; e < M; ++e) x[e] = a * s[e];
+  float x[RowShape<D, L>::M];
+  row_decay<D, L>(s, a, x);
   const float u = contract_dot<D, L>(x, k);
-  const float diff = v_i - u;
-  const float delta = b * diff;
-#pragma unroll
-  for (int e = 0; e < M; ++e) s[e] = __builtin_fmaf(delta, k[e], x[e]);
+  row_update<D, L>(s, row_delta(b, v_i, u), k, x);
   return contract_dot<D, L>(s, q);
 }
 

@@ -38,7 +38,8 @@
  * Sequence n owns tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of the packed batch.
  *
  * OWNERSHIP, STREAMS, ERRORS. The caller allocates every buffer; the library allocates
- * and frees no device memory and keeps no state between calls. Work is enqueued on the
+ * and frees no device memory and keeps no state between calls other than a per-device
+ * cache of the compute-unit count, read once. Work is enqueued on the
  * hipStream_t passed as `stream` (NULL = the null stream) of the current HIP device; the
  * calls return before the work finishes. All argument checks run on the host before
  * anything is enqueued, so a non-GDN_OK status means nothing was launched, except
@@ -49,9 +50,11 @@
  * state of decode). gdn_last_error() returns text for the calling thread's last error.
  * All functions are thread-safe.
  *
- * TUNING. The environment variable GDN_CPR_LANES_PER_ROW (16, 8 or 4) overrides how many
- * lanes of a wavefront share one state row; the contract makes every admitted value give
- * the same bits, which the tests check.
+ * TUNING. How many lanes of a wavefront share one state row is chosen per call from the
+ * number of rows: 16 when that gives at most one wavefront per SIMD, 8 when 8 lanes do, 4
+ * otherwise (decode: 16). The environment variable GDN_CPR_LANES_PER_ROW (16, 8 or 4)
+ * overrides the choice; the contract makes every admitted value give the same bits, which
+ * the tests check.
  */
 #ifndef GDN_CPR_H
 #define GDN_CPR_H
