@@ -30,6 +30,7 @@ FP32_FMA_PEAK_TFLOPS = 78.6       # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GH
 FP32_PACKED_PEAK_TFLOPS = 157.3   # spec-sheet figure with packed fp32 (not used by these kernels)
 METRIC = "GDN-CPR tokens/s (trainer_fwd, prefill), decode-step us, % of HBM peak"
 KERNEL_SOURCES = ["cpr_kernels.hip", "cpr_row.hpp"]
+COPY_PROBE_BYTES = 256 << 20  # read once and written once by the calibration copy
 
 
 def log(msg):
@@ -118,6 +119,59 @@ def traffic_for(name, launches_bytes_fn=None):
     if t.get("kernel_source_sha256") != kernel_source_digest():
         return None
     return int(t["hbm_bytes_per_launch"])
+
+
+def write_traffic(fetch_csv, write_csv, kernel_substr="cpr_scan_kernel", name="cpr_scan_trainer_fwd"):
+    """From two rocprofv3 --pmc runs of `bench.py --cases main --copy-probe` (FETCH_SIZE,
+    then WRITE_SIZE; KiB per dispatch), write profiles/<name>_traffic.json: the kernel's HBM
+    bytes per launch, each counter scaled by what it reads for the 256 MiB calibration copy
+    (read once, written once)."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        copy = [float(r["Counter_Value"]) for r in rows
+                if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) > 1024]
+        kern = [float(r["Counter_Value"]) for r in rows if kernel_substr in r["Kernel_Name"]]
+        knames = sorted({r["Kernel_Name"] for r in rows if kernel_substr in r["Kernel_Name"]})
+        if not copy or not kern:
+            raise SystemExit(f"{path}: no calibration copy or no {kernel_substr} dispatch")
+        return statistics.median(copy), statistics.median(kern), len(kern), knames
+
+    cf, kf, nf, names = per_kernel(fetch_csv, "FETCH_SIZE")
+    cw, kw, nw, _ = per_kernel(write_csv, "WRITE_SIZE")
+    fetch_scale = COPY_PROBE_BYTES / (cf * 1024)
+    write_scale = COPY_PROBE_BYTES / (cw * 1024)
+    fetch_b = kf * 1024 * fetch_scale
+    write_b = kw * 1024 * write_scale
+    from bitwise_consistent_linear_amd import workloads as W
+    w = W.trainer_fwd()
+    out = {
+        "kernel": names,
+        "workload": "trainer_fwd: 4 x 4096 tokens, 16 heads, d=128, C=64, bf16 q/k/v",
+        "kernel_source_sha256": kernel_source_digest(),
+        "fetch_size_kib_per_launch": kf, "write_size_kib_per_launch": kw,
+        "dispatches_counted": [nf, nw],
+        "calibration_copy_bytes": COPY_PROBE_BYTES,
+        "calibration_fetch_kib": cf, "calibration_write_kib": cw,
+        "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+        "hbm_fetch_bytes_per_launch": int(fetch_b), "hbm_write_bytes_per_launch": int(write_b),
+        "hbm_bytes_per_launch": int(fetch_b + write_b),
+        "algorithmic_bytes_per_launch": int(scan_bytes(w, chunk_states=w.total_chunks)),
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o fetch -- python3 bench.py "
+            "--cases main --no-cpu-baseline --steps 3 --warmup 1 --copy-probe",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o write -- python3 bench.py "
+            "--cases main --no-cpu-baseline --steps 3 --warmup 1 --copy-probe",
+            "python3 bench.py --traffic-from <dir>/fetch_counter_collection.csv "
+            "<dir>/write_counter_collection.csv"],
+    }
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 # ------------------------------------------------------------------------------ cases
@@ -275,7 +329,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cases", choices=["all", "main"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (untimed), the known-size "
+                         "reference that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/cpr_scan_trainer_fwd_traffic.json from two rocprofv3 "
+                         "counter CSVs and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (every state "
               "row is independent; see DESIGN.md for how the work would shard).",
@@ -288,6 +351,13 @@ def main():
     api.lib()
     log(f"device: {torch.cuda.get_device_name(0)}")
 
+    if args.copy_probe:
+        x = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
     w, wall, kernel_ms, flops, nbytes = bench_trainer(args.steps, args.warmup)
     ms_per_step = wall / args.steps * 1e3
     roof = roofline_alu(flops, kernel_ms)

@@ -166,6 +166,25 @@ __device__ int ranked_sequence(const int32_t *cu, int N, int64_t T, int rank, in
   return *s_pick;
 }
 
+// Workgroup -> (head pair, row block), XCD-aware. The dispatcher hands workgroups to the
+// 8 XCDs (each with its own L2) in round-robin order of workgroup id. Pairs (work units of
+// one sequence and value head, in scheduling order) are taken 8 at a time; within such a
+// group, pair g*8+x gets every workgroup id congruent to x mod 8, so all row blocks of a
+// pair run on one XCD and read its q, k, a and b through one L2. A last group of fewer than
+// 8 pairs is laid out linearly.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ void block_work(int b, int pairs, int rblocks, int &pair, int &rb) {
+  const int group = b / (kXcds * rblocks), within = b % (kXcds * rblocks);
+  if (group < pairs / kXcds) {
+    pair = group * kXcds + within % kXcds;
+    rb = within / kXcds;
+  } else {
+    pair = group * kXcds + within / rblocks;
+    rb = within % rblocks;
+  }
+}
+
 // Index of sequence n's first chunk-boundary state: sum over m < n of floor(T_m / C).
 __device__ int64_t first_chunk_slot(const int32_t *cu, int n, int64_t T, int C, int *s_acc) {
   if (threadIdx.x == 0) *s_acc = 0;
@@ -249,10 +268,11 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
   const int tid = threadIdx.x, row = tid / L, lane = tid % L;
   const int Hv = p.num_v_heads, Hk = p.num_qk_heads, dv = p.d_v;
   const int rblocks = (dv + ROWS - 1) / ROWS;
-  const int per_seq = Hv * rblocks;
-  const int rank = blockIdx.x / per_seq;
-  const int h = (blockIdx.x % per_seq) / rblocks;
-  const int r0 = (blockIdx.x % rblocks) * ROWS;
+  int pair, rblock;
+  block_work(blockIdx.x, p.num_seqs * Hv, rblocks, pair, rblock);
+  const int rank = pair / Hv;
+  const int h = pair % Hv;
+  const int r0 = rblock * ROWS;
   const int64_t T = p.total_tokens;
 
   const int n = ranked_sequence(p.cu_seqlens, p.num_seqs, T, rank, s_len, &s_pick);
@@ -453,10 +473,11 @@ __global__ __launch_bounds__(kThreads) void cpr_decode_kernel(const DecodeArgs p
   const int tid = threadIdx.x, row = tid / L, lane = tid % L;
   const int Hv = p.num_v_heads, Hk = p.num_qk_heads, dv = p.d_v;
   const int rblocks = (dv + ROWS - 1) / ROWS;
-  const int per_seq = Hv * rblocks;
-  const int n = blockIdx.x / per_seq;
-  const int h = (blockIdx.x % per_seq) / rblocks;
-  const int i = (blockIdx.x % rblocks) * ROWS + row;
+  int pair, rblock;
+  block_work(blockIdx.x, p.num_seqs * Hv, rblocks, pair, rblock);
+  const int n = pair / Hv;
+  const int h = pair % Hv;
+  const int i = rblock * ROWS + row;
   const int pos = p.pos[n];
   if (pos < 0) return;  // idle slot: uniform over the workgroup
   const bool valid = i < dv;
