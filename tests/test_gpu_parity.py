@@ -292,3 +292,79 @@ def test_config_long_context():
         if (t + 1) % 64 == 0:
             assert_dev_equal(rs, cs[(t + 1) // 64 - 1:(t + 1) // 64], f"long resync step {s}")
     sampled_oracle(w, [(0, 0), (0, 31)], o, cs, fs)
+
+
+# ------------------------------------------------------------------ more edge cases
+
+def test_many_sequences_unranked_path():
+    # more than 1024 sequences: workgroups take sequences in natural order (no length rank)
+    g = np.random.default_rng(21)
+    lengths = g.integers(0, 40, 1100)
+    w = W.make_packed("many", lengths, Hk=1, Hv=2, d=32, chunk=16, bf16=True, seed=21)
+    log(f"many sequences: N={w.num_seqs} T={w.total_tokens}")
+    ro, rcs, rfs = O.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=16,
+                          want_chunk_states=True, want_final_state=True)
+    d = up_workload(w)
+    for L in LANES:
+        with lanes(L):
+            o, cs = run_trainer(w, d)
+            po, fs = run_prefill(w, d)
+        assert_bits(o, ro, f"many L={L} trainer o")
+        assert_bits(cs, rcs, f"many L={L} chunk states")
+        assert_bits(po, ro, f"many L={L} prefill o")
+        assert_bits(fs, rfs, f"many L={L} final")
+
+
+def test_subnormal_states_kept():
+    # a tiny decay drives the state into the binary32 subnormal range; the contract keeps
+    # denormals, so GPU and oracle must agree bit for bit there too
+    w, s0 = small_workload("subnormal", [48, 20], 1, 2, 64, 64, 16, False, True)
+    w.a[:] = np.float32(2.0 ** -20)
+    w.b[:] = np.float32(2.0 ** -60)
+    w.v *= np.float32(2.0 ** -70)
+    ro, rcs, rfs = O.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=16, initial_state=s0,
+                          want_chunk_states=True, want_final_state=True)
+    tiny = np.abs(rfs[rfs != 0])
+    assert tiny.size and (tiny < np.float32(2.0 ** -126)).mean() > 0.5, "case must reach subnormals"
+    d = up_workload(w)
+    for L in LANES:
+        with lanes(L):
+            o, cs = run_trainer(w, d, up(s0))
+            po, fs = run_prefill(w, d, up(s0))
+        assert_bits(o, ro, f"subnormal L={L} o")
+        assert_bits(cs, rcs, f"subnormal L={L} chunk states")
+        assert_bits(fs, rfs, f"subnormal L={L} final")
+
+
+def test_onehot_closed_form_on_gpu():
+    # exact arithmetic: one-hot k and q, a in {1, 1/2}, b in {0, 1}, small-integer v and S0
+    import oracle_pins
+    cu, q, k, v, a, b, s0, kap, rho = oracle_pins.onehot_case(T=40, Hk=2, Hv=4, d=32, seed=9)
+    ro, rcs, rfs = O.scan(cu, q, k, v, a, b, chunk=16, initial_state=s0,
+                          want_chunk_states=True, want_final_state=True)
+    dcu, dq, dk, dv, da, db = map(up, (cu, q, k, v, a, b))
+    for L in LANES:
+        with lanes(L):
+            o, cs = api.trainer_fwd(dcu, dq, dk, dv, da, db, chunk=16, initial_state=up(s0))
+        assert_bits(o, ro, f"one-hot L={L} o")
+        assert_bits(cs, rcs, f"one-hot L={L} chunk states")
+
+
+@pytest.mark.parametrize("chunk", [16, 128, 256])
+def test_config_trainer_fwd_other_chunks(chunk):
+    # C changes only which states are emitted: o is the same bits for every C, and every
+    # emitted state equals the C=64 run's state at the same token
+    w = W.trainer_fwd()
+    d = up_workload(w)
+    o64, cs64 = run_trainer(w, d)
+    w.chunk = chunk
+    o, cs = run_trainer(w, d)
+    assert_dev_equal(o, o64, f"C={chunk} vs C=64 o")
+    per = 4096 // chunk
+    a = cs.view(4, per, 16, 128, 128)
+    b = cs64.view(4, 64, 16, 128, 128)
+    if chunk < 64:
+        assert_dev_equal(a[:, 64 // chunk - 1::64 // chunk].contiguous(), b, "boundary states")
+    else:
+        assert_dev_equal(a, b[:, chunk // 64 - 1::chunk // 64].contiguous(), "boundary states")
+    sampled_oracle(w, [(2, 9)], o, cs)
