@@ -250,12 +250,31 @@ def bench_decode_after_prefill(w, prefix, nsteps, warmup_steps, label):
 
     wall, per = timed(step, nsteps, warmup_steps)
     ms = sum(per) / len(per)
+    # The same steps captured in one HIP graph and replayed: what an engine that captures
+    # its decode loop sees, without the per-call host work of the Python binding.
+    g = torch.cuda.CUDAGraph()
+    first = warmup_steps
+    with torch.cuda.graph(g):
+        for s in range(first, first + nsteps):
+            api.decode_step(ds["pos"][s], ds["q"][s], ds["k"][s], ds["v"][s], ds["a"][s],
+                            ds["b"][s], state, chunk=w.chunk, o=o, resync_states=rs)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / nsteps
+    del g
     nbytes = decode_step_bytes(N, w.num_qk_heads, w.num_v_heads, w.d_k, w.d_v,
                                2 if w.bf16 else 4, w.chunk)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    log(f"{label}: {nsteps} decode steps, {ms * 1e3:.1f} us/step (events)")
+    log(f"{label}: {nsteps} decode steps, {ms * 1e3:.1f} us/step (events per call), "
+        f"{graph_us:.1f} us/step (HIP graph)")
     return {"us_per_step_kernel": round(ms * 1e3, 2),
-            "us_per_step_wall": round(wall / nsteps * 1e6, 2), "steps": nsteps,
+            "us_per_step_wall": round(wall / nsteps * 1e6, 2),
+            "us_per_step_hip_graph": round(graph_us, 2), "steps": nsteps,
             "warmup_steps": warmup_steps,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},

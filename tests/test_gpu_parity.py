@@ -368,3 +368,45 @@ def test_config_trainer_fwd_other_chunks(chunk):
     else:
         assert_dev_equal(a, b[:, chunk // 64 - 1::chunk // 64].contiguous(), "boundary states")
     sampled_oracle(w, [(2, 9)], o, cs)
+
+
+def test_decode_steps_in_hip_graph_match_eager():
+    # Decode steps captured once into a HIP graph (the library only launches kernels on the
+    # caller's stream) and replayed: every replay, run after eager work and a sync, must
+    # give the bits of the same steps run eagerly.
+    w = W.make_packed("graph", [40] * 6, Hk=2, Hv=4, d=64, chunk=16, bf16=True, seed=31)
+    pre, steps = W.split_for_decode(w, 24)
+    dst = up_steps(steps)
+    _, s_start = run_prefill(pre, up_workload(pre))
+    S = dst["q"].shape[0]
+    # eager reference
+    st = s_start.clone()
+    ref_o, ref_rs = [], []
+    for s, o, rs in decode_steps(dst, st, 16):
+        ref_o.append(o.clone())
+        ref_rs.append(rs.clone())
+    ref_state = st.clone()
+    # capture
+    state = s_start.clone()
+    outs = [torch.empty_like(ref_o[0]) for _ in range(S)]
+    rss = [torch.empty_like(state) for _ in range(S)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in range(S):
+            api.decode_step(dst["pos"][s], dst["q"][s], dst["k"][s], dst["v"][s], dst["a"][s],
+                            dst["b"][s], state, chunk=16, o=outs[s], resync_states=rss[s])
+    for replay in range(3):
+        junk = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        state.copy_(s_start)
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        del junk
+        for s in range(S):
+            assert_dev_equal(outs[s], ref_o[s], f"replay {replay} step {s} o")
+            if (24 + s + 1) % 16 == 0:
+                assert_dev_equal(rss[s], ref_rs[s], f"replay {replay} step {s} resync")
+        assert_dev_equal(state, ref_state, f"replay {replay} final state")
