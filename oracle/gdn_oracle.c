@@ -274,3 +274,206 @@ int oracle_decode_step(int N, int Hk, int Hv, int dk, int dv, int C, int dtype,
 
 /* The contract dot product on its own, exposed so that tests can pin the reduction order. */
 float oracle_dot(const float *x, const float *y, int d) { return contract_dot(x, y, d); }
+
+/* ========================================================================================
+ * Backward of the recurrence (gradients of a loss L given dL/do and dL/dS_final).
+ *
+ * The pages give no backward; this is the exact derivative of the forward above, taken in
+ * this reading's fixed binary32 order. Per row i of (n, h), with sh = dL/ds (d_k values,
+ * starting from dS_final's row or +0), for t = T_n-1 down to 0, g = do[t,h,i], and the
+ * forward quantities of token t (x = a*s_{t-1}, u, diff = v_i - u, delta = b*diff, s_t)
+ * recomputed in the forward order:
+ *   sh_e  = fmaf(g, q_e, sh_e)                    dL/ds_t including o_t = s_t . q
+ *   pq_e  = g * s_t,e                             row's share of dq_t
+ *   dh    = dot(sh, k)                            dL/d delta (contract dot)
+ *   dv_i  = b * dh                                dL/dv_i
+ *   pb    = dh * diff                             row's share of db_t
+ *   uh    = -dv_i                                 dL/du
+ *   xh_e  = fmaf(uh, k_e, sh_e)                   dL/dx
+ *   pk_e  = fmaf(uh, x_e, delta * sh_e)           row's share of dk_t
+ *   pa    = dot(xh, s_{t-1})                      row's share of da_t (contract dot)
+ *   sh_e  = a * xh_e                              dL/ds_{t-1}
+ * dS0 row = sh after t = 0. The shares are summed over the d_v rows of (n, h) by a pairwise
+ * tree in natural row order in which a pair whose second half holds no row passes the first
+ * half through unchanged; dq and dk then sum the value heads of a q/k group left to right.
+ * ======================================================================================== */
+
+static void row_forward(float *s, int dk, float a, float b, float v_i, const float *k,
+                        float *x_out, float *u_out, float *diff_out, float *delta_out) {
+  for (int e = 0; e < dk; ++e) x_out[e] = a * s[e];
+  float u = contract_dot(x_out, k, dk);
+  float diff = v_i - u;
+  float delta = b * diff;
+  for (int e = 0; e < dk; ++e) s[e] = fmaf(delta, k[e], x_out[e]);
+  *u_out = u;
+  *diff_out = diff;
+  *delta_out = delta;
+}
+
+/* pairwise tree over `count` present rows, stride `stride` between row values */
+static float row_tree(float *vals, int count, int stride) {
+  int P = 1;
+  while (P < count) P *= 2;
+  for (int w = 1; w < P; w *= 2)
+    for (int j = 0; j + w < count; j += 2 * w) vals[(int64_t)j * stride] =
+        vals[(int64_t)j * stride] + vals[(int64_t)(j + w) * stride];
+  return vals[0];
+}
+
+typedef struct {
+  int N, Hk, Hv, dk, dv, C, dtype;
+  const int32_t *cu;
+  const void *q, *k, *v;
+  const float *a, *b, *S0, *dO, *dSf;
+  float *dq, *dkk, *dvv, *da, *db, *dS0;
+  int ngroups; /* (n, hk) pairs */
+} bwd_job;
+
+typedef struct {
+  const bwd_job *job;
+  int begin, end;
+  int rc;
+} bwd_slice;
+
+static void backward_group(const bwd_job *J, int grp) {
+  const int n = grp / J->Hk, hk = grp % J->Hk;
+  const int G = J->Hv / J->Hk, dk = J->dk, dv = J->dv, C = J->C;
+  const int64_t bos = J->cu[n], Tn = (int64_t)J->cu[n + 1] - J->cu[n];
+  /* per value head of the group: its dq, dk shares summed over rows, [Tn][dk] each */
+  float *DQh = calloc((size_t)G * (Tn ? Tn : 1) * dk, sizeof(float));
+  float *DKh = calloc((size_t)G * (Tn ? Tn : 1) * dk, sizeof(float));
+  int64_t nck = Tn / C + 1; /* states at in-sequence positions 0, C, 2C, ... (start of each block) */
+  float *ck = malloc(sizeof(float) * (size_t)nck * dv * dk);
+  float *blk = malloc(sizeof(float) * (size_t)(C + 1) * dv * dk); /* states s_{t0-1} .. s_{t0+C-1} */
+  float *sh = malloc(sizeof(float) * (size_t)dv * dk);
+  float *pq = malloc(sizeof(float) * (size_t)dv * dk), *pk = malloc(sizeof(float) * (size_t)dv * dk);
+  float *pa = malloc(sizeof(float) * dv), *pb = malloc(sizeof(float) * dv);
+  float kq[ORACLE_MAX_D], qq[ORACLE_MAX_D], x[ORACLE_MAX_D], xh[ORACLE_MAX_D];
+  if (!DQh || !DKh || !ck || !blk || !sh || !pq || !pk || !pa || !pb) goto done;
+  for (int g = 0; g < G; ++g) {
+    const int h = hk * G + g;
+    /* forward, keeping the state at the start of every C-token block */
+    float *s = blk;
+    for (int i = 0; i < dv; ++i)
+      for (int e = 0; e < dk; ++e)
+        s[(int64_t)i * dk + e] = J->S0 ? J->S0[(((int64_t)n * J->Hv + h) * dv + i) * dk + e] : 0.0f;
+    for (int64_t j = 0; j < Tn; ++j) {
+      if (j % C == 0) memcpy(ck + (j / C) * dv * dk, s, sizeof(float) * dv * dk);
+      const int64_t t = bos + j;
+      for (int e = 0; e < dk; ++e) kq[e] = load_widened(J->k, (t * J->Hk + hk) * (int64_t)dk + e, J->dtype);
+      const float A = J->a[t * J->Hv + h], B = J->b[t * J->Hv + h];
+      for (int i = 0; i < dv; ++i) {
+        float u, diff, delta;
+        const float v_i = load_widened(J->v, (t * J->Hv + h) * (int64_t)dv + i, J->dtype);
+        row_forward(s + (int64_t)i * dk, dk, A, B, v_i, kq, x, &u, &diff, &delta);
+      }
+    }
+    /* backward, block by block from the end, recomputing each block's states */
+    for (int i = 0; i < dv; ++i)
+      for (int e = 0; e < dk; ++e)
+        sh[(int64_t)i * dk + e] = J->dSf ? J->dSf[(((int64_t)n * J->Hv + h) * dv + i) * dk + e] : 0.0f;
+    for (int64_t blk0 = (Tn - 1) / C * C; Tn > 0 && blk0 >= 0; blk0 -= C) {
+      const int64_t len = Tn - blk0 < C ? Tn - blk0 : C;
+      memcpy(blk, ck + (blk0 / C) * dv * dk, sizeof(float) * dv * dk);
+      for (int64_t j = 0; j < len; ++j) {
+        const int64_t t = bos + blk0 + j;
+        memcpy(blk + (j + 1) * dv * dk, blk + j * dv * dk, sizeof(float) * dv * dk);
+        for (int e = 0; e < dk; ++e) kq[e] = load_widened(J->k, (t * J->Hk + hk) * (int64_t)dk + e, J->dtype);
+        const float A = J->a[t * J->Hv + h], B = J->b[t * J->Hv + h];
+        for (int i = 0; i < dv; ++i) {
+          float u, diff, delta;
+          const float v_i = load_widened(J->v, (t * J->Hv + h) * (int64_t)dv + i, J->dtype);
+          row_forward(blk + (j + 1) * dv * dk + (int64_t)i * dk, dk, A, B, v_i, kq, x, &u, &diff, &delta);
+        }
+      }
+      for (int64_t j = len - 1; j >= 0; --j) {
+        const int64_t t = bos + blk0 + j;
+        for (int e = 0; e < dk; ++e) {
+          kq[e] = load_widened(J->k, (t * J->Hk + hk) * (int64_t)dk + e, J->dtype);
+          qq[e] = load_widened(J->q, (t * J->Hk + hk) * (int64_t)dk + e, J->dtype);
+        }
+        const float A = J->a[t * J->Hv + h], B = J->b[t * J->Hv + h];
+        for (int i = 0; i < dv; ++i) {
+          const float *s_prev = blk + j * dv * dk + (int64_t)i * dk;
+          float s_cur[ORACLE_MAX_D];
+          memcpy(s_cur, s_prev, sizeof(float) * dk);
+          float u, diff, delta;
+          const float v_i = load_widened(J->v, (t * J->Hv + h) * (int64_t)dv + i, J->dtype);
+          row_forward(s_cur, dk, A, B, v_i, kq, x, &u, &diff, &delta);
+          const float gg = J->dO[(t * J->Hv + h) * (int64_t)dv + i];
+          float *shr = sh + (int64_t)i * dk;
+          for (int e = 0; e < dk; ++e) shr[e] = fmaf(gg, qq[e], shr[e]);
+          for (int e = 0; e < dk; ++e) pq[(int64_t)i * dk + e] = gg * s_cur[e];
+          const float dh = contract_dot(shr, kq, dk);
+          const float dvi = B * dh;
+          J->dvv[(t * J->Hv + h) * (int64_t)dv + i] = dvi;
+          pb[i] = dh * diff;
+          const float uh = -dvi;
+          for (int e = 0; e < dk; ++e) xh[e] = fmaf(uh, kq[e], shr[e]);
+          for (int e = 0; e < dk; ++e) {
+            const float ds = delta * shr[e];
+            pk[(int64_t)i * dk + e] = fmaf(uh, x[e], ds);
+          }
+          pa[i] = contract_dot(xh, s_prev, dk);
+          for (int e = 0; e < dk; ++e) shr[e] = A * xh[e];
+        }
+        J->da[t * J->Hv + h] = row_tree(pa, dv, 1);
+        J->db[t * J->Hv + h] = row_tree(pb, dv, 1);
+        for (int e = 0; e < dk; ++e) {
+          DQh[((int64_t)g * Tn + (t - bos)) * dk + e] = row_tree(pq + e, dv, dk);
+          DKh[((int64_t)g * Tn + (t - bos)) * dk + e] = row_tree(pk + e, dv, dk);
+        }
+      }
+    }
+    for (int i = 0; i < dv; ++i)
+      memcpy(J->dS0 + (((int64_t)n * J->Hv + h) * dv + i) * dk, sh + (int64_t)i * dk, sizeof(float) * dk);
+  }
+  /* q/k group: value heads left to right */
+  for (int64_t j = 0; j < Tn; ++j)
+    for (int e = 0; e < dk; ++e) {
+      float accq = DQh[j * dk + e], acck = DKh[j * dk + e];
+      for (int g = 1; g < G; ++g) {
+        accq = accq + DQh[((int64_t)g * Tn + j) * dk + e];
+        acck = acck + DKh[((int64_t)g * Tn + j) * dk + e];
+      }
+      J->dq[((bos + j) * J->Hk + hk) * (int64_t)dk + e] = accq;
+      J->dkk[((bos + j) * J->Hk + hk) * (int64_t)dk + e] = acck;
+    }
+done:
+  free(DQh); free(DKh); free(ck); free(blk); free(sh); free(pq); free(pk); free(pa); free(pb);
+}
+
+static void *bwd_worker(void *arg) {
+  bwd_slice *S = (bwd_slice *)arg;
+  for (int g = S->begin; g < S->end; ++g) backward_group(S->job, g);
+  return NULL;
+}
+
+/*
+ * Gradients of the recurrence over a packed batch. Inputs as for oracle_scan, plus
+ * dO [T, Hv, dv] and dS_final [N, Hv, dv, dk] (NULL = 0). Outputs: dq, dk [T, Hk, dk];
+ * dv [T, Hv, dv]; da, db [T, Hv]; dS0 [N, Hv, dv, dk]. Threads over (sequence, q/k head).
+ */
+int oracle_backward(int N, int Hk, int Hv, int dk, int dv, int C, int dtype,
+                    const int32_t *cu_seqlens, const void *q, const void *k, const void *v,
+                    const float *a, const float *b, const float *S0, const float *dO,
+                    const float *dS_final, float *dq, float *dk_out, float *dv_out, float *da,
+                    float *db, float *dS0, int nthreads) {
+  if (check_dims(N, Hk, Hv, dk, dv, C, dtype)) return -1;
+  bwd_job J = {N, Hk, Hv, dk, dv, C, dtype, cu_seqlens, q, k, v, a, b, S0, dO, dS_final,
+               dq, dk_out, dv_out, da, db, dS0, N * Hk};
+  int nt = nthreads < 1 ? 1 : (nthreads > 256 ? 256 : nthreads);
+  if (J.ngroups < nt) nt = J.ngroups > 0 ? J.ngroups : 1;
+  pthread_t th[256];
+  bwd_slice sl[256];
+  for (int w = 0; w < nt; ++w) {
+    sl[w].job = &J;
+    sl[w].begin = (int)((int64_t)J.ngroups * w / nt);
+    sl[w].end = (int)((int64_t)J.ngroups * (w + 1) / nt);
+  }
+  for (int w = 1; w < nt; ++w)
+    if (pthread_create(&th[w], NULL, bwd_worker, &sl[w]) != 0) return -2;
+  bwd_worker(&sl[0]);
+  for (int w = 1; w < nt; ++w) pthread_join(th[w], NULL);
+  return 0;
+}

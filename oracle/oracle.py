@@ -52,6 +52,8 @@ class Oracle:
         lib.oracle_scan_pairs.restype = I
         lib.oracle_decode_step.argtypes = [I] * 7 + [P] * 9
         lib.oracle_decode_step.restype = I
+        lib.oracle_backward.argtypes = [I] * 7 + [P] * 15 + [I]
+        lib.oracle_backward.restype = I
         lib.oracle_dot.argtypes = [P, P, I]
         lib.oracle_dot.restype = ctypes.c_float
         self.lib = lib
@@ -130,6 +132,36 @@ class Oracle:
             c_at += nc
         return out
 
+    def backward(self, cu_seqlens, q, k, v, a, b, do, *, chunk, initial_state=None,
+                 dstate_final=None, nthreads=None):
+        """Gradients given dL/do [T, Hv, dv] and dL/dS_final [N, Hv, dv, dk] (None = 0).
+
+        Returns dict with dq, dk [T, Hk, dk]; dv [T, Hv, dv]; da, db [T, Hv];
+        dS0 [N, Hv, dv, dk] (all float32), in the backward contract's fixed order.
+        """
+        cu = _c(cu_seqlens, np.int32)
+        q, k, v = _c(q), _c(k), _c(v)
+        a, b = _c(a, np.float32), _c(b, np.float32)
+        do = _c(do, np.float32)
+        dt = _dtype_code(q)
+        N = cu.size - 1
+        T, Hk, dk = k.shape
+        Hv, dv = v.shape[1], v.shape[2]
+        s0 = _c(initial_state, np.float32)
+        dsf = _c(dstate_final, np.float32)
+        out = {"dq": np.zeros((T, Hk, dk), np.float32), "dk": np.zeros((T, Hk, dk), np.float32),
+               "dv": np.zeros((T, Hv, dv), np.float32), "da": np.zeros((T, Hv), np.float32),
+               "db": np.zeros((T, Hv), np.float32),
+               "dS0": np.zeros((N, Hv, dv, dk), np.float32)}
+        rc = self.lib.oracle_backward(N, Hk, Hv, dk, dv, chunk, dt, _ptr(cu), _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(a), _ptr(b), _ptr(s0), _ptr(do), _ptr(dsf),
+                                      _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                      _ptr(out["da"]), _ptr(out["db"]), _ptr(out["dS0"]),
+                                      nthreads or default_threads())
+        if rc != 0:
+            raise ValueError(f"oracle_backward rejected its arguments (rc={rc})")
+        return out
+
     def decode_step(self, pos, q, k, v, a, b, state, *, chunk, want_resync=True):
         """One decode step; updates ``state`` in place and returns (o, resync or None).
 
@@ -206,3 +238,7 @@ def scan_pairs(*args, **kw):
 
 def decode_step(*args, **kw):
     return get().decode_step(*args, **kw)
+
+
+def backward(*args, **kw):
+    return get().backward(*args, **kw)

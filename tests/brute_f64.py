@@ -40,3 +40,41 @@ def scan_f64(cu_seqlens, q, k, v, a, b, chunk, initial_state=None):
         finals[n] = S
     cs = np.stack(chunks) if chunks else np.zeros((0, Hv, dv, dk))
     return o, cs, finals
+
+
+def loss_f64(cu_seqlens, q, k, v, a, b, s0, do, dsf):
+    """L = sum(do * o) + sum(dsf * S_final), everything in float64 (dense form)."""
+    o, _, fs = scan_f64(cu_seqlens, q, k, v, a, b, 1 << 30, s0)
+    return float(np.sum(o * do.astype(np.float64)) + np.sum(fs * dsf.astype(np.float64)))
+
+
+def grads_torch_f64(cu_seqlens, q, k, v, a, b, s0, do, dsf):
+    """Exact gradients of loss_f64 by torch autograd in float64 on the CPU (dense form)."""
+    import torch
+
+    def t(x):
+        return torch.tensor(as_f64(x), dtype=torch.float64, requires_grad=True)
+
+    tq, tk, tv, ta, tb, ts0 = t(q), t(k), t(v), t(a), t(b), t(s0)
+    N = len(cu_seqlens) - 1
+    Hk, dk = k.shape[1], k.shape[2]
+    Hv = v.shape[1]
+    G = Hv // Hk
+    eye = torch.eye(dk, dtype=torch.float64)
+    tdo = torch.tensor(do, dtype=torch.float64)
+    loss = torch.zeros((), dtype=torch.float64)
+    for n in range(N):
+        S = ts0[n]
+        for t_ in range(int(cu_seqlens[n]), int(cu_seqlens[n + 1])):
+            heads = []
+            for h in range(Hv):
+                kk = tk[t_, h // G]
+                Sh = ta[t_, h] * S[h] @ (eye - tb[t_, h] * torch.outer(kk, kk)) \
+                    + tb[t_, h] * torch.outer(tv[t_, h], kk)
+                loss = loss + (tdo[t_, h] * (Sh @ tq[t_, h // G])).sum()
+                heads.append(Sh)
+            S = torch.stack(heads)
+        loss = loss + (torch.tensor(dsf[n], dtype=torch.float64) * S).sum()
+    loss.backward()
+    return {"dq": tq.grad.numpy(), "dk": tk.grad.numpy(), "dv": tv.grad.numpy(),
+            "da": ta.grad.numpy(), "db": tb.grad.numpy(), "dS0": ts0.grad.numpy()}

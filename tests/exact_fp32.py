@@ -97,3 +97,90 @@ def token(s, a, b, v_i, k, q):
     delta = mul(b, sub(v_i, u))
     s_new = [fma(delta, ke, xe) for ke, xe in zip(k, x)]
     return s_new, dot(s_new, q)
+
+
+def row_tree(vals):
+    """Pairwise tree over rows in natural order; a pair with no second half passes through."""
+    vals = list(vals)
+    n = len(vals)
+    w = 1
+    while w < n:
+        for j in range(0, n - w, 2 * w):
+            vals[j] = add(vals[j], vals[j + w])
+        w *= 2
+    return vals[0]
+
+
+def backward(cu, q, k, v, a, b, do, s0, dsf, Hk):
+    """The backward contract on tiny inputs (nested lists of binary32 Python floats).
+
+    q, k [T][Hk][d]; v [T][Hv][dv]; a, b [T][Hv]; do [T][Hv][dv]; s0, dsf [N][Hv][dv][d].
+    Returns dict dq, dk, dv, da, db, dS0 with the same nesting.
+    """
+    T = len(q)
+    Hv = len(v[0])
+    dv = len(v[0][0])
+    d = len(q[0][0])
+    G = Hv // Hk
+    N = len(cu) - 1
+    out = {"dq": [[[0.0] * d for _ in range(Hk)] for _ in range(T)],
+           "dk": [[[0.0] * d for _ in range(Hk)] for _ in range(T)],
+           "dv": [[[0.0] * dv for _ in range(Hv)] for _ in range(T)],
+           "da": [[0.0] * Hv for _ in range(T)], "db": [[0.0] * Hv for _ in range(T)],
+           "dS0": [[[None] * dv for _ in range(Hv)] for _ in range(N)]}
+    for n in range(N):
+        bos, eos = cu[n], cu[n + 1]
+        for hk in range(Hk):
+            dqh = [[[0.0] * d for _ in range(T)] for _ in range(G)]
+            dkh = [[[0.0] * d for _ in range(T)] for _ in range(G)]
+            for g in range(G):
+                h = hk * G + g
+                # forward states s_{t} for t = bos-1 .. eos-1, per row
+                states = [[list(s0[n][h][i]) for i in range(dv)]]
+                fwd = []
+                for t in range(bos, eos):
+                    cur, info = [], []
+                    for i in range(dv):
+                        s = states[-1][i]
+                        x = [mul(a[t][h], se) for se in s]
+                        u = dot(x, k[t][hk])
+                        diff = sub(v[t][h][i], u)
+                        delta = mul(b[t][h], diff)
+                        cur.append([fma(delta, ke, xe) for ke, xe in zip(k[t][hk], x)])
+                        info.append((x, diff, delta))
+                    states.append(cur)
+                    fwd.append(info)
+                sh = [list(dsf[n][h][i]) for i in range(dv)]
+                for t in range(eos - 1, bos - 1, -1):
+                    j = t - bos
+                    pq, pk, pa, pb = [], [], [], []
+                    for i in range(dv):
+                        x, diff, delta = fwd[j][i]
+                        s_prev, s_cur = states[j][i], states[j + 1][i]
+                        gg = do[t][h][i]
+                        shr = [fma(gg, qe, se) for qe, se in zip(q[t][hk], sh[i])]
+                        pq.append([mul(gg, se) for se in s_cur])
+                        dh = dot(shr, k[t][hk])
+                        dvi = mul(b[t][h], dh)
+                        out["dv"][t][h][i] = dvi
+                        pb.append(mul(dh, diff))
+                        uh = -dvi
+                        xh = [fma(uh, ke, se) for ke, se in zip(k[t][hk], shr)]
+                        pk.append([fma(uh, xe, mul(delta, se)) for xe, se in zip(x, shr)])
+                        pa.append(dot(xh, s_prev))
+                        sh[i] = [mul(a[t][h], xe) for xe in xh]
+                    out["da"][t][h] = row_tree(pa)
+                    out["db"][t][h] = row_tree(pb)
+                    dqh[g][j] = [row_tree([pq[i][e] for i in range(dv)]) for e in range(d)]
+                    dkh[g][j] = [row_tree([pk[i][e] for i in range(dv)]) for e in range(d)]
+                for i in range(dv):
+                    out["dS0"][n][h][i] = sh[i]
+            for t in range(bos, eos):
+                for e in range(d):
+                    aq, ak = dqh[0][t - bos][e], dkh[0][t - bos][e]
+                    for g in range(1, G):
+                        aq = add(aq, dqh[g][t - bos][e])
+                        ak = add(ak, dkh[g][t - bos][e])
+                    out["dq"][t][hk][e] = aq
+                    out["dk"][t][hk][e] = ak
+    return out

@@ -330,4 +330,96 @@ def pin_idle_slot(orc):
     assert not same_bits(state[1], s0[1]) and same_bits(rs[1], state[1]), "active slot resync"
 
 
+
+
+# --------------------------------------------------------------------------- backward
+
+GRAD_KEYS = ("dq", "dk", "dv", "da", "db", "dS0")
+
+
+def bwd_case(seed, lengths, Hk, Hv, d, chunk=16, bf16=False):
+    w, s0 = small_case(seed, lengths, Hk=Hk, Hv=Hv, d=d, chunk=chunk, bf16=bf16, with_s0=True)
+    g = np.random.default_rng(3000 + seed)
+    do = g.standard_normal((w.total_tokens, Hv, d)).astype(np.float32)
+    dsf = (0.5 * g.standard_normal((w.num_seqs, Hv, d, d))).astype(np.float32)
+    return w, s0, do, dsf
+
+
+def pin_bwd_vs_autograd_f64(orc):
+    for c in [(31, [37, 20], 1, 2, 32), (32, [64], 2, 4, 16), (33, [5, 0, 40], 1, 1, 64),
+              (34, [29, 11], 1, 3, 16, 16, True)]:
+        w, s0, do, dsf = bwd_case(*c)
+        got = orc.backward(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, do, chunk=16,
+                           initial_state=s0, dstate_final=dsf)
+        ref = brute_f64.grads_torch_f64(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, s0, do, dsf)
+        for key in GRAD_KEYS:
+            e = _normwise(got[key].astype(np.float64) - ref[key], ref[key])
+            assert e <= REL_TOL_F64, f"backward case {c[0]}: {key} rel err {e:.3g}"
+
+
+def pin_bwd_finite_differences(orc):
+    # directional derivatives of the float64 dense loss (no torch, no tree, no fmaf)
+    w, s0, do, dsf = bwd_case(35, [9, 6], 1, 2, 16)
+    got = orc.backward(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, do, chunk=16, initial_state=s0,
+                       dstate_final=dsf)
+    g = np.random.default_rng(35)
+    base = {"q": w.q.astype(np.float64), "k": w.k.astype(np.float64),
+            "v": w.v.astype(np.float64), "a": w.a.astype(np.float64),
+            "b": w.b.astype(np.float64), "s0": s0.astype(np.float64)}
+    names = {"q": "dq", "k": "dk", "v": "dv", "a": "da", "b": "db", "s0": "dS0"}
+    for name, key in names.items():
+        direction = g.standard_normal(base[name].shape)
+        eps = 1e-6
+        args = dict(base)
+        args[name] = base[name] + eps * direction
+        lp = brute_f64.loss_f64(w.cu_seqlens, args["q"], args["k"], args["v"], args["a"],
+                                args["b"], args["s0"], do, dsf)
+        args[name] = base[name] - eps * direction
+        lm = brute_f64.loss_f64(w.cu_seqlens, args["q"], args["k"], args["v"], args["a"],
+                                args["b"], args["s0"], do, dsf)
+        fd = (lp - lm) / (2 * eps)
+        an = float(np.sum(got[key].astype(np.float64) * direction))
+        assert abs(fd - an) <= 1e-5 * max(1.0, abs(fd)), f"{key}: fd {fd:.9g} vs {an:.9g}"
+
+
+def pin_bwd_exact_emulator(orc):
+    # 5 rows (a ragged row tree), a group of 3 value heads (order of the group sum), C < T
+    w, s0, do, dsf = bwd_case(36, [6, 3], 1, 3, 16)
+    w.v = W.make_packed("v5", [6, 3], Hk=3, Hv=3, d=5, chunk=16, bf16=False, seed=36).v
+    g = np.random.default_rng(36)
+    s0 = (0.3 * g.standard_normal((2, 3, 5, 16))).astype(np.float32)
+    do = g.standard_normal((9, 3, 5)).astype(np.float32)
+    dsf = (0.5 * g.standard_normal((2, 3, 5, 16))).astype(np.float32)
+    got = orc.backward(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, do, chunk=4, initial_state=s0,
+                       dstate_final=dsf)
+    tl = lambda x: np.asarray(x, np.float64).tolist()  # noqa: E731
+    want = exact_fp32.backward([int(c) for c in w.cu_seqlens], tl(w.q), tl(w.k), tl(w.v),
+                               tl(w.a), tl(w.b), tl(do), tl(s0), tl(dsf), Hk=1)
+    for key in GRAD_KEYS:
+        assert same_bits(got[key], np.array(want[key], np.float32)), f"emulator {key}"
+
+
+def pin_bwd_linear_scaling(orc):
+    # every gradient is linear in (do, dS_final): doubling both doubles every bit pattern
+    w, s0, do, dsf = bwd_case(37, [21, 14], 2, 4, 32, chunk=8, bf16=True)
+    r1 = orc.backward(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, do, chunk=8, initial_state=s0,
+                      dstate_final=dsf)
+    r2 = orc.backward(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, 2 * do, chunk=8, initial_state=s0,
+                      dstate_final=2 * dsf)
+    for key in GRAD_KEYS:
+        assert same_bits(r2[key], 2 * r1[key]), f"scaling {key}"
+
+
+def pin_bwd_chunk_invariance(orc):
+    w, s0, do, dsf = bwd_case(38, [33, 17], 1, 2, 16)
+    ref = None
+    for C in (1, 4, 16, 64):
+        r = orc.backward(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, do, chunk=C, initial_state=s0,
+                         dstate_final=dsf)
+        if ref is None:
+            ref = r
+        for key in GRAD_KEYS:
+            assert same_bits(r[key], ref[key]), f"C={C} changed {key}"
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -47,6 +47,38 @@ MUTANTS = {
     "resync_off_by_one": [("((int64_t)pos[n] + 1) % C == 0", "((int64_t)pos[n]) % C == 0")],
     "bf16_widening_wrong_half": [("(uint32_t)((const uint16_t *)base)[index] << 16",
                                   "(uint32_t)((const uint16_t *)base)[index] << 15")],
+    # backward
+    "bwd_sh_update_unfused": [("shr[e] = fmaf(gg, qq[e], shr[e]);", "shr[e] = gg * qq[e] + shr[e];")],
+    "bwd_dq_from_previous_state": [("pq[(int64_t)i * dk + e] = gg * s_cur[e];",
+                                    "pq[(int64_t)i * dk + e] = gg * s_prev[e];")],
+    "bwd_du_sign": [("const float uh = -dvi;", "const float uh = dvi;")],
+    "bwd_dk_drops_delta_term": [("pk[(int64_t)i * dk + e] = fmaf(uh, x[e], ds);",
+                                 "pk[(int64_t)i * dk + e] = uh * x[e] + 0.0f * ds;")],
+    "bwd_da_from_current_state": [("pa[i] = contract_dot(xh, s_prev, dk);",
+                                   "pa[i] = contract_dot(xh, s_cur, dk);")],
+    "bwd_no_decay": [("for (int e = 0; e < dk; ++e) shr[e] = A * xh[e];",
+                      "for (int e = 0; e < dk; ++e) shr[e] = xh[e];")],
+    "bwd_db_uses_delta": [("pb[i] = dh * diff;", "pb[i] = dh * delta;")],
+    "bwd_row_sum_serial": [("""  for (int w = 1; w < P; w *= 2)
+    for (int j = 0; j + w < count; j += 2 * w) vals[(int64_t)j * stride] =
+        vals[(int64_t)j * stride] + vals[(int64_t)(j + w) * stride];""",
+                            """  for (int j = 1; j < count && P; ++j)
+    vals[0] = vals[0] + vals[(int64_t)j * stride];""")],
+    "bwd_group_sum_right_to_left": [("""      for (int g = 1; g < G; ++g) {
+        accq = accq + DQh[((int64_t)g * Tn + j) * dk + e];
+        acck = acck + DKh[((int64_t)g * Tn + j) * dk + e];
+      }""", """      if (G > 1) {
+        float rq = DQh[((int64_t)(G - 1) * Tn + j) * dk + e];
+        float rk = DKh[((int64_t)(G - 1) * Tn + j) * dk + e];
+        for (int g = G - 2; g >= 1; --g) {
+          rq = DQh[((int64_t)g * Tn + j) * dk + e] + rq;
+          rk = DKh[((int64_t)g * Tn + j) * dk + e] + rk;
+        }
+        accq = accq + rq;
+        acck = acck + rk;
+      }""")],
+    "bwd_final_state_gradient_ignored": [("sh[(int64_t)i * dk + e] = J->dSf ? J->dSf[",
+                                          "sh[(int64_t)i * dk + e] = J->dSf ? 0.0f * J->dSf[")],
 }
 
 
@@ -64,10 +96,15 @@ def test_mutant_is_caught(name, tmp_path):
     mutant_src.write_text(_apply(src, MUTANTS[name]))
     lib = O.build(force=True, src=str(mutant_src), out=str(tmp_path / f"lib{name}.so"))
     orc = O.Oracle(lib)
-    caught = []
-    for pin in oracle_pins.ALL_PINS:
+    # backward mutants are most quickly caught by the backward pins: try those first
+    pins = sorted(oracle_pins.ALL_PINS,
+                  key=lambda p: (not (name.startswith("bwd") == p.__name__.startswith("pin_bwd")),
+                                 p.__name__))
+    caught = None
+    for pin in pins:
         try:
             pin(orc)
-        except AssertionError:
-            caught.append(pin.__name__)
+        except (AssertionError, FloatingPointError):
+            caught = pin.__name__
+            break
     assert caught, f"mutant {name} passed every pin"
