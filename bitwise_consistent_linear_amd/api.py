@@ -63,6 +63,13 @@ def lib():
         L.gdn_cpr_decode_step.restype = I32
         L.gdn_cpr_decode_step.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_char_p, P,
                                           P, P, P, P, P, P, P, P, P]
+        L.gdn_cpr_trainer_bwd_workspace.restype = I32
+        L.gdn_cpr_trainer_bwd_workspace.argtypes = [ctypes.POINTER(GdnShape), I64, I64,
+                                                    ctypes.POINTER(ctypes.c_size_t)]
+        L.gdn_cpr_trainer_bwd.restype = I32
+        L.gdn_cpr_trainer_bwd.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_char_p, P, I64,
+                                          P, P, P, P, P, P, P, I64, P, P,
+                                          P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_last_error.argtypes = []
         _lib = L
@@ -257,3 +264,63 @@ def decode_step(pos, q, k, v, a, b, state, *, chunk, o=None, resync_states=None,
                                      _ptr(v), _ptr(a), _ptr(b), _ptr(state), _ptr(o),
                                      _ptr(resync_states), _stream(stream)))
     return o
+
+
+def trainer_bwd_workspace_bytes(shape: GdnShape, total_tokens: int, total_chunks: int) -> int:
+    """gdn_cpr_trainer_bwd_workspace: device bytes the backward needs for these sizes."""
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_cpr_trainer_bwd_workspace(ctypes.byref(shape), total_tokens,
+                                               total_chunks, ctypes.byref(n)))
+    return n.value
+
+
+def trainer_bwd(cu_seqlens, q, k, v, a, b, chunk_states, d_o, *, chunk, initial_state=None,
+                d_final_state=None, total_chunks=None, workspace=None, out=None,
+                identity=None, stream=None):
+    """gdn_cpr_trainer_bwd: gradients through trainer_fwd, given d_o [T, Hv, dv] and
+    optionally d_final_state [N, Hv, dv, dk].
+
+    chunk_states is trainer_fwd's output for the same inputs. ``workspace`` is a uint8 GPU
+    tensor of at least trainer_bwd_workspace_bytes() bytes (allocated here when omitted);
+    ``out`` may hold preallocated dq, dk, dv, da, db, dS0 tensors.
+    Returns a dict with dq, dk [T, Hk, dk]; dv [T, Hv, dv]; da, db [T, Hv];
+    dS0 [N, Hv, dv, dk], all fp32.
+    """
+    torch = _torch()
+    dt = _qkv(q, k, v)
+    _need(cu_seqlens, "cu_seqlens", (torch.int32,), 1)
+    N = cu_seqlens.shape[0] - 1
+    T, Hk, Hv, dv, dk = q.shape[0], q.shape[1], v.shape[1], v.shape[2], q.shape[2]
+    _ab(a, b, T, Hv)
+    _state(initial_state, "initial_state", N, Hv, dv, dk)
+    _state(d_final_state, "d_final_state", N, Hv, dv, dk)
+    _need(d_o, "d_o", (torch.float32,), 3)
+    if tuple(d_o.shape) != (T, Hv, dv):
+        raise ValueError(f"d_o must be [{T}, {Hv}, {dv}], got {tuple(d_o.shape)}")
+    if total_chunks is None:
+        total_chunks = count_chunks(cu_seqlens, chunk)
+    _need(chunk_states, "chunk_states", (torch.float32,), 4)
+    if chunk_states.shape[0] < total_chunks or tuple(chunk_states.shape[1:]) != (Hv, dv, dk):
+        raise ValueError("chunk_states does not hold total_chunks states of this shape")
+    shapes = {"dq": (T, Hk, dk), "dk": (T, Hk, dk), "dv": (T, Hv, dv), "da": (T, Hv),
+              "db": (T, Hv), "dS0": (N, Hv, dv, dk)}
+    out = dict(out or {})
+    for name, shp in shapes.items():
+        if name not in out:
+            out[name] = torch.empty(shp, dtype=torch.float32, device=q.device)
+        _need(out[name], name, (torch.float32,), len(shp))
+        if tuple(out[name].shape) != shp:
+            raise ValueError(f"{name} must be {list(shp)}, got {tuple(out[name].shape)}")
+    shape = _shape(N, q, v, chunk, dt)
+    need = trainer_bwd_workspace_bytes(shape, T, total_chunks)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", (torch.uint8,), 1)
+    ident = identity if identity is not None else contract_identity(chunk, dk)
+    _check(lib().gdn_cpr_trainer_bwd(
+        ctypes.byref(shape), ident, _ptr(cu_seqlens), T, _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+        _ptr(b), _ptr(initial_state), _ptr(chunk_states) if total_chunks else None,
+        total_chunks, _ptr(d_o), _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]),
+        _ptr(out["dv"]), _ptr(out["da"]), _ptr(out["db"]), _ptr(out["dS0"]),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn_cpr.so")
 
-SOURCES = ["cpr_kernels.hip", "api.cpp", "contract.cpp"]
+SOURCES = ["cpr_kernels.hip", "cpr_backward.hip", "api.cpp", "contract.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950",
@@ -52,14 +52,26 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+KERNEL_SOURCES = [s for s in SOURCES if s.endswith(".hip")]
+
+
 def device_asm(out_path: str) -> str:
-    """Write the gfx950 assembly of the kernels (for instruction-mix checks)."""
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
-           "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "--cuda-device-only", "-S", "-I", INCLUDE, "-I", CSRC, "-o", out_path,
-           os.path.join(CSRC, "cpr_kernels.hip")]
-    subprocess.run(cmd, check=True, capture_output=True)
+    """Write the gfx950 assembly of every kernel source, concatenated (for instruction-mix
+    checks)."""
+    parts = []
+    for src in KERNEL_SOURCES:
+        one = out_path + "." + src + ".s"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
+               "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "--cuda-device-only", "-S", "-I", INCLUDE, "-I", CSRC, "-o", one,
+               os.path.join(CSRC, src)]
+        subprocess.run(cmd, check=True, capture_output=True)
+        with open(one) as f:
+            parts.append(f.read())
+        os.remove(one)
+    with open(out_path, "w") as f:
+        f.write("\n".join(parts))
     return out_path
 
 

@@ -267,4 +267,110 @@ GDN_EXPORT gdn_status_t gdn_cpr_decode_step(const gdn_shape_t *shape,
   return gdn::ok();
 }
 
+static gdn_status_t bwd_claims(const char *fn, const gdn_shape_t *shape, int64_t total_tokens,
+                               int64_t total_chunks) {
+  if (!shape) return gdn::fail(GDN_E_NULL, std::string(fn) + ": shape is NULL");
+  if (shape->chunk != 16 && shape->chunk != 32 && shape->chunk != 64)
+    return gdn::fail(GDN_E_UNSUPPORTED, std::string(fn) + ": the backward admits chunk 16, 32 or 64");
+  if (total_tokens < 0 || total_tokens > gdn::kMaxInt32)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": total_tokens must be in [0, 2^31)");
+  if (total_chunks < 0 || total_chunks > total_tokens / (shape->chunk > 0 ? shape->chunk : 1))
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": total_chunks must be in [0, total_tokens / chunk]");
+  return GDN_OK;
+}
+
+GDN_EXPORT gdn_status_t gdn_cpr_trainer_bwd_workspace(const gdn_shape_t *shape,
+                                                      int64_t total_tokens, int64_t total_chunks,
+                                                      size_t *bytes) {
+  const char *fn = "gdn_cpr_trainer_bwd_workspace";
+  if (!bytes) return gdn::fail(GDN_E_NULL, std::string(fn) + ": bytes is NULL");
+  gdn_status_t st = bwd_claims(fn, shape, total_tokens, total_chunks);
+  if (st != GDN_OK) return st;
+  if (shape->num_seqs < 0 || shape->num_v_heads < 1 || !gdn::admitted_dk(shape->d_k) ||
+      shape->d_v < 1 || shape->d_v > 1024)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": bad num_seqs, num_v_heads, d_k or d_v");
+  *bytes = (size_t)gdn::backward_workspace(shape->num_seqs, shape->num_v_heads, shape->d_k,
+                                           shape->d_v, total_tokens, total_chunks).total;
+  return gdn::ok();
+}
+
+GDN_EXPORT gdn_status_t gdn_cpr_trainer_bwd(
+    const gdn_shape_t *shape, const uint8_t *expected_identity, const int32_t *cu_seqlens,
+    int64_t total_tokens, const void *q, const void *k, const void *v, const float *a,
+    const float *b, const float *initial_state, const float *chunk_states, int64_t total_chunks,
+    const float *d_o, const float *d_final_state, float *dq, float *dk, float *dv, float *da,
+    float *db, float *d_initial_state, void *workspace, size_t workspace_bytes, void *stream) {
+  const char *fn = "gdn_cpr_trainer_bwd";
+  gdn::ScanArgs fwd;  // the forward claims apply unchanged (o is dq here: any non-null f32)
+  gdn_status_t st = gdn::scan_common(fn, shape, expected_identity, cu_seqlens, total_tokens, q,
+                                     k, v, a, b, initial_state, dq, fwd);
+  if (st != GDN_OK) return st;
+  if ((st = bwd_claims(fn, shape, total_tokens, total_chunks)) != GDN_OK) return st;
+  if (total_chunks > 0 && !chunk_states)
+    return gdn::fail(GDN_E_NULL, std::string(fn) + ": chunk_states is required");
+  if (total_tokens > 0 && (!d_o || !dq || !dk || !dv || !da || !db))
+    return gdn::fail(GDN_E_NULL, std::string(fn) + ": d_o, dq, dk, dv, da and db are required");
+  if (shape->num_seqs > 0 && !d_initial_state)
+    return gdn::fail(GDN_E_NULL, std::string(fn) + ": d_initial_state is required");
+  const float *f32[] = {chunk_states, d_final_state, d_initial_state};
+  for (const float *ptr : f32)
+    if ((st = gdn::check_state(fn, "a state buffer", ptr)) != GDN_OK) return st;
+  const float *f4[] = {d_o, dq, dk, dv, da, db};
+  for (const float *ptr : f4)
+    if (ptr && !gdn::aligned(ptr, 4))
+      return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": gradient buffers must be 4-byte aligned");
+  const gdn::BwdWorkspace ws = gdn::backward_workspace(
+      shape->num_seqs, shape->num_v_heads, shape->d_k, shape->d_v, total_tokens, total_chunks);
+  if (!workspace) return gdn::fail(GDN_E_NULL, std::string(fn) + ": workspace is NULL");
+  if (!gdn::aligned(workspace, 256))
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": workspace must be 256-byte aligned");
+  if ((int64_t)workspace_bytes < ws.total)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": workspace smaller than "
+                                      "gdn_cpr_trainer_bwd_workspace reports");
+  if (ws.slots_max > gdn::kMaxInt32)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": too many chunks");
+  gdn::BwdArgs args{};
+  args.num_seqs = shape->num_seqs;
+  args.num_qk_heads = shape->num_qk_heads;
+  args.num_v_heads = shape->num_v_heads;
+  args.d_k = shape->d_k;
+  args.d_v = shape->d_v;
+  args.chunk = shape->chunk;
+  args.bf16 = shape->qkv_dtype == GDN_DTYPE_BF16;
+  args.slots_max = (int32_t)ws.slots_max;
+  args.row_blocks = gdn::backward_row_blocks(shape->d_v);
+  args.total_tokens = total_tokens;
+  args.total_chunks = total_chunks;
+  args.cu_seqlens = cu_seqlens;
+  args.q = q;
+  args.k = k;
+  args.v = v;
+  args.a = a;
+  args.b = b;
+  args.initial_state = initial_state;
+  args.chunk_states = chunk_states;
+  args.d_o = d_o;
+  args.d_final_state = d_final_state;
+  args.dq = dq;
+  args.dk = dk;
+  args.dv = dv;
+  args.da = da;
+  args.db = db;
+  args.d_initial_state = d_initial_state;
+  char *w = static_cast<char *>(workspace);
+  args.plan = reinterpret_cast<int32_t *>(w + ws.plan_off);
+  args.plan_cbase = reinterpret_cast<int32_t *>(w + ws.cbase_off);
+  args.dsh_bnd = reinterpret_cast<float *>(w + ws.dsh_off);
+  args.partials = reinterpret_cast<float *>(w + ws.partials_off);
+  if (shape->num_seqs == 0) return gdn::ok();
+  const int L = gdn::scan_lanes(fwd);
+  if (gdn::backward_state_grid(args, L) > gdn::kMaxInt32 ||
+      gdn::backward_chunk_grid(args) > gdn::kMaxInt32)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": grid too large");
+  const hipError_t e = gdn::launch_backward(args, L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return gdn::fail(GDN_E_DEVICE, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
+  return gdn::ok();
+}
+
 }  // extern "C"

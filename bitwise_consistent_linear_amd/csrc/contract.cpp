@@ -118,9 +118,9 @@ bool admitted_dk(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; 
 std::string contract_text(int32_t chunk, int32_t d_k) {
   std::string s;
   s += "contract=isoexec-gdn-cpr\n";
-  s += "version=1\n";
+  s += "version=2\n";
   s += "region=gated_delta_rule\n";
-  s += "cases=trainer_fwd,engine_prefill,engine_decode\n";
+  s += "cases=trainer_fwd,trainer_bwd,engine_prefill,engine_decode\n";
   s += "recurrence=S_t=a_t*S_{t-1}*(I-b_t*k_t*k_t^T)+b_t*v_t*k_t^T;o_t=S_t*q_t\n";
   s += "row_update=x_e=a*s_e;u=dot(x,k);d=b*(v_i-u);s_e=fma(d,k_e,x_e);o_i=dot(s,q)\n";
   s += "dot=leaves:16;leaf:contiguous d_k/16;leaf_first:mul;leaf_rest:fma ascending;"
@@ -133,6 +133,11 @@ std::string contract_text(int32_t chunk, int32_t d_k) {
   s += "gqa=qk_head=v_head/(Hv/Hk)\n";
   s += "chunk_state=after in-sequence index j with (j+1)%C==0;floor(T_n/C) per sequence\n";
   s += "decode_resync=state after token pos when (pos+1)%C==0\n";
+  s += "bwd_order=reverse tokens;sh=dL/dS_final or 0;dS0=sh after the first token\n";
+  s += "bwd_row=sh_e=fma(g,q_e,sh_e);pq_e=g*s_e;dh=dot(sh,k);dv_i=b*dh;pb=dh*(v_i-u);"
+       "xh_e=fma(-dv_i,k_e,sh_e);pk_e=fma(-dv_i,x_e,d*sh_e);pa=dot(xh,s_prev);sh_e=a*xh_e\n";
+  s += "bwd_rows=dq,dk,da,db:pairwise over rows in natural order;unpaired passes through\n";
+  s += "bwd_gqa=dq,dk:value heads of the group added in ascending order\n";
   s += "chunk=" + std::to_string(chunk) + "\n";
   s += "d_k=" + std::to_string(d_k) + "\n";
   return s;

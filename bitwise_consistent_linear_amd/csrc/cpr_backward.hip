@@ -1,0 +1,580 @@
+// HIP kernels for the backward of CPR Gated DeltaNet (the trainer's gradients) on gfx950.
+//
+// Per row i of (n, h), dL/ds (sh) runs backward over the tokens:
+//   sh += g q;  dh = sh . k;  dv_i = b dh;  xh = sh - dv_i k;  [shares];  sh = a xh
+// (row_bwd_* in cpr_row.hpp, in the contract's binary32 order). The shares of dq, dk, da
+// and db need the forward states, the recurrence of sh does not. So:
+//   1. plan:    one workgroup maps chunk slots to (sequence, chunk) and computes each
+//               sequence's first chunk-state index;
+//   2. state:   a reverse scan of sh per row (as parallel as the forward scan), writing dv,
+//               dS0 and sh at every chunk boundary;
+//   3. chunk:   for every (chunk, value head, block of 16 rows) in parallel: the forward
+//               states recomputed from the trainer's chunk state (checkpoints every 8 tokens
+//               in registers), sh re-run from the boundary value the state pass stored (the
+//               same operations, so the same bits), and every token's shares summed over
+//               the block's rows: pairwise in natural row order, within the wave through
+//               LDS, then across the 4 waves; one partial per (token, head, row block);
+//   4. combine: the pairwise tree continued over the row blocks, then the value heads of a
+//               q/k group left to right.
+// A pair of the row tree whose second half holds no row (d_v not a power of two) passes its
+// first half through unchanged, at every level; that is what makes the hierarchical sums
+// equal the contract's single tree over the d_v rows.
+
+#include <algorithm>
+#include <type_traits>
+#include <utility>
+
+#include "cpr_io.hpp"
+#include "cpr_row.hpp"
+#include "internal.h"
+
+namespace gdn {
+namespace {
+
+using namespace io;
+
+constexpr int kThreads = 256;
+constexpr int kStateStage = 16;                   // tokens staged at a time by the state pass
+constexpr int kSub = 8;                           // tokens per recomputed sub-block
+constexpr int kMaxSub = 8;                        // sub-blocks per chunk: C <= 64
+constexpr int kChunkLanes = 16;                   // lanes per row in the chunk kernel
+constexpr int kChunkRows = kThreads / kChunkLanes;
+constexpr int kPlanHeader = 4;                    // int32 slots before the (n, c) pairs
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1 (REVERSE: N-1 .. 0), each with its own
+// compile-time index, so register arrays indexed by i stay in registers.
+template <bool REVERSE, int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, REVERSE ? N - 1 - I : I>{}), ...);
+}
+template <int N, bool REVERSE = false, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl<REVERSE, N>(f, std::make_integer_sequence<int, N>{});
+}
+
+// --------------------------------------------------------------------------------- plan
+
+// Sums run in 64 bits: lengths come from device memory the host cannot check, and whatever
+// they hold, every slot and chunk-state base written below stays inside its buffer.
+__global__ __launch_bounds__(kThreads) void cpr_bwd_plan_kernel(const BwdArgs p) {
+  __shared__ int64_t s_ceil[kThreads], s_floor[kThreads];
+  __shared__ int64_t s_carry_ceil, s_carry_floor;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    s_carry_ceil = 0;
+    s_carry_floor = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < p.num_seqs; base += kThreads) {
+    const int m = base + tid;
+    int64_t len = 0;
+    if (m < p.num_seqs) {
+      int64_t b, e;
+      seq_range(p.cu_seqlens, m, p.total_tokens, b, e);
+      len = e - b;
+    }
+    const int64_t nc = (len + p.chunk - 1) / p.chunk, nf = len / p.chunk;
+    s_ceil[tid] = nc;
+    s_floor[tid] = nf;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off *= 2) {  // inclusive scan
+      const int64_t vc = tid >= off ? s_ceil[tid - off] : 0;
+      const int64_t vf = tid >= off ? s_floor[tid - off] : 0;
+      __syncthreads();
+      s_ceil[tid] += vc;
+      s_floor[tid] += vf;
+      __syncthreads();
+    }
+    const int64_t ex_ceil = s_carry_ceil + s_ceil[tid] - nc;
+    const int64_t ex_floor = s_carry_floor + s_floor[tid] - nf;
+    if (m < p.num_seqs) {
+      p.plan_cbase[m] = (int32_t)(ex_floor < p.total_chunks ? ex_floor : p.total_chunks);
+      for (int64_t c = 0; c < nc && ex_ceil + c < p.slots_max; ++c) {
+        const int64_t slot = ex_ceil + c;
+        p.plan[kPlanHeader + 2 * slot] = m;
+        p.plan[kPlanHeader + 2 * slot + 1] = (int32_t)c;
+      }
+    }
+    __syncthreads();
+    if (tid == kThreads - 1) {
+      s_carry_ceil += s_ceil[tid];
+      s_carry_floor += s_floor[tid];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) p.plan[0] = (int32_t)(s_carry_ceil < p.slots_max ? s_carry_ceil : p.slots_max);
+}
+
+// ---------------------------------------------------------------------------- state pass
+
+template <int D, int L, bool BF16>
+__global__ __launch_bounds__(kThreads) void cpr_bwd_state_kernel(const BwdArgs p) {
+  constexpr int ROWS = kThreads / L;
+  constexpr int M = D / L;
+  constexpr int TS = kStateStage;
+  constexpr int GROUPS = D / 4;
+  constexpr int KQ_ITEMS = TS * GROUPS, V_ITEMS = TS * ROWS;
+  constexpr int KQ_PER = (KQ_ITEMS + kThreads - 1) / kThreads;
+  constexpr int V_PER = (V_ITEMS + kThreads - 1) / kThreads;
+  using raw_t = typename Raw4<BF16>::type;
+
+  __shared__ __align__(16) float sk[2][TS * D];
+  __shared__ __align__(16) float sq[2][TS * D];
+  __shared__ float sg[2][V_ITEMS];   // dL/do of the block's rows
+  __shared__ float sdv[2][V_ITEMS];  // dv of the block's rows, stored coalesced after a stage
+  __shared__ float sa[2][TS], sb[2][TS];
+  __shared__ int s_len[kMaxRankedSeqs];
+  __shared__ int s_pick;
+
+  const int tid = threadIdx.x, row = tid / L, lane = tid % L;
+  const int Hv = p.num_v_heads, Hk = p.num_qk_heads, dv = p.d_v;
+  const int rblocks = (dv + ROWS - 1) / ROWS;
+  int pair, rblock;
+  block_work(blockIdx.x, p.num_seqs * Hv, rblocks, pair, rblock);
+  const int rank = pair / Hv;
+  const int h = pair % Hv;
+  const int r0 = rblock * ROWS;
+  const int64_t T = p.total_tokens;
+  const int n = ranked_sequence(p.cu_seqlens, p.num_seqs, T, rank, s_len, &s_pick);
+  int64_t bos, eos;
+  seq_range(p.cu_seqlens, n, T, bos, eos);
+  const int64_t Tn = eos - bos;
+  const int64_t cbase = p.plan_cbase[n];
+  const int hk = h / (Hv / Hk);
+  const int i = r0 + row;
+  const bool valid = i < dv;
+  const int64_t row_off = (((int64_t)n * Hv + h) * dv + i) * D + lane * M;
+  const int64_t vstride = (int64_t)Hv * dv;
+
+  float sh[M];
+  if (p.d_final_state && valid) {
+    load_row<M>(p.d_final_state + row_off, sh);
+  } else {
+#pragma unroll
+    for (int e = 0; e < M; ++e) sh[e] = 0.0f;
+  }
+#pragma unroll
+  for (int e = 0; e < M; ++e) asm volatile("" ::"v"(sh[e]));
+
+  raw_t rk[KQ_PER], rq[KQ_PER];
+  float rg[V_PER], ra, rb;
+  auto fetch = [&](int64_t t0) {
+    const int64_t last = Tn - 1;
+#pragma unroll
+    for (int j = 0; j < KQ_PER; ++j) {
+      const int g = (tid + j * kThreads) % KQ_ITEMS;
+      const int64_t t = t0 + g / GROUPS < last ? t0 + g / GROUPS : last;
+      const int64_t src = ((bos + t) * Hk + hk) * D + 4 * (g % GROUPS);
+      rk[j] = load_raw4<BF16>(p.k, src);
+      rq[j] = load_raw4<BF16>(p.q, src);
+    }
+#pragma unroll
+    for (int j = 0; j < V_PER; ++j) {
+      const int e = (tid + j * kThreads) % V_ITEMS;
+      const int64_t t = t0 + e / ROWS < last ? t0 + e / ROWS : last;
+      const int r = r0 + e % ROWS < dv ? r0 + e % ROWS : dv - 1;
+      rg[j] = p.d_o[(bos + t) * vstride + (int64_t)h * dv + r];
+    }
+    const int64_t t = t0 + tid % TS < last ? t0 + tid % TS : last;
+    ra = p.a[(bos + t) * Hv + h];
+    rb = p.b[(bos + t) * Hv + h];
+  };
+  auto deposit = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < KQ_PER; ++j) {
+      const int g = tid + j * kThreads;
+      if (KQ_ITEMS % kThreads == 0 || g < KQ_ITEMS) {
+        const int off = (g / GROUPS) * D + stage_slot<D, L>(g % GROUPS);
+        *reinterpret_cast<float4 *>(&sk[buf][off]) = widen4<BF16>(rk[j]);
+        *reinterpret_cast<float4 *>(&sq[buf][off]) = widen4<BF16>(rq[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < V_PER; ++j) {
+      const int e = tid + j * kThreads;
+      if (V_ITEMS % kThreads == 0 || e < V_ITEMS) sg[buf][e] = rg[j];
+    }
+    if (tid < TS) {
+      sa[buf][tid] = ra;
+      sb[buf][tid] = rb;
+    }
+  };
+  auto write_dv = [&](int64_t t0, int nt, int buf) {
+#pragma unroll
+    for (int j = 0; j < V_PER; ++j) {
+      const int e = tid + j * kThreads;
+      const int tt = e / ROWS, r = e % ROWS;
+      if ((V_ITEMS % kThreads == 0 || e < V_ITEMS) && tt < nt && r0 + r < dv)
+        p.dv[(bos + t0 + tt) * vstride + (int64_t)h * dv + r0 + r] = sdv[buf][e];
+    }
+  };
+  auto run_token = [&](int buf, int tt) {
+    float kr[M], qr[M], xh[M], dh;
+    lds_slice<D, L>(&sk[buf][tt * D], lane, kr);
+    lds_slice<D, L>(&sq[buf][tt * D], lane, qr);
+    row_bwd_absorb<D, L>(sh, sg[buf][tt * ROWS + row], qr);
+    sdv[buf][tt * ROWS + row] = row_bwd_delta<D, L>(sh, kr, sb[buf][tt], xh, dh);
+    row_bwd_decay<D, L>(sh, sa[buf][tt], xh);
+  };
+
+  const int chunk_shift = __builtin_ctz((unsigned)p.chunk);
+  const int64_t nstages = (Tn + TS - 1) / TS;
+  if (Tn > 0) {
+    fetch((nstages - 1) * TS);
+    deposit(0);
+  }
+  __syncthreads();
+  for (int64_t idx = 0; idx < nstages; ++idx) {
+    const int64_t st = nstages - 1 - idx;
+    const int buf = (int)(idx & 1);
+    const int64_t t0 = st * TS;
+    const int nt = (int)(Tn - t0 < TS ? Tn - t0 : TS);
+    const bool more = st > 0;
+    if (more) fetch(t0 - TS);
+    if (nt == TS) {
+      // dL/d(state after a full chunk's last token), from everything after it
+      const int64_t done = t0 + TS;
+      if ((done & (p.chunk - 1)) == 0) {
+        const int64_t c = cbase + (done >> chunk_shift) - 1;
+        if (valid && c < p.total_chunks)
+          store_row<M>(p.dsh_bnd + ((c * Hv + h) * dv + i) * D + lane * M, sh);
+      }
+#pragma unroll
+      for (int tt = TS - 1; tt >= 0; --tt) run_token(buf, tt);
+    } else {
+#pragma unroll 1
+      for (int tt = nt - 1; tt >= 0; --tt) run_token(buf, tt);
+    }
+    if (more) deposit(buf ^ 1);
+    __syncthreads();
+    write_dv(t0, nt, buf);
+  }
+  if (valid) store_row<M>(p.d_initial_state + row_off, sh);
+}
+
+// ---------------------------------------------------------------------------- chunk pass
+
+// Checkpoints and a sub-block of recomputed states live in registers: allow up to 256
+// VGPRs (two waves per SIMD) rather than spill.
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void cpr_bwd_chunk_kernel(const BwdArgs p) {
+  constexpr int L = kChunkLanes, ROWS = kChunkRows, M = D / L, SB = kSub;
+  constexpr int WAVES = kThreads / 64, RPW = 64 / L;  // rows per wave
+  constexpr int PW = 2 * D + 2;                       // shares of a token: dq, dk, da, db
+  constexpr int GROUPS = D / 4;
+  __shared__ __align__(16) float sk[SB * D];
+  __shared__ __align__(16) float sq[SB * D];
+  __shared__ float sv[SB * ROWS], sg[SB * ROWS], sa[SB], sb[SB];
+  __shared__ __align__(16) float srow[WAVES][RPW][PW];  // one token's shares of a wave's rows
+  __shared__ float swave[SB][WAVES][PW];                // wave sums of a sub-block's tokens
+
+  const int tid = threadIdx.x, row = tid / L, lane = tid % L;
+  const int wave = tid / 64, wl = tid % 64, rw = row % RPW;
+  const int Hv = p.num_v_heads, Hk = p.num_qk_heads, dv = p.d_v, RB = p.row_blocks;
+  int pair, rblock;
+  block_work(blockIdx.x, p.slots_max * Hv, RB, pair, rblock);
+  const int slot = pair / Hv, h = pair % Hv;
+  if (slot >= p.plan[0]) return;  // uniform: this workgroup has no chunk
+  const int n = p.plan[kPlanHeader + 2 * slot], c = p.plan[kPlanHeader + 2 * slot + 1];
+  int64_t bos, eos;
+  seq_range(p.cu_seqlens, n, p.total_tokens, bos, eos);
+  const int64_t Tn = eos - bos, c0 = (int64_t)c * p.chunk;
+  if (c0 >= Tn) return;  // uniform
+  const int len = (int)(Tn - c0 < p.chunk ? Tn - c0 : p.chunk);
+  const int64_t cbase = p.plan_cbase[n];
+  const int hk = h / (Hv / Hk);
+  const int r0 = rblock * ROWS, i = r0 + row;
+  const bool valid = i < dv;
+  const int64_t vstride = (int64_t)Hv * dv;
+  const int64_t row_off = (((int64_t)n * Hv + h) * dv + i) * D + lane * M;
+
+  // state at the chunk's start, dL/ds at its end
+  float s[M], sh[M];
+#pragma unroll
+  for (int e = 0; e < M; ++e) {
+    s[e] = 0.0f;
+    sh[e] = 0.0f;
+  }
+  if (valid) {
+    if (c == 0) {
+      if (p.initial_state) load_row<M>(p.initial_state + row_off, s);
+    } else if (cbase + c - 1 < p.total_chunks) {
+      load_row<M>(p.chunk_states + (((cbase + c - 1) * Hv + h) * dv + i) * D + lane * M, s);
+    }
+    if (c0 + p.chunk <= Tn) {
+      if (cbase + c < p.total_chunks)
+        load_row<M>(p.dsh_bnd + (((cbase + c) * Hv + h) * dv + i) * D + lane * M, sh);
+    } else if (p.d_final_state) {
+      load_row<M>(p.d_final_state + row_off, sh);
+    }
+  }
+
+  // tokens [c0 + j0, c0 + j0 + nt) of the chunk into LDS
+  auto stage = [&](int j0, int nt) {
+    for (int g = tid; g < nt * GROUPS; g += kThreads) {
+      const int tt = g / GROUPS, cc = g % GROUPS;
+      const int64_t src = ((bos + c0 + j0 + tt) * Hk + hk) * D + 4 * cc;
+      *reinterpret_cast<float4 *>(&sk[tt * D + stage_slot<D, L>(cc)]) = load4<BF16>(p.k, src);
+      *reinterpret_cast<float4 *>(&sq[tt * D + stage_slot<D, L>(cc)]) = load4<BF16>(p.q, src);
+    }
+    for (int e = tid; e < nt * ROWS; e += kThreads) {
+      const int tt = e / ROWS, r = e % ROWS;
+      const int64_t at = (bos + c0 + j0 + tt) * vstride + (int64_t)h * dv + r0 + r;
+      sv[e] = r0 + r < dv ? load1<BF16>(p.v, at) : 0.0f;
+      sg[e] = r0 + r < dv ? p.d_o[at] : 0.0f;
+    }
+    if (tid < nt) {
+      sa[tid] = p.a[(bos + c0 + j0 + tid) * Hv + h];
+      sb[tid] = p.b[(bos + c0 + j0 + tid) * Hv + h];
+    }
+  };
+
+  // Sums one token's shares over this wave's rows (pairwise, natural order) into swave[j].
+  // A wave's LDS operations complete in order, so each lane may read what other lanes of
+  // the wave wrote just before.
+  const int wrow0 = r0 + wave * RPW;  // first row of this wave
+  auto wave_sum = [&](int j, const float (&pq)[M], const float (&pk)[M], float pa, float pb) {
+#pragma unroll
+    for (int e = 0; e < M; ++e) {
+      srow[wave][rw][lane * M + e] = pq[e];
+      srow[wave][rw][D + lane * M + e] = pk[e];
+    }
+    if (lane == 0) {
+      srow[wave][rw][2 * D] = pa;
+      srow[wave][rw][2 * D + 1] = pb;
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int f = wl; f < PW; f += 64) {
+      float v[RPW];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) v[r] = srow[wave][r][f];
+#pragma unroll
+      for (int w = 1; w < RPW; w *= 2)
+#pragma unroll
+        for (int r = 0; r + w < RPW; r += 2 * w)
+          if (wrow0 + r + w < dv) v[r] = v[r] + v[r + w];
+      swave[j][wave][f] = v[0];
+    }
+    __builtin_amdgcn_wave_barrier();  // the next token's writes follow these reads
+  };
+
+  const int nsb = (len + SB - 1) / SB;
+  float ck[kMaxSub][M];  // state at the start of every sub-block
+  static_for<kMaxSub>([&](auto sbi_c) {
+    constexpr int sbi = decltype(sbi_c)::value;
+    if (sbi < nsb) {
+      const int nt = len - sbi * SB < SB ? len - sbi * SB : SB;
+#pragma unroll
+      for (int e = 0; e < M; ++e) ck[sbi][e] = s[e];
+      __syncthreads();
+      stage(sbi * SB, nt);
+      __syncthreads();
+      for (int j = 0; j < nt; ++j) {
+        float kr[M], x[M];
+        lds_slice<D, L>(&sk[j * D], lane, kr);
+        row_decay<D, L>(s, sa[j], x);
+        const float u = contract_dot<D, L>(x, kr);
+        row_update<D, L>(s, row_delta(sb[j], sv[j * ROWS + row], u), kr, x);
+      }
+    }
+  });
+
+  static_for<kMaxSub, true>([&](auto sbi_c) {
+    constexpr int sbi = decltype(sbi_c)::value;
+    if (sbi < nsb) {
+      const int nt = len - sbi * SB < SB ? len - sbi * SB : SB;
+      __syncthreads();
+      stage(sbi * SB, nt);
+      __syncthreads();
+      float st[SB + 1][M], dif[SB], del[SB];
+#pragma unroll
+      for (int e = 0; e < M; ++e) st[0][e] = ck[sbi][e];
+#pragma unroll
+      for (int j = 0; j < SB; ++j) {
+        if (j < nt) {
+          float kr[M], x[M];
+          lds_slice<D, L>(&sk[j * D], lane, kr);
+          row_decay<D, L>(st[j], sa[j], x);
+          const float u = contract_dot<D, L>(x, kr);
+          dif[j] = sv[j * ROWS + row] - u;
+          del[j] = sb[j] * dif[j];
+#pragma unroll
+          for (int e = 0; e < M; ++e) st[j + 1][e] = st[j][e];
+          row_update<D, L>(st[j + 1], del[j], kr, x);
+        }
+      }
+#pragma unroll
+      for (int j = SB - 1; j >= 0; --j) {
+        if (j < nt) {
+          float kr[M], qr[M], x[M], xh[M], pq[M], pk[M], dh;
+          lds_slice<D, L>(&sk[j * D], lane, kr);
+          lds_slice<D, L>(&sq[j * D], lane, qr);
+          const float g = sg[j * ROWS + row], a = sa[j], b = sb[j];
+          row_bwd_absorb<D, L>(sh, g, qr);
+#pragma unroll
+          for (int e = 0; e < M; ++e) pq[e] = g * st[j + 1][e];
+          const float dv_i = row_bwd_delta<D, L>(sh, kr, b, xh, dh);
+          const float pb = dh * dif[j];
+          const float uh = -dv_i;
+          row_decay<D, L>(st[j], a, x);
+#pragma unroll
+          for (int e = 0; e < M; ++e) {
+            const float ds = del[j] * sh[e];
+            pk[e] = __builtin_fmaf(uh, x[e], ds);
+          }
+          const float pa = contract_dot<D, L>(xh, st[j]);
+          row_bwd_decay<D, L>(sh, a, xh);
+          wave_sum(j, pq, pk, pa, pb);
+        }
+      }
+      __syncthreads();
+      // across the 4 waves (rows r0+4w .. r0+4w+3), pairwise with pass-through
+      for (int e = tid; e < nt * PW; e += kThreads) {
+        const int j = e / PW, f = e % PW;
+        float w0 = swave[j][0][f], w1 = swave[j][1][f], w2 = swave[j][2][f], w3 = swave[j][3][f];
+        if (r0 + RPW < dv) w0 = w0 + w1;
+        if (r0 + 3 * RPW < dv) w2 = w2 + w3;
+        if (r0 + 2 * RPW < dv) w0 = w0 + w2;
+        const int64_t t = bos + c0 + sbi * SB + j;
+        p.partials[((t * Hv + h) * RB + rblock) * PW + f] = w0;
+      }
+    }
+  });
+}
+
+// -------------------------------------------------------------------------- combine pass
+
+// Pairwise tree over the RB row-block sums (natural order, pass-through); RBMAX is the power
+// of two at or above RB.
+template <int RBMAX>
+__device__ __forceinline__ float rb_tree(const float *base, int64_t stride, int RB) {
+  constexpr int kMaxRB = RBMAX;
+  float v[kMaxRB];
+#pragma unroll
+  for (int j = 0; j < kMaxRB; ++j) v[j] = j < RB ? base[j * stride] : 0.0f;
+#pragma unroll
+  for (int w = 1; w < kMaxRB; w *= 2)
+#pragma unroll
+    for (int j = 0; j + w < kMaxRB; j += 2 * w)
+      if (j + w < RB) v[j] = v[j] + v[j + w];
+  return v[0];
+}
+
+template <int RBMAX>
+__global__ __launch_bounds__(kThreads) void cpr_bwd_combine_kernel(const BwdArgs p) {
+  const int D = p.d_k, PW = 2 * D + 2, RB = p.row_blocks;
+  const int Hv = p.num_v_heads, Hk = p.num_qk_heads, G = Hv / Hk;
+  const int64_t T = p.total_tokens;
+  const int64_t nqk = T * Hk * D, nab = T * Hv;
+  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < nqk + nab;
+       idx += (int64_t)gridDim.x * kThreads) {
+    if (idx < nqk) {
+      const int64_t t = idx / ((int64_t)Hk * D);
+      const int hk = (int)((idx / D) % Hk), e = (int)(idx % D);
+      float aq = 0.0f, ak = 0.0f;
+      for (int g = 0; g < G; ++g) {
+        const float *base = p.partials + ((t * Hv + hk * G + g) * RB) * PW;
+        const float vq = rb_tree<RBMAX>(base + e, PW, RB);
+        const float vk = rb_tree<RBMAX>(base + D + e, PW, RB);
+        aq = g == 0 ? vq : aq + vq;
+        ak = g == 0 ? vk : ak + vk;
+      }
+      p.dq[(t * Hk + hk) * D + e] = aq;
+      p.dk[(t * Hk + hk) * D + e] = ak;
+    } else {
+      const int64_t r = idx - nqk, t = r / Hv;
+      const int h = (int)(r % Hv);
+      const float *base = p.partials + ((t * Hv + h) * RB) * PW;
+      p.da[t * Hv + h] = rb_tree<RBMAX>(base + 2 * D, PW, RB);
+      p.db[t * Hv + h] = rb_tree<RBMAX>(base + 2 * D + 1, PW, RB);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- launchers
+
+template <typename Args>
+hipError_t launch1(const void *fn, int64_t grid, Args args, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  void *kargs[] = {&args};
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
+}
+
+template <int D>
+const void *state_fn(int L, bool bf16) {
+  switch (L) {
+    case 16: return bf16 ? (const void *)cpr_bwd_state_kernel<D, 16, true>
+                         : (const void *)cpr_bwd_state_kernel<D, 16, false>;
+    case 8: return bf16 ? (const void *)cpr_bwd_state_kernel<D, 8, true>
+                        : (const void *)cpr_bwd_state_kernel<D, 8, false>;
+    default: return bf16 ? (const void *)cpr_bwd_state_kernel<D, 4, true>
+                         : (const void *)cpr_bwd_state_kernel<D, 4, false>;
+  }
+}
+
+template <int D>
+const void *chunk_fn(bool bf16) {
+  return bf16 ? (const void *)cpr_bwd_chunk_kernel<D, true>
+              : (const void *)cpr_bwd_chunk_kernel<D, false>;
+}
+
+}  // namespace
+
+int backward_row_blocks(int d_v) { return (d_v + kChunkRows - 1) / kChunkRows; }
+
+BwdWorkspace backward_workspace(int64_t num_seqs, int64_t num_v_heads, int64_t d_k,
+                                int64_t d_v, int64_t total_tokens, int64_t total_chunks) {
+  auto up256 = [](int64_t x) { return (x + 255) / 256 * 256; };
+  BwdWorkspace w{};
+  const int64_t slots = total_chunks + num_seqs;
+  w.plan_off = 0;
+  w.plan_bytes = up256((kPlanHeader + 2 * slots) * 4);
+  w.cbase_off = w.plan_off + w.plan_bytes;
+  w.cbase_bytes = up256(std::max<int64_t>(num_seqs, 1) * 4);
+  w.dsh_off = w.cbase_off + w.cbase_bytes;
+  w.dsh_bytes = up256(total_chunks * num_v_heads * d_v * d_k * 4);
+  w.partials_off = w.dsh_off + w.dsh_bytes;
+  w.partials_bytes =
+      up256(total_tokens * num_v_heads * backward_row_blocks((int)d_v) * (2 * d_k + 2) * 4);
+  w.total = w.partials_off + w.partials_bytes;
+  w.slots_max = slots;
+  return w;
+}
+
+int64_t backward_state_grid(const BwdArgs &a, int L) {
+  const int64_t rows = kThreads / L;
+  return (int64_t)a.num_seqs * a.num_v_heads * ((a.d_v + rows - 1) / rows);
+}
+
+int64_t backward_chunk_grid(const BwdArgs &a) {
+  return (int64_t)a.slots_max * a.num_v_heads * a.row_blocks;
+}
+
+hipError_t launch_backward(const BwdArgs &a, int L, hipStream_t st) {
+  hipError_t e = launch1((const void *)cpr_bwd_plan_kernel, 1, a, st);
+  if (e != hipSuccess) return e;
+  const void *sf, *cf;
+  switch (a.d_k) {
+    case 16: sf = state_fn<16>(L, a.bf16); cf = chunk_fn<16>(a.bf16); break;
+    case 32: sf = state_fn<32>(L, a.bf16); cf = chunk_fn<32>(a.bf16); break;
+    case 64: sf = state_fn<64>(L, a.bf16); cf = chunk_fn<64>(a.bf16); break;
+    case 128: sf = state_fn<128>(L, a.bf16); cf = chunk_fn<128>(a.bf16); break;
+    default: return hipErrorInvalidValue;
+  }
+  if ((e = launch1(sf, backward_state_grid(a, L), a, st)) != hipSuccess) return e;
+  if ((e = launch1(cf, backward_chunk_grid(a), a, st)) != hipSuccess) return e;
+  const int64_t items = a.total_tokens * (a.num_qk_heads * (int64_t)a.d_k + a.num_v_heads);
+  const int64_t grid = std::min<int64_t>((items + kThreads - 1) / kThreads, 65536);
+  const void *comb;
+  if (a.row_blocks <= 1) comb = (const void *)cpr_bwd_combine_kernel<1>;
+  else if (a.row_blocks <= 2) comb = (const void *)cpr_bwd_combine_kernel<2>;
+  else if (a.row_blocks <= 4) comb = (const void *)cpr_bwd_combine_kernel<4>;
+  else if (a.row_blocks <= 8) comb = (const void *)cpr_bwd_combine_kernel<8>;
+  else if (a.row_blocks <= 16) comb = (const void *)cpr_bwd_combine_kernel<16>;
+  else if (a.row_blocks <= 32) comb = (const void *)cpr_bwd_combine_kernel<32>;
+  else comb = (const void *)cpr_bwd_combine_kernel<64>;
+  return launch1(comb, grid, a, st);
+}
+
+}  // namespace gdn

@@ -1,0 +1,222 @@
+// Device helpers shared by the forward and backward kernels: input loads (bf16 widened
+// exactly), state-row transfers, the LDS layout of staged k/q vectors, and the mapping of
+// workgroups to sequences and head pairs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace gdn {
+namespace io {
+
+constexpr int kMaxRankedSeqs = 1024;
+
+// ---------------------------------------------------------------------- loads and stores
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void *base, int64_t idx) {
+  if constexpr (BF16)
+    return __uint_as_float((uint32_t)static_cast<const uint16_t *>(base)[idx] << 16);
+  else
+    return static_cast<const float *>(base)[idx];
+}
+
+// Four consecutive input elements starting at idx (idx % 4 == 0), widened to binary32.
+template <bool BF16>
+__device__ __forceinline__ float4 load4(const void *base, int64_t idx) {
+  if constexpr (BF16) {
+    const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(base) + idx);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+  } else {
+    return *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + idx);
+  }
+}
+
+template <int M, bool BF16>
+__device__ __forceinline__ void load_input(const void *base, int64_t idx, float (&r)[M]) {
+  if constexpr (M % 4 == 0) {
+#pragma unroll
+    for (int g = 0; g < M / 4; ++g) {
+      const float4 x = load4<BF16>(base, idx + 4 * g);
+      r[4 * g] = x.x; r[4 * g + 1] = x.y; r[4 * g + 2] = x.z; r[4 * g + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < M; ++e) r[e] = load1<BF16>(base, idx + e);
+  }
+}
+
+template <int M>
+__device__ __forceinline__ void load_row(const float *src, float (&r)[M]) {
+  if constexpr (M % 4 == 0) {
+#pragma unroll
+    for (int g = 0; g < M / 4; ++g) {
+      const float4 x = reinterpret_cast<const float4 *>(src)[g];
+      r[4 * g] = x.x; r[4 * g + 1] = x.y; r[4 * g + 2] = x.z; r[4 * g + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < M; ++e) r[e] = src[e];
+  }
+}
+
+template <int M>
+__device__ __forceinline__ void store_row(float *dst, const float (&r)[M]) {
+  if constexpr (M % 4 == 0) {
+#pragma unroll
+    for (int g = 0; g < M / 4; ++g)
+      reinterpret_cast<float4 *>(dst)[g] =
+          make_float4(r[4 * g], r[4 * g + 1], r[4 * g + 2], r[4 * g + 3]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < M; ++e) dst[e] = r[e];
+  }
+}
+
+// LDS layout of one staged k or q vector (D floats). When a lane's slice (M floats) is a
+// whole number of float4, group g of lane l sits at float4 slot g*L + l, so one ds_read_b128
+// per group covers L*16 contiguous bytes across the lanes of a row; otherwise plain order.
+template <int D, int L>
+__device__ __forceinline__ int stage_slot(int c) {  // float offset of logical floats 4c..4c+3
+  constexpr int M = D / L;
+  if constexpr (M % 4 == 0) {
+    const int e = 4 * c;
+    return (((e % M) / 4) * L + e / M) * 4;
+  } else {
+    return 4 * c;
+  }
+}
+
+template <int D, int L>
+__device__ __forceinline__ void lds_slice(const float *vec, int lane, float (&r)[D / L]) {
+  constexpr int M = D / L;
+  if constexpr (M % 4 == 0) {
+#pragma unroll
+    for (int g = 0; g < M / 4; ++g) {
+      const float4 x = *reinterpret_cast<const float4 *>(vec + (g * L + lane) * 4);
+      r[4 * g] = x.x; r[4 * g + 1] = x.y; r[4 * g + 2] = x.z; r[4 * g + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < M; ++e) r[e] = vec[lane * M + e];
+  }
+}
+
+// --------------------------------------------------------------------------- scheduling
+
+// Token range of sequence n, clamped to [0, T) so that bad cu_seqlens cannot address
+// outside the buffers.
+__device__ __forceinline__ void seq_range(const int32_t *cu, int n, int64_t T, int64_t &bos,
+                                          int64_t &eos) {
+  int64_t lo = cu[n], hi = cu[n + 1];
+  lo = lo < 0 ? 0 : (lo > T ? T : lo);
+  hi = hi < lo ? lo : (hi > T ? T : hi);
+  bos = lo;
+  eos = hi;
+}
+
+// The sequence of the given rank when sequences are ordered by decreasing length (ties by
+// index); natural order beyond kMaxRankedSeqs sequences. Uniform over the workgroup.
+__device__ inline int ranked_sequence(const int32_t *cu, int N, int64_t T, int rank, int *s_len,
+                               int *s_pick) {
+  if (N > kMaxRankedSeqs) return rank;
+  for (int j = threadIdx.x; j < N; j += blockDim.x) {
+    int64_t b, e;
+    seq_range(cu, j, T, b, e);
+    s_len[j] = (int)(e - b);
+  }
+  if (threadIdx.x == 0) *s_pick = rank;  // overwritten below: ranks are a permutation
+  __syncthreads();
+  for (int j = threadIdx.x; j < N; j += blockDim.x) {
+    const int lj = s_len[j];
+    int r = 0;
+    for (int m = 0; m < N; ++m) {
+      const int lm = s_len[m];
+      r += (lm > lj) | ((lm == lj) & (m < j));
+    }
+    if (r == rank) *s_pick = j;
+  }
+  __syncthreads();
+  return *s_pick;
+}
+
+// Workgroup -> (head pair, row block), XCD-aware. The dispatcher hands workgroups to the
+// 8 XCDs (each with its own L2) in round-robin order of workgroup id. Pairs (work units of
+// one sequence and value head, in scheduling order) are taken 8 at a time; within such a
+// group, pair g*8+x gets every workgroup id congruent to x mod 8, so all row blocks of a
+// pair run on one XCD and read its q, k, a and b through one L2. A last group of fewer than
+// 8 pairs is laid out linearly.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ void block_work(int b, int pairs, int rblocks, int &pair, int &rb) {
+  const int group = b / (kXcds * rblocks), within = b % (kXcds * rblocks);
+  if (group < pairs / kXcds) {
+    pair = group * kXcds + within % kXcds;
+    rb = within / kXcds;
+  } else {
+    pair = group * kXcds + within / rblocks;
+    rb = within % rblocks;
+  }
+}
+
+// Index of sequence n's first chunk-boundary state: sum over m < n of floor(T_m / C).
+__device__ inline int64_t first_chunk_slot(const int32_t *cu, int n, int64_t T, int C, int *s_acc) {
+  if (threadIdx.x == 0) *s_acc = 0;
+  __syncthreads();
+  int local = 0;
+  for (int m = threadIdx.x; m < n; m += blockDim.x) {
+    int64_t b, e;
+    seq_range(cu, m, T, b, e);
+    local += (int)((e - b) / C);
+  }
+  atomicAdd(s_acc, local);
+  __syncthreads();
+  return *s_acc;
+}
+
+// Raw register copy of four input elements: bf16 stays packed until it is written to LDS.
+template <bool BF16>
+struct Raw4 {
+  using type = float4;
+};
+template <>
+struct Raw4<true> {
+  using type = uint2;
+};
+
+template <bool BF16>
+__device__ __forceinline__ typename Raw4<BF16>::type load_raw4(const void *base, int64_t idx) {
+  if constexpr (BF16)
+    return *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(base) + idx);
+  else
+    return *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + idx);
+}
+
+// One input element kept raw (bf16 bits or binary32 bits) until it is written to LDS, so
+// that no arithmetic on it forces the prefetch loads to complete early.
+template <bool BF16>
+__device__ __forceinline__ uint32_t load_raw1(const void *base, int64_t idx) {
+  if constexpr (BF16)
+    return static_cast<const uint16_t *>(base)[idx];
+  else
+    return __float_as_uint(static_cast<const float *>(base)[idx]);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float widen1(uint32_t r) {
+  return __uint_as_float(BF16 ? r << 16 : r);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float4 widen4(typename Raw4<BF16>::type r) {
+  if constexpr (BF16)
+    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u),
+                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xFFFF0000u));
+  else
+    return r;
+}
+
+}  // namespace io
+}  // namespace gdn

@@ -133,4 +133,35 @@ __device__ __forceinline__ float row_token(float (&s)[D / L], float a, float b, 
   return contract_dot<D, L>(s, q);
 }
 
+// --------------------------------------------------------------------------- backward
+// The backward steps of one token on one row, sh being the lane's slice of dL/ds. The
+// reverse scan and the chunk kernel both use these, so they produce the same dL/ds bits.
+
+// sh_e = fmaf(g, q_e, sh_e): adds the readout's share, g = dL/do_i.
+template <int D, int L>
+__device__ __forceinline__ void row_bwd_absorb(float (&sh)[D / L], float g,
+                                               const float (&q)[D / L]) {
+#pragma unroll
+  for (int e = 0; e < RowShape<D, L>::M; ++e) sh[e] = __builtin_fmaf(g, q[e], sh[e]);
+}
+
+// dh = dot(sh, k); dv_i = b * dh; xh_e = fmaf(-dv_i, k_e, sh_e). Returns dv_i.
+template <int D, int L>
+__device__ __forceinline__ float row_bwd_delta(const float (&sh)[D / L], const float (&k)[D / L],
+                                               float b, float (&xh)[D / L], float &dh) {
+  dh = contract_dot<D, L>(sh, k);
+  const float dv_i = b * dh;
+  const float uh = -dv_i;
+#pragma unroll
+  for (int e = 0; e < RowShape<D, L>::M; ++e) xh[e] = __builtin_fmaf(uh, k[e], sh[e]);
+  return dv_i;
+}
+
+// sh_e = a * xh_e: dL/ds of the previous state.
+template <int D, int L>
+__device__ __forceinline__ void row_bwd_decay(float (&sh)[D / L], float a, const float (&xh)[D / L]) {
+#pragma unroll
+  for (int e = 0; e < RowShape<D, L>::M; ++e) sh[e] = a * xh[e];
+}
+
 }  // namespace gdn

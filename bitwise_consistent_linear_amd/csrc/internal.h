@@ -47,6 +47,38 @@ struct DecodeArgs {
   float *state, *o, *resync_states;
 };
 
+// Arguments of the backward (plan, state, chunk and combine kernels); validated on the host.
+struct BwdArgs {
+  int32_t num_seqs, num_qk_heads, num_v_heads, d_k, d_v, chunk;
+  int32_t bf16;
+  int32_t slots_max;   // chunk slots the plan may fill: total_chunks + num_seqs
+  int32_t row_blocks;  // blocks of 16 rows per value head in the chunk kernel
+  int64_t total_tokens;
+  int64_t total_chunks;
+  const int32_t *cu_seqlens;
+  const void *q, *k, *v;
+  const float *a, *b, *initial_state, *chunk_states, *d_o, *d_final_state;
+  float *dq, *dk, *dv, *da, *db, *d_initial_state;
+  // workspace
+  int32_t *plan;        // [0]: slots used; then (sequence, chunk) pairs
+  int32_t *plan_cbase;  // [N]: index of each sequence's first chunk state
+  float *dsh_bnd;       // [total_chunks, Hv, d_v, d_k]: dL/ds at chunk ends
+  float *partials;      // [T, Hv, row_blocks, 2 d_k + 2]: row-block sums of the shares
+};
+
+// Byte offsets of the backward workspace's parts (each 256-byte aligned).
+struct BwdWorkspace {
+  int64_t plan_off, plan_bytes, cbase_off, cbase_bytes, dsh_off, dsh_bytes;
+  int64_t partials_off, partials_bytes, total, slots_max;
+};
+
+int backward_row_blocks(int d_v);
+BwdWorkspace backward_workspace(int64_t num_seqs, int64_t num_v_heads, int64_t d_k,
+                                int64_t d_v, int64_t total_tokens, int64_t total_chunks);
+int64_t backward_state_grid(const BwdArgs &args, int lanes_per_row);
+int64_t backward_chunk_grid(const BwdArgs &args);
+hipError_t launch_backward(const BwdArgs &args, int lanes_per_row, hipStream_t stream);
+
 // Enqueue the kernels. lanes_per_row is 16, 8 or 4. Return the HIP launch status.
 hipError_t launch_scan(const ScanArgs &args, int lanes_per_row, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &args, int lanes_per_row, hipStream_t stream);

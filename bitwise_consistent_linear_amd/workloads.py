@@ -181,6 +181,19 @@ def make_packed(name: str, lengths, Hk: int, Hv: int, d: int, chunk: int, bf16: 
     return Workload(name, cu.astype(np.int32), q, k, v, a, b, chunk, bf16)
 
 
+def cotangents(w: Workload, seed: int, with_final: bool = True, final_scale: float = 0.1):
+    """Seeded upstream gradients for the backward: dL/do ~ N(0, 1) float32 [T, Hv, d_v]
+    and, if ``with_final``, dL/dS_final ~ final_scale * N(0, 1) float32 [N, Hv, d_v, d_k]
+    (else None), from the two children of ``SeedSequence(seed)``, drawn as above."""
+    st = np.random.SeedSequence(seed).spawn(2)
+    do = _draw(st[0], (w.total_tokens, w.num_v_heads, w.d_v), "normal")
+    dsf = None
+    if with_final:
+        dsf = _draw(st[1], (w.num_seqs, w.num_v_heads, w.d_v, w.d_k), "normal")
+        dsf *= np.float32(final_scale)
+    return do, dsf
+
+
 # ----------------------------------------------------------------------------------------
 # The five workload configurations.
 

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define GDN_CPR_ABI_VERSION 1
+#define GDN_CPR_ABI_VERSION 2
 #define GDN_CPR_LEAVES 16
 #define GDN_CPR_IDENTITY_BYTES 32
 
@@ -170,6 +170,63 @@ gdn_status_t gdn_cpr_decode_step(const gdn_shape_t *shape, const uint8_t *expect
                                  const int32_t *pos, const void *q, const void *k,
                                  const void *v, const float *a, const float *b, float *state,
                                  float *o, float *resync_states, void *stream);
+
+/* Bytes of device workspace that gdn_cpr_trainer_bwd needs for this shape, total_tokens
+ * and total_chunks, into *bytes (host). Host only. Errors: GDN_E_NULL, GDN_E_UNSUPPORTED
+ * (chunk not 16, 32 or 64), GDN_E_SHAPE (sizes outside the claims of gdn_cpr_trainer_bwd). */
+gdn_status_t gdn_cpr_trainer_bwd_workspace(const gdn_shape_t *shape, int64_t total_tokens,
+                                           int64_t total_chunks, size_t *bytes);
+
+/* trainer_bwd: gradients of a scalar loss L through gdn_cpr_trainer_fwd, given dL/do and
+ * dL/d(final state), in a fixed operation order, so the same inputs give the same bits on
+ * every launch (the backward half of the trainer's forward+backward step in the IsoExec
+ * table of stage costs, agentlenshq.com, section "Chunkwise-Parallel Recurrent (CPR) Gated
+ * DeltaNet"; the fixed reduction tree with binary32 accumulation follows that page's
+ * section on achieving parallel invariance). The pages give no backward arithmetic; this
+ * library's order, hashed into the contract identity, is, per row i and token t in reverse
+ * order, with sh = dL/dS_t[i, :] (starting from d_final_state, or zeros), g = d_o[t, h, i],
+ * s and s_prev the row after and before token t, x = a*s_prev, and u, d as in the forward:
+ *     sh_e = fmaf(g, q_e, sh_e)        pq_e = g * s_e
+ *     dh = dot(sh, k)   dv_i = b*dh    pb = dh * (v_i - u)
+ *     xh_e = fmaf(-dv_i, k_e, sh_e)    pk_e = fmaf(-dv_i, x_e, d * sh_e)
+ *     pa = dot(xh, s_prev)             sh_e = a * xh_e
+ * dv[t, h, i] = dv_i; d_initial_state[n, h, i, :] = sh after the sequence's first token.
+ * dq[t, hk, e], dk[t, hk, e], da[t, h] and db[t, h] sum pq_e, pk_e, pa and pb over the rows
+ * i = 0 .. d_v-1 by a pairwise tree in natural order, where at every level a pair whose
+ * second member holds no row passes its first member on unchanged; then dq and dk add the
+ * value heads of the q/k group hk in ascending order, left to right.
+ * Arguments:
+ *   shape, expected_identity, cu_seqlens, total_tokens, q, k, v, a, b, initial_state:
+ *                    as passed to the gdn_cpr_trainer_fwd call being differentiated;
+ *                    shape->chunk must be 16, 32 or 64
+ *   chunk_states     [total_chunks, Hv, d_v, d_k]: that call's output (read only); NULL
+ *                    only when total_chunks == 0
+ *   total_chunks     sum_n floor(T_n / C), as for gdn_cpr_trainer_fwd
+ *   d_o              float [T, Hv, d_v]: dL/do (required when T > 0)
+ *   d_final_state    float [N, Hv, d_v, d_k]: dL/d(state after each sequence's last token),
+ *                    or NULL for zeros
+ *   dq, dk           float [T, Hk, d_k] outputs; dv float [T, Hv, d_v]; da, db float [T, Hv]
+ *                    (required when T > 0)
+ *   d_initial_state  float [N, Hv, d_v, d_k] output, written whether or not initial_state
+ *                    is NULL (required when N > 0)
+ *   workspace        device memory of at least gdn_cpr_trainer_bwd_workspace() bytes,
+ *                    256-byte aligned, owned by the caller; its contents on entry do not
+ *                    matter and are overwritten. Calls that share a workspace must not run
+ *                    concurrently.
+ *   stream           hipStream_t or NULL.
+ * Outputs must not alias inputs, each other or the workspace. Errors: as for
+ * gdn_cpr_trainer_fwd; GDN_E_UNSUPPORTED for chunk 128 or 256; GDN_E_NULL for a missing
+ * required pointer or workspace; GDN_E_SHAPE for total_chunks outside [0, T / C], a
+ * workspace smaller than reported or misaligned, or a grid too large. */
+gdn_status_t gdn_cpr_trainer_bwd(const gdn_shape_t *shape, const uint8_t *expected_identity,
+                                 const int32_t *cu_seqlens, int64_t total_tokens,
+                                 const void *q, const void *k, const void *v, const float *a,
+                                 const float *b, const float *initial_state,
+                                 const float *chunk_states, int64_t total_chunks,
+                                 const float *d_o, const float *d_final_state, float *dq,
+                                 float *dk, float *dv, float *da, float *db,
+                                 float *d_initial_state, void *workspace,
+                                 size_t workspace_bytes, void *stream);
 
 /* Text describing the calling thread's last non-GDN_OK status ("" if none). The pointer
  * stays valid until the thread's next call into the library. Host only. */

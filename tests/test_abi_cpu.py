@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\s[TW]\s+(gdn_\w+)$", out, flags=re.M))
@@ -68,12 +68,15 @@ def test_identities_are_distinct():
     assert len(ids) == len(CHUNKS) * len(DKS)
 
 
-def test_identity_matches_committed_digest():
-    with open(os.path.join(GOLDEN, "contract_identity.json")) as f:
-        want = json.load(f)
-    for key, hexdigest in want["identities"].items():
-        c, d = (int(x) for x in key.split(","))
-        assert api.contract_identity(c, d).hex() == hexdigest, key
+@pytest.mark.parametrize("chunk", CHUNKS)
+@pytest.mark.parametrize("d_k", DKS)
+def test_contract_text_matches_the_written_spec(chunk, d_k):
+    """tests/golden/contract_text.txt is the contract written out by hand; the library's
+    text, and so its identity, must be exactly that text for every admitted (C, d_k)."""
+    with open(os.path.join(GOLDEN, "contract_text.txt")) as f:
+        want = f.read().replace("{chunk}", str(chunk)).replace("{d_k}", str(d_k))
+    assert api.contract_string(chunk, d_k) == want
+    assert api.contract_identity(chunk, d_k) == hashlib.sha256(want.encode()).digest()
 
 
 @pytest.mark.parametrize("chunk,d_k", [(48, 128), (0, 128), (64, 48), (64, 256), (-16, 16)])
@@ -126,6 +129,17 @@ def prefill(L, sh, identity=None, T=128, **ptrs):
                              p["a"], p["b"], p["s0"], p["o"], p["fs"], None)
 
 
+def bwd(L, sh, identity=None, T=128, total_chunks=2, ws_bytes=1 << 30, **ptrs):
+    p = dict(cu=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s0=None, cs=FAKE, do=FAKE,
+             dsf=None, dq=FAKE, dk=FAKE, dv=FAKE, da=FAKE, db=FAKE, ds0=FAKE, ws=FAKE)
+    p.update(ptrs)
+    idb = ident(sh) if identity is None else identity
+    return L.gdn_cpr_trainer_bwd(ctypes.byref(sh), idb, p["cu"], T, p["q"], p["k"], p["v"],
+                                 p["a"], p["b"], p["s0"], p["cs"], total_chunks, p["do"],
+                                 p["dsf"], p["dq"], p["dk"], p["dv"], p["da"], p["db"],
+                                 p["ds0"], p["ws"], ws_bytes, None)
+
+
 def decode(L, sh, identity=None, **ptrs):
     p = dict(pos=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, state=FAKE, o=FAKE, rs=None)
     p.update(ptrs)
@@ -169,6 +183,22 @@ REFUSALS = [
     ("decode misaligned resync", lambda L: decode(L, shape(), rs=FAKE + 4), api.GDN_E_SHAPE),
     ("decode wrong identity", lambda L: decode(L, shape(), identity=b"\x01" * 32), api.GDN_E_IDENTITY),
     ("decode chunk not admitted", lambda L: decode(L, shape(chunk=100)), api.GDN_E_UNSUPPORTED),
+    ("bwd wrong identity", lambda L: bwd(L, shape(), identity=bytes(32)), api.GDN_E_IDENTITY),
+    ("bwd chunk 128", lambda L: bwd(L, shape(chunk=128), total_chunks=1), api.GDN_E_UNSUPPORTED),
+    ("bwd chunk 256", lambda L: bwd(L, shape(chunk=256), total_chunks=0), api.GDN_E_UNSUPPORTED),
+    ("bwd more chunks than T/C", lambda L: bwd(L, shape(), total_chunks=3), api.GDN_E_SHAPE),
+    ("bwd null chunk_states", lambda L: bwd(L, shape(), cs=None), api.GDN_E_NULL),
+    ("bwd null d_o", lambda L: bwd(L, shape(), do=None), api.GDN_E_NULL),
+    ("bwd null dk", lambda L: bwd(L, shape(), dk=None), api.GDN_E_NULL),
+    ("bwd null db", lambda L: bwd(L, shape(), db=None), api.GDN_E_NULL),
+    ("bwd null dS0", lambda L: bwd(L, shape(), ds0=None), api.GDN_E_NULL),
+    ("bwd null workspace", lambda L: bwd(L, shape(), ws=None), api.GDN_E_NULL),
+    ("bwd misaligned workspace", lambda L: bwd(L, shape(), ws=FAKE + 64), api.GDN_E_SHAPE),
+    ("bwd workspace too small", lambda L: bwd(L, shape(), ws_bytes=256), api.GDN_E_SHAPE),
+    ("bwd misaligned d_final_state", lambda L: bwd(L, shape(), dsf=FAKE + 4), api.GDN_E_SHAPE),
+    ("bwd misaligned dq", lambda L: bwd(L, shape(), dq=FAKE + 2), api.GDN_E_SHAPE),
+    ("bwd null q", lambda L: bwd(L, shape(), q=None), api.GDN_E_NULL),
+    ("bwd heads not a multiple", lambda L: bwd(L, shape(num_qk_heads=3)), api.GDN_E_SHAPE),
 ]
 
 
@@ -194,3 +224,20 @@ def test_product_path_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", text, flags=re.M), f
                 assert "gdn_oracle" not in text and "liboracle" not in text, f
+
+
+def test_bwd_workspace_size(L):
+    """The workspace holds the plan, the chunk-boundary gradients and the row-block partial
+    sums; it grows with tokens and chunks and is refused for unadmitted sizes."""
+    sh = shape(num_seqs=3, num_v_heads=4, d_k=64, d_v=40, chunk=32)
+    small = api.trainer_bwd_workspace_bytes(sh, 100, 2)
+    big = api.trainer_bwd_workspace_bytes(sh, 1000, 30)
+    rb = 3  # ceil(40 / 16) blocks of 16 rows
+    assert small >= 100 * 4 * rb * (2 * 64 + 2) * 4 + 2 * 4 * 40 * 64 * 4
+    assert big > small and small % 256 == 0 and big % 256 == 0
+    n = ctypes.c_size_t(0)
+    assert L.gdn_cpr_trainer_bwd_workspace(ctypes.byref(shape(chunk=128)), 128, 1,
+                                           ctypes.byref(n)) == api.GDN_E_UNSUPPORTED
+    assert L.gdn_cpr_trainer_bwd_workspace(ctypes.byref(sh), 100, 4,
+                                           ctypes.byref(n)) == api.GDN_E_SHAPE
+    assert L.gdn_cpr_trainer_bwd_workspace(ctypes.byref(sh), 100, 2, None) == api.GDN_E_NULL

@@ -4,6 +4,7 @@
 * no packed fp32 instructions and no unfused multiply-add (v_mad/v_mac) forms;
 * every fused multiply-add is a v_fma/v_fmac, every DPP reduction step an add;
 * no register spills in any kernel.
+Forward, decode and backward kernels alike.
 """
 
 import re
@@ -27,6 +28,10 @@ def test_all_kernels_present(asm):
     names = kernels(asm)
     assert sum("cpr_scan_kernel" in n for n in names) == 4 * 3 * 2 * 2
     assert sum("cpr_decode_kernel" in n for n in names) == 4 * 3 * 2
+    assert sum("cpr_bwd_plan_kernel" in n for n in names) == 1
+    assert sum("cpr_bwd_state_kernel" in n for n in names) == 4 * 3 * 2
+    assert sum("cpr_bwd_chunk_kernel" in n for n in names) == 4 * 2
+    assert sum("cpr_bwd_combine_kernel" in n for n in names) == 7
 
 
 def test_denormals_kept(asm):
