@@ -6,10 +6,11 @@ boundary) over the trainer workload: 4 sequences x 4096 tokens, 16 heads, d_k = 
 C = 64, bf16 q/k/v, fp32 a/b/state/o. `value` is tokens/s of that step with inputs already
 in HBM. The same line also reports, under "cases", engine_prefill tokens/s (64 varlen
 sequences, 262144 tokens, 16 q/k / 32 v heads), the engine_decode step time (256
-sequences after a 1000-token prefill, 512 steps) and the long-context runs, each with its
+sequences after a 1000-token prefill, 512 steps), the backward (gdn_cpr_trainer_bwd) on
+the trainer workload and the long-context runs, each with its
 fraction of the relevant peak, plus the CPU oracle timed on the host as a baseline.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cases all|main]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cases all|main|bwd]
                        [--no-cpu-baseline]
 """
 
@@ -29,7 +30,7 @@ HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, spec sheet
 FP32_FMA_PEAK_TFLOPS = 78.6       # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (no packed fp32)
 FP32_PACKED_PEAK_TFLOPS = 157.3   # spec-sheet figure with packed fp32 (not used by these kernels)
 METRIC = "GDN-CPR tokens/s (trainer_fwd, prefill), decode-step us, % of HBM peak"
-KERNEL_SOURCES = ["cpr_kernels.hip", "cpr_row.hpp"]
+KERNEL_SOURCES = ["cpr_kernels.hip", "cpr_row.hpp", "cpr_io.hpp"]
 COPY_PROBE_BYTES = 256 << 20  # read once and written once by the calibration copy
 
 
@@ -49,6 +50,27 @@ def flops_per_token_head(dk, dv):
     # per row and token: decay d_k mul; two contract dots of 16 mul + (d_k-16) fma + 15 add
     # = 2 d_k - 1 flop each; delta 2; rank-1 update d_k fma = 2 d_k  ->  7 d_k flop
     return 7 * dk * dv
+
+
+def bwd_flops_per_token_head(dk, dv):
+    # per row and token, in the backward contract's order: one recompute of the forward
+    # state (decay d_k, dot 2 d_k - 1, delta 2, update 2 d_k: 5 d_k + 1); the backward's own
+    # work: sh += g q (2 d_k), pq = g s (d_k), dh = dot (2 d_k - 1), dv and pb (2),
+    # xh (2 d_k), pk (3 d_k), pa = dot (2 d_k - 1), sh = a xh (d_k): 13 d_k; the row sums of
+    # dq and dk (2 d_k adds per row) -> 20 d_k flop, rounded down
+    return 20 * dk * dv
+
+
+def bwd_bytes(w):
+    """Algorithmic HBM bytes of one backward call: inputs (q, k, v, a, b, d_o, d_final_state,
+    the chunk states) read once, outputs (dq, dk, dv, da, db, dS0) written once."""
+    el = 2 if w.bf16 else 4
+    T, Hk, Hv, dk, dv, N = w.total_tokens, w.num_qk_heads, w.num_v_heads, w.d_k, w.d_v, w.num_seqs
+    state = Hv * dv * dk * 4
+    reads = (T * Hk * dk * el * 2 + T * Hv * dv * el + T * Hv * 4 * 2 + T * Hv * dv * 4
+             + (w.total_chunks + N) * state + (N + 1) * 4)
+    writes = T * Hk * dk * 4 * 2 + T * Hv * dv * 4 + T * Hv * 4 * 2 + N * state
+    return reads + writes
 
 
 def scan_bytes(w, with_o=True, chunk_states=0, final_states=0, initial_states=0):
@@ -225,6 +247,43 @@ def bench_prefill(steps, warmup):
             "steps": steps, "roofline": roofline_alu(flops, ms), "hbm": hbm(nbytes, ms)}
 
 
+def bench_trainer_bwd(steps, warmup, fwd_kernel_ms):
+    """gdn_cpr_trainer_bwd on the trainer workload, given seeded dL/do and dL/dS_final."""
+    import torch
+    from bitwise_consistent_linear_amd import api
+    from bitwise_consistent_linear_amd import workloads as W
+    w = W.trainer_fwd()
+    do, dsf = W.cotangents(w, 11)
+    log("trainer_bwd: same workload, seeded dL/do and dL/dS_final")
+    cu, q, k, v, a, b = (up(x) for x in (w.cu_seqlens, w.q, w.k, w.v, w.a, w.b))
+    ddo, ddsf = up(do), up(dsf)
+    tc = w.total_chunks
+    _, cs = api.trainer_fwd(cu, q, k, v, a, b, chunk=w.chunk, total_chunks=tc)
+    shape = api.GdnShape(w.num_seqs, w.num_qk_heads, w.num_v_heads, w.d_k, w.d_v, w.chunk,
+                         api.GDN_DTYPE_BF16)
+    need = api.trainer_bwd_workspace_bytes(shape, w.total_tokens, tc)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    grads = api.trainer_bwd(cu, q, k, v, a, b, cs, ddo, chunk=w.chunk, d_final_state=ddsf,
+                            total_chunks=tc, workspace=ws)
+
+    def step():
+        api.trainer_bwd(cu, q, k, v, a, b, cs, ddo, chunk=w.chunk, d_final_state=ddsf,
+                        total_chunks=tc, workspace=ws, out=grads)
+
+    wall, per = timed(step, steps, warmup)
+    ms = sum(per) / len(per)
+    flops = bwd_flops_per_token_head(w.d_k, w.d_v) * w.total_tokens * w.num_v_heads
+    del q, k, v, cs, ws, grads
+    return {"workload": "trainer_bwd: the trainer_fwd workload (4 x 4096 tokens, 16 heads, "
+                        "d=128, C=64, bf16 q/k/v) given dL/do and dL/dS_final; writes dq, dk, "
+                        "dv, da, db, dS0",
+            "tokens_per_s": round(w.total_tokens / (wall / steps), 1),
+            "ms_per_call": round(wall / steps * 1e3, 4), "kernel_ms": round(ms, 4),
+            "fwd_plus_bwd_kernel_ms": round(fwd_kernel_ms + ms, 4),
+            "workspace_bytes": int(need), "steps": steps,
+            "roofline": roofline_alu(flops, ms), "hbm": hbm(bwd_bytes(w), ms)}
+
+
 def bench_decode_after_prefill(w, prefix, nsteps, warmup_steps, label):
     """Prefill `prefix` tokens of every sequence, then time decode steps one by one."""
     import torch
@@ -346,7 +405,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cases", choices=["all", "main"], default="all")
+    ap.add_argument("--cases", choices=["all", "main", "bwd"], default="all",
+                    help="all: every case; main: trainer_fwd only; bwd: trainer_fwd and the "
+                         "backward (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (untimed), the known-size "
@@ -409,6 +470,8 @@ def main():
     }
     if args.cases == "all":
         cases = {}
+        cases["trainer_bwd"] = bench_trainer_bwd(max(3, args.steps // 4), 1, kernel_ms)
+        torch.cuda.empty_cache()
         cases["engine_prefill"] = bench_prefill(max(3, args.steps // 4), 1)
         torch.cuda.empty_cache()
         cases["engine_decode"] = bench_decode()
@@ -416,6 +479,8 @@ def main():
         cases["long_context"] = bench_long(max(2, args.steps // 10))
         torch.cuda.empty_cache()
         out["cases"] = cases
+    elif args.cases == "bwd":
+        out["cases"] = {"trainer_bwd": bench_trainer_bwd(max(3, args.steps // 4), 1, kernel_ms)}
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the trainer_fwd workload")
         out["cpu_baseline"] = cpu_baseline(w)

@@ -254,6 +254,58 @@ __global__ __launch_bounds__(kThreads) void cpr_bwd_state_kernel(const BwdArgs p
 
 // ---------------------------------------------------------------------------- chunk pass
 
+// Lane swaps between the 16-lane rows of a wave (gfx950): swap16 exchanges the odd rows of
+// `hi` with the even rows of `lo`; swap32 exchanges the upper 32 lanes of `hi` with the lower
+// 32 lanes of `lo`. (a, b) are the two registers afterwards.
+__device__ __forceinline__ void swap16(float hi, float lo, float &a, float &b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(hi), __float_as_uint(lo),
+                                                  false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float hi, float lo, float &a, float &b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(hi), __float_as_uint(lo),
+                                                  false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// One token's shares summed over the four rows of a wave (row r in lanes 16r .. 16r+15) in
+// the row tree's order, (r0 + r1) + (r2 + r3), scattered over the lanes. Each level is one
+// swap and one add: after a swap, register a holds the pair's first row and b its second,
+// so a + b is the pair's sum on both rows' lanes, and a alone is the pass-through value.
+// On return, lane (r, c) holds the 4-row sums of z[0 .. H-1] = elements
+// (r odd ? dq : dk)[c M + (r < 2 ? H : 0) + 0 .. H-1] (H = M / 2; for M = 1 every lane holds
+// element c, and lanes of rows 0 and 1 report it), and y = (r odd ? da : db).
+// c1: this lane's level-one pair is combined; c2: the two halves are combined. FULL: all
+// four rows hold rows below d_v (no pass-through).
+template <int M, bool FULL>
+__device__ __forceinline__ void rows4_sum(const float (&pq)[M], const float (&pk)[M], float pa,
+                                          float pb, bool c1, bool c2,
+                                          float (&z)[M >= 2 ? M / 2 : 1], float &y) {
+  float w[M], a, b;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    swap16(pk[j], pq[j], a, b);
+    w[j] = (FULL || c1) ? a + b : a;
+  }
+  if constexpr (M >= 2) {
+    constexpr int H = M / 2;
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      swap32(w[H + j], w[j], a, b);
+      z[j] = (FULL || c2) ? a + b : a;
+    }
+  } else {
+    swap32(w[0], w[0], a, b);
+    z[0] = (FULL || c2) ? a + b : a;
+  }
+  swap16(pb, pa, a, b);
+  const float x = (FULL || c1) ? a + b : a;
+  swap32(x, x, a, b);
+  y = (FULL || c2) ? a + b : a;
+}
+
 // Checkpoints and a sub-block of recomputed states live in registers: allow up to 256
 // VGPRs (two waves per SIMD) rather than spill.
 template <int D, bool BF16>
@@ -262,15 +314,20 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
   constexpr int L = kChunkLanes, ROWS = kChunkRows, M = D / L, SB = kSub;
   constexpr int WAVES = kThreads / 64, RPW = 64 / L;  // rows per wave
   constexpr int PW = 2 * D + 2;                       // shares of a token: dq, dk, da, db
+  constexpr int PWP = 2 * D + 4;                      // their LDS row, 16-byte aligned
+  constexpr int H = M >= 2 ? M / 2 : 1;               // elements each lane holds after rows4_sum
   constexpr int GROUPS = D / 4;
-  __shared__ __align__(16) float sk[SB * D];
-  __shared__ __align__(16) float sq[SB * D];
-  __shared__ float sv[SB * ROWS], sg[SB * ROWS], sa[SB], sb[SB];
-  __shared__ __align__(16) float srow[WAVES][RPW][PW];  // one token's shares of a wave's rows
-  __shared__ float swave[SB][WAVES][PW];                // wave sums of a sub-block's tokens
+  constexpr int KQ_ITEMS = SB * GROUPS, V_ITEMS = SB * ROWS;
+  constexpr int KQ_PER = (KQ_ITEMS + kThreads - 1) / kThreads;
+  static_assert(V_ITEMS <= kThreads && SB <= kThreads, "one v/g and a/b item per thread");
+  using raw_t = typename Raw4<BF16>::type;
+  __shared__ __align__(16) float sk[2][SB * D];
+  __shared__ __align__(16) float sq[2][SB * D];
+  __shared__ float sv[2][V_ITEMS], sg[2][V_ITEMS], sa[2][SB], sb[2][SB];
+  __shared__ __align__(16) float swave[SB][WAVES][PWP];  // wave sums of a sub-block's tokens
 
   const int tid = threadIdx.x, row = tid / L, lane = tid % L;
-  const int wave = tid / 64, wl = tid % 64, rw = row % RPW;
+  const int wave = tid / 64, wl = tid % 64, r4 = wl / L, c16 = wl % L;
   const int Hv = p.num_v_heads, Hk = p.num_qk_heads, dv = p.d_v, RB = p.row_blocks;
   int pair, rblock;
   block_work(blockIdx.x, p.slots_max * Hv, RB, pair, rblock);
@@ -288,6 +345,9 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
   const bool valid = i < dv;
   const int64_t vstride = (int64_t)Hv * dv;
   const int64_t row_off = (((int64_t)n * Hv + h) * dv + i) * D + lane * M;
+  const int wrow0 = r0 + wave * RPW;  // first row of this wave
+  const bool full4 = wrow0 + RPW - 1 < dv;
+  const bool c1 = r4 < 2 ? wrow0 + 1 < dv : wrow0 + 3 < dv, c2 = wrow0 + 2 < dv;
 
   // state at the chunk's start, dL/ds at its end
   float s[M], sh[M];
@@ -310,83 +370,88 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
     }
   }
 
-  // tokens [c0 + j0, c0 + j0 + nt) of the chunk into LDS
-  auto stage = [&](int j0, int nt) {
-    for (int g = tid; g < nt * GROUPS; g += kThreads) {
-      const int tt = g / GROUPS, cc = g % GROUPS;
-      const int64_t src = ((bos + c0 + j0 + tt) * Hk + hk) * D + 4 * cc;
-      *reinterpret_cast<float4 *>(&sk[tt * D + stage_slot<D, L>(cc)]) = load4<BF16>(p.k, src);
-      *reinterpret_cast<float4 *>(&sq[tt * D + stage_slot<D, L>(cc)]) = load4<BF16>(p.q, src);
+  // Tokens [c0 + j0, c0 + j0 + nt) of the chunk: global memory -> registers (fetch), then
+  // registers -> LDS buffer (deposit), so the loads of the next sub-block overlap the
+  // arithmetic of this one. Items past nt repeat the last token and are never read.
+  raw_t rk[KQ_PER], rq[KQ_PER];
+  uint32_t rv = 0;
+  float rg = 0.0f, ra = 0.0f, rb = 0.0f;
+  auto fetch = [&](int j0, int nt) {
+#pragma unroll
+    for (int jj = 0; jj < KQ_PER; ++jj) {
+      const int g = (tid + jj * kThreads) % KQ_ITEMS;
+      const int tt = g / GROUPS < nt ? g / GROUPS : nt - 1;
+      const int64_t src = ((bos + c0 + j0 + tt) * Hk + hk) * D + 4 * (g % GROUPS);
+      rk[jj] = load_raw4<BF16>(p.k, src);
+      rq[jj] = load_raw4<BF16>(p.q, src);
     }
-    for (int e = tid; e < nt * ROWS; e += kThreads) {
-      const int tt = e / ROWS, r = e % ROWS;
-      const int64_t at = (bos + c0 + j0 + tt) * vstride + (int64_t)h * dv + r0 + r;
-      sv[e] = r0 + r < dv ? load1<BF16>(p.v, at) : 0.0f;
-      sg[e] = r0 + r < dv ? p.d_o[at] : 0.0f;
+    {
+      const int e = tid % V_ITEMS;
+      const int tt = e / ROWS < nt ? e / ROWS : nt - 1;
+      const int r = r0 + e % ROWS < dv ? r0 + e % ROWS : dv - 1;
+      const int64_t at = (bos + c0 + j0 + tt) * vstride + (int64_t)h * dv + r;
+      rv = load_raw1<BF16>(p.v, at);
+      rg = p.d_o[at];
     }
-    if (tid < nt) {
-      sa[tid] = p.a[(bos + c0 + j0 + tid) * Hv + h];
-      sb[tid] = p.b[(bos + c0 + j0 + tid) * Hv + h];
-    }
+    const int tt = tid % SB < nt ? tid % SB : nt - 1;
+    ra = p.a[(bos + c0 + j0 + tt) * Hv + h];
+    rb = p.b[(bos + c0 + j0 + tt) * Hv + h];
   };
-
-  // Sums one token's shares over this wave's rows (pairwise, natural order) into swave[j].
-  // A wave's LDS operations complete in order, so each lane may read what other lanes of
-  // the wave wrote just before.
-  const int wrow0 = r0 + wave * RPW;  // first row of this wave
-  auto wave_sum = [&](int j, const float (&pq)[M], const float (&pk)[M], float pa, float pb) {
+  auto deposit = [&](int buf) {
 #pragma unroll
-    for (int e = 0; e < M; ++e) {
-      srow[wave][rw][lane * M + e] = pq[e];
-      srow[wave][rw][D + lane * M + e] = pk[e];
+    for (int jj = 0; jj < KQ_PER; ++jj) {
+      const int g = tid + jj * kThreads;
+      if (KQ_ITEMS % kThreads == 0 || g < KQ_ITEMS) {
+        const int off = (g / GROUPS) * D + stage_slot<D, L>(g % GROUPS);
+        *reinterpret_cast<float4 *>(&sk[buf][off]) = widen4<BF16>(rk[jj]);
+        *reinterpret_cast<float4 *>(&sq[buf][off]) = widen4<BF16>(rq[jj]);
+      }
     }
-    if (lane == 0) {
-      srow[wave][rw][2 * D] = pa;
-      srow[wave][rw][2 * D + 1] = pb;
+    if (tid < V_ITEMS) {
+      const bool ok = r0 + tid % ROWS < dv;
+      sv[buf][tid] = ok ? widen1<BF16>(rv) : 0.0f;
+      sg[buf][tid] = ok ? rg : 0.0f;
     }
-    __builtin_amdgcn_wave_barrier();
-    for (int f = wl; f < PW; f += 64) {
-      float v[RPW];
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) v[r] = srow[wave][r][f];
-#pragma unroll
-      for (int w = 1; w < RPW; w *= 2)
-#pragma unroll
-        for (int r = 0; r + w < RPW; r += 2 * w)
-          if (wrow0 + r + w < dv) v[r] = v[r] + v[r + w];
-      swave[j][wave][f] = v[0];
+    if (tid < SB) {
+      sa[buf][tid] = ra;
+      sb[buf][tid] = rb;
     }
-    __builtin_amdgcn_wave_barrier();  // the next token's writes follow these reads
   };
 
   const int nsb = (len + SB - 1) / SB;
-  float ck[kMaxSub][M];  // state at the start of every sub-block
+  auto sub_len = [&](int sbi) { return len - sbi * SB < SB ? len - sbi * SB : SB; };
+  fetch(0, sub_len(0));
+  deposit(0);
+  __syncthreads();
+
+  // forward over the chunk, keeping the state at the start of every sub-block
+  float ck[kMaxSub][M];
   static_for<kMaxSub>([&](auto sbi_c) {
-    constexpr int sbi = decltype(sbi_c)::value;
+    constexpr int sbi = decltype(sbi_c)::value, buf = sbi & 1;
     if (sbi < nsb) {
-      const int nt = len - sbi * SB < SB ? len - sbi * SB : SB;
+      const bool next = sbi + 1 < nsb;
+      if (next) fetch((sbi + 1) * SB, sub_len(sbi + 1));
 #pragma unroll
       for (int e = 0; e < M; ++e) ck[sbi][e] = s[e];
-      __syncthreads();
-      stage(sbi * SB, nt);
-      __syncthreads();
+      const int nt = sub_len(sbi);
       for (int j = 0; j < nt; ++j) {
         float kr[M], x[M];
-        lds_slice<D, L>(&sk[j * D], lane, kr);
-        row_decay<D, L>(s, sa[j], x);
+        lds_slice<D, L>(&sk[buf][j * D], lane, kr);
+        row_decay<D, L>(s, sa[buf][j], x);
         const float u = contract_dot<D, L>(x, kr);
-        row_update<D, L>(s, row_delta(sb[j], sv[j * ROWS + row], u), kr, x);
+        row_update<D, L>(s, row_delta(sb[buf][j], sv[buf][j * ROWS + row], u), kr, x);
       }
+      if (next) deposit(buf ^ 1);  // its last reader finished before the previous barrier
+      __syncthreads();
     }
   });
 
+  // sub-blocks in reverse: recompute the states, run sh back, sum the shares over rows
   static_for<kMaxSub, true>([&](auto sbi_c) {
-    constexpr int sbi = decltype(sbi_c)::value;
+    constexpr int sbi = decltype(sbi_c)::value, buf = sbi & 1;
     if (sbi < nsb) {
-      const int nt = len - sbi * SB < SB ? len - sbi * SB : SB;
-      __syncthreads();
-      stage(sbi * SB, nt);
-      __syncthreads();
+      const int nt = sub_len(sbi);
+      if (sbi > 0) fetch((sbi - 1) * SB, SB);
       float st[SB + 1][M], dif[SB], del[SB];
 #pragma unroll
       for (int e = 0; e < M; ++e) st[0][e] = ck[sbi][e];
@@ -394,11 +459,11 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
       for (int j = 0; j < SB; ++j) {
         if (j < nt) {
           float kr[M], x[M];
-          lds_slice<D, L>(&sk[j * D], lane, kr);
-          row_decay<D, L>(st[j], sa[j], x);
+          lds_slice<D, L>(&sk[buf][j * D], lane, kr);
+          row_decay<D, L>(st[j], sa[buf][j], x);
           const float u = contract_dot<D, L>(x, kr);
-          dif[j] = sv[j * ROWS + row] - u;
-          del[j] = sb[j] * dif[j];
+          dif[j] = sv[buf][j * ROWS + row] - u;
+          del[j] = sb[buf][j] * dif[j];
 #pragma unroll
           for (int e = 0; e < M; ++e) st[j + 1][e] = st[j][e];
           row_update<D, L>(st[j + 1], del[j], kr, x);
@@ -408,9 +473,9 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
       for (int j = SB - 1; j >= 0; --j) {
         if (j < nt) {
           float kr[M], qr[M], x[M], xh[M], pq[M], pk[M], dh;
-          lds_slice<D, L>(&sk[j * D], lane, kr);
-          lds_slice<D, L>(&sq[j * D], lane, qr);
-          const float g = sg[j * ROWS + row], a = sa[j], b = sb[j];
+          lds_slice<D, L>(&sk[buf][j * D], lane, kr);
+          lds_slice<D, L>(&sq[buf][j * D], lane, qr);
+          const float g = sg[buf][j * ROWS + row], a = sa[buf][j], b = sb[buf][j];
           row_bwd_absorb<D, L>(sh, g, qr);
 #pragma unroll
           for (int e = 0; e < M; ++e) pq[e] = g * st[j + 1][e];
@@ -425,7 +490,25 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
           }
           const float pa = contract_dot<D, L>(xh, st[j]);
           row_bwd_decay<D, L>(sh, a, xh);
-          wave_sum(j, pq, pk, pa, pb);
+          float z[H], y;
+          if (full4)
+            rows4_sum<M, true>(pq, pk, pa, pb, c1, c2, z, y);
+          else
+            rows4_sum<M, false>(pq, pk, pa, pb, c1, c2, z, y);
+          float *dst = &swave[j][wave][0];
+          if constexpr (M >= 2) {
+            float *o = dst + ((r4 & 1) ? 0 : D) + c16 * M + (r4 < 2 ? H : 0);
+            if constexpr (H == 4) {
+              *reinterpret_cast<float4 *>(o) = make_float4(z[0], z[1], z[2], z[3]);
+            } else if constexpr (H == 2) {
+              *reinterpret_cast<float2 *>(o) = make_float2(z[0], z[1]);
+            } else {
+              o[0] = z[0];
+            }
+          } else {
+            if (r4 < 2) dst[((r4 & 1) ? 0 : D) + c16] = z[0];
+          }
+          if (c16 == 0 && r4 < 2) dst[2 * D + ((r4 & 1) ? 0 : 1)] = y;
         }
       }
       __syncthreads();
@@ -439,6 +522,8 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
         const int64_t t = bos + c0 + sbi * SB + j;
         p.partials[((t * Hv + h) * RB + rblock) * PW + f] = w0;
       }
+      if (sbi > 0) deposit(buf ^ 1);  // its last reader finished before the barrier above
+      __syncthreads();
     }
   });
 }
