@@ -63,6 +63,17 @@ int scan_lanes(const ScanArgs &a) {
   return 4;
 }
 
+// The backward's state pass is one dependent chain per row (no readout beside it to
+// overlap), so it takes the widest rows that keep at most 2 waves per SIMD.
+int bwd_state_lanes(const ScanArgs &a) {
+  if (const int o = lanes_override()) return o;
+  const int64_t rows = (int64_t)a.num_seqs * a.num_v_heads * a.d_v;
+  const int64_t simds = device_simds();
+  if (rows / 4 <= 2 * simds) return 16;
+  if (rows / 8 <= 2 * simds) return 8;
+  return 4;
+}
+
 // Decode streams every row once per step; 16 lanes per row keeps each lane's slice of the
 // 512-byte row at 32 bytes and gives the most loads in flight.
 int decode_lanes() {
@@ -363,7 +374,7 @@ GDN_EXPORT gdn_status_t gdn_cpr_trainer_bwd(
   args.dsh_bnd = reinterpret_cast<float *>(w + ws.dsh_off);
   args.partials = reinterpret_cast<float *>(w + ws.partials_off);
   if (shape->num_seqs == 0) return gdn::ok();
-  const int L = gdn::scan_lanes(fwd);
+  const int L = gdn::bwd_state_lanes(fwd);
   if (gdn::backward_state_grid(args, L) > gdn::kMaxInt32 ||
       gdn::backward_chunk_grid(args) > gdn::kMaxInt32)
     return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": grid too large");

@@ -8,9 +8,9 @@
 //               sequence's first chunk-state index;
 //   2. state:   a reverse scan of sh per row (as parallel as the forward scan), writing dv,
 //               dS0 and sh at every chunk boundary;
-//   3. chunk:   for every (chunk, value head, block of 16 rows) in parallel: the forward
+//   3. chunk:   for every (chunk, value head, block of 32 rows) in parallel: the forward
 //               states recomputed from the trainer's chunk state (checkpoints every 8 tokens
-//               in registers), sh re-run from the boundary value the state pass stored (the
+//               in registers, each token's v_i - u in LDS), sh re-run from the boundary value the state pass stored (the
 //               same operations, so the same bits), and every token's shares summed over
 //               the block's rows: pairwise in natural row order, within the wave through
 //               LDS, then across the 4 waves; one partial per (token, head, row block);
@@ -38,7 +38,9 @@ constexpr int kStateStage = 16;                   // tokens staged at a time by 
 constexpr int kSub = 8;                           // tokens per recomputed sub-block
 constexpr int kMaxSub = 8;                        // sub-blocks per chunk: C <= 64
 constexpr int kChunkLanes = 16;                   // lanes per row in the chunk kernel
-constexpr int kChunkRows = kThreads / kChunkLanes;
+constexpr int kChunkWaves = 8;                    // waves per chunk-kernel workgroup
+constexpr int kChunkThreads = 64 * kChunkWaves;
+constexpr int kChunkRows = kChunkThreads / kChunkLanes;
 constexpr int kPlanHeader = 4;                    // int32 slots before the (n, c) pairs
 
 // f(std::integral_constant<int, i>) for i = 0 .. N-1 (REVERSE: N-1 .. 0), each with its own
@@ -309,10 +311,11 @@ __device__ __forceinline__ void rows4_sum(const float (&pq)[M], const float (&pk
 // Checkpoints and a sub-block of recomputed states live in registers: allow up to 256
 // VGPRs (two waves per SIMD) rather than spill.
 template <int D, bool BF16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
+__global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void cpr_bwd_chunk_kernel(const BwdArgs p) {
+  constexpr int kThreads = kChunkThreads;
   constexpr int L = kChunkLanes, ROWS = kChunkRows, M = D / L, SB = kSub;
-  constexpr int WAVES = kThreads / 64, RPW = 64 / L;  // rows per wave
+  constexpr int WAVES = kChunkWaves, RPW = 64 / L;  // rows per wave
   constexpr int PW = 2 * D + 2;                       // shares of a token: dq, dk, da, db
   constexpr int PWP = 2 * D + 4;                      // their LDS row, 16-byte aligned
   constexpr int H = M >= 2 ? M / 2 : 1;               // elements each lane holds after rows4_sum
@@ -325,6 +328,7 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
   __shared__ __align__(16) float sq[2][SB * D];
   __shared__ float sv[2][V_ITEMS], sg[2][V_ITEMS], sa[2][SB], sb[2][SB];
   __shared__ __align__(16) float swave[SB][WAVES][PWP];  // wave sums of a sub-block's tokens
+  __shared__ float sdif[kMaxSub * SB][ROWS];             // v_i - u of every token of the chunk
 
   const int tid = threadIdx.x, row = tid / L, lane = tid % L;
   const int wave = tid / 64, wl = tid % 64, r4 = wl / L, c16 = wl % L;
@@ -348,6 +352,11 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
   const int wrow0 = r0 + wave * RPW;  // first row of this wave
   const bool full4 = wrow0 + RPW - 1 < dv;
   const bool c1 = r4 < 2 ? wrow0 + 1 < dv : wrow0 + 3 < dv, c2 = wrow0 + 2 < dv;
+  // where this lane stores its row sums in swave[j][wave][.] (see rows4_sum); computed once
+  int zofs = (M >= 2) ? ((r4 & 1) ? 0 : D) + c16 * M + (r4 < 2 ? H : 0) : ((r4 & 1) ? 0 : D) + c16;
+  int yofs = 2 * D + ((r4 & 1) ? 0 : 1);
+  asm volatile("" : "+v"(zofs), "+v"(yofs));  // keep them in registers, not recomputed per token
+  const bool zwrite = M >= 2 || r4 < 2, ywrite = c16 == 0 && r4 < 2;
 
   // state at the chunk's start, dL/ds at its end
   float s[M], sh[M];
@@ -439,7 +448,9 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
         lds_slice<D, L>(&sk[buf][j * D], lane, kr);
         row_decay<D, L>(s, sa[buf][j], x);
         const float u = contract_dot<D, L>(x, kr);
-        row_update<D, L>(s, row_delta(sb[buf][j], sv[buf][j * ROWS + row], u), kr, x);
+        const float dif = sv[buf][j * ROWS + row] - u;  // d = b (v_i - u), as row_delta
+        if (lane == 0) sdif[sbi * SB + j][row] = dif;
+        row_update<D, L>(s, sb[buf][j] * dif, kr, x);
       }
       if (next) deposit(buf ^ 1);  // its last reader finished before the previous barrier
       __syncthreads();
@@ -457,12 +468,11 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
       for (int e = 0; e < M; ++e) st[0][e] = ck[sbi][e];
 #pragma unroll
       for (int j = 0; j < SB; ++j) {
-        if (j < nt) {
+        if (j < nt) {  // the forward sweep left v_i - u of each token: no dot product here
           float kr[M], x[M];
           lds_slice<D, L>(&sk[buf][j * D], lane, kr);
           row_decay<D, L>(st[j], sa[buf][j], x);
-          const float u = contract_dot<D, L>(x, kr);
-          dif[j] = sv[buf][j * ROWS + row] - u;
+          dif[j] = sdif[sbi * SB + j][row];
           del[j] = sb[buf][j] * dif[j];
 #pragma unroll
           for (int e = 0; e < M; ++e) st[j + 1][e] = st[j][e];
@@ -496,31 +506,30 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
           else
             rows4_sum<M, false>(pq, pk, pa, pb, c1, c2, z, y);
           float *dst = &swave[j][wave][0];
-          if constexpr (M >= 2) {
-            float *o = dst + ((r4 & 1) ? 0 : D) + c16 * M + (r4 < 2 ? H : 0);
-            if constexpr (H == 4) {
-              *reinterpret_cast<float4 *>(o) = make_float4(z[0], z[1], z[2], z[3]);
-            } else if constexpr (H == 2) {
-              *reinterpret_cast<float2 *>(o) = make_float2(z[0], z[1]);
-            } else {
-              o[0] = z[0];
-            }
+          if constexpr (H == 4) {
+            *reinterpret_cast<float4 *>(dst + zofs) = make_float4(z[0], z[1], z[2], z[3]);
+          } else if constexpr (H == 2) {
+            *reinterpret_cast<float2 *>(dst + zofs) = make_float2(z[0], z[1]);
           } else {
-            if (r4 < 2) dst[((r4 & 1) ? 0 : D) + c16] = z[0];
+            if (zwrite) dst[zofs] = z[0];
           }
-          if (c16 == 0 && r4 < 2) dst[2 * D + ((r4 & 1) ? 0 : 1)] = y;
+          if (ywrite) dst[yofs] = y;
         }
       }
       __syncthreads();
-      // across the 4 waves (rows r0+4w .. r0+4w+3), pairwise with pass-through
+      // across the waves (wave w holds rows r0 + 4w .. r0 + 4w + 3), pairwise, pass-through
       for (int e = tid; e < nt * PW; e += kThreads) {
         const int j = e / PW, f = e % PW;
-        float w0 = swave[j][0][f], w1 = swave[j][1][f], w2 = swave[j][2][f], w3 = swave[j][3][f];
-        if (r0 + RPW < dv) w0 = w0 + w1;
-        if (r0 + 3 * RPW < dv) w2 = w2 + w3;
-        if (r0 + 2 * RPW < dv) w0 = w0 + w2;
+        float w[WAVES];
+#pragma unroll
+        for (int x = 0; x < WAVES; ++x) w[x] = swave[j][x][f];
+#pragma unroll
+        for (int st = 1; st < WAVES; st *= 2)
+#pragma unroll
+          for (int x = 0; x + st < WAVES; x += 2 * st)
+            if (r0 + (x + st) * RPW < dv) w[x] = w[x] + w[x + st];
         const int64_t t = bos + c0 + sbi * SB + j;
-        p.partials[((t * Hv + h) * RB + rblock) * PW + f] = w0;
+        p.partials[((t * Hv + h) * RB + rblock) * PW + f] = w[0];
       }
       if (sbi > 0) deposit(buf ^ 1);  // its last reader finished before the barrier above
       __syncthreads();
@@ -580,10 +589,11 @@ __global__ __launch_bounds__(kThreads) void cpr_bwd_combine_kernel(const BwdArgs
 // ---------------------------------------------------------------------------- launchers
 
 template <typename Args>
-hipError_t launch1(const void *fn, int64_t grid, Args args, hipStream_t stream) {
+hipError_t launch1(const void *fn, int64_t grid, Args args, hipStream_t stream,
+                   int threads = kThreads) {
   if (grid <= 0) return hipSuccess;
   void *kargs[] = {&args};
-  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(threads), kargs, 0, stream);
 }
 
 template <int D>
@@ -637,6 +647,7 @@ int64_t backward_chunk_grid(const BwdArgs &a) {
 }
 
 hipError_t launch_backward(const BwdArgs &a, int L, hipStream_t st) {
+  if (a.row_blocks < 1 || a.row_blocks > 32) return hipErrorInvalidValue;  // d_v in [1, 1024]
   hipError_t e = launch1((const void *)cpr_bwd_plan_kernel, 1, a, st);
   if (e != hipSuccess) return e;
   const void *sf, *cf;
@@ -648,7 +659,7 @@ hipError_t launch_backward(const BwdArgs &a, int L, hipStream_t st) {
     default: return hipErrorInvalidValue;
   }
   if ((e = launch1(sf, backward_state_grid(a, L), a, st)) != hipSuccess) return e;
-  if ((e = launch1(cf, backward_chunk_grid(a), a, st)) != hipSuccess) return e;
+  if ((e = launch1(cf, backward_chunk_grid(a), a, st, kChunkThreads)) != hipSuccess) return e;
   const int64_t items = a.total_tokens * (a.num_qk_heads * (int64_t)a.d_k + a.num_v_heads);
   const int64_t grid = std::min<int64_t>((items + kThreads - 1) / kThreads, 65536);
   const void *comb;
@@ -657,8 +668,7 @@ hipError_t launch_backward(const BwdArgs &a, int L, hipStream_t st) {
   else if (a.row_blocks <= 4) comb = (const void *)cpr_bwd_combine_kernel<4>;
   else if (a.row_blocks <= 8) comb = (const void *)cpr_bwd_combine_kernel<8>;
   else if (a.row_blocks <= 16) comb = (const void *)cpr_bwd_combine_kernel<16>;
-  else if (a.row_blocks <= 32) comb = (const void *)cpr_bwd_combine_kernel<32>;
-  else comb = (const void *)cpr_bwd_combine_kernel<64>;
+  else comb = (const void *)cpr_bwd_combine_kernel<32>;  // d_v <= 1024: at most 32 blocks
   return launch1(comb, grid, a, st);
 }
 

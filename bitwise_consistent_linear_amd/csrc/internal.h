@@ -52,7 +52,7 @@ struct BwdArgs {
   int32_t num_seqs, num_qk_heads, num_v_heads, d_k, d_v, chunk;
   int32_t bf16;
   int32_t slots_max;   // chunk slots the plan may fill: total_chunks + num_seqs
-  int32_t row_blocks;  // blocks of 16 rows per value head in the chunk kernel
+  int32_t row_blocks;  // blocks of 32 rows per value head in the chunk kernel
   int64_t total_tokens;
   int64_t total_chunks;
   const int32_t *cu_seqlens;

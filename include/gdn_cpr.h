@@ -52,9 +52,10 @@
  *
  * TUNING. How many lanes of a wavefront share one state row is chosen per call from the
  * number of rows: 16 when that gives at most one wavefront per SIMD, 8 when 8 lanes do, 4
- * otherwise (decode: 16). The environment variable GDN_CPR_LANES_PER_ROW (16, 8 or 4)
- * overrides the choice; the contract makes every admitted value give the same bits, which
- * the tests check.
+ * otherwise (decode: 16; the backward's reverse pass over dL/dS: the widest that keeps at
+ * most two wavefronts per SIMD). The environment variable GDN_CPR_LANES_PER_ROW (16, 8 or
+ * 4) overrides the choice; the contract makes every admitted value give the same bits,
+ * which the tests check.
  */
 #ifndef GDN_CPR_H
 #define GDN_CPR_H

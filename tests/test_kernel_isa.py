@@ -31,7 +31,7 @@ def test_all_kernels_present(asm):
     assert sum("cpr_bwd_plan_kernel" in n for n in names) == 1
     assert sum("cpr_bwd_state_kernel" in n for n in names) == 4 * 3 * 2
     assert sum("cpr_bwd_chunk_kernel" in n for n in names) == 4 * 2
-    assert sum("cpr_bwd_combine_kernel" in n for n in names) == 7
+    assert sum("cpr_bwd_combine_kernel" in n for n in names) == 6
 
 
 def test_denormals_kept(asm):
