@@ -74,6 +74,18 @@ int bwd_state_lanes(const ScanArgs &a) {
   return 4;
 }
 
+// The backward sweeps each sequence's chunks in one workgroup per (sequence, value head,
+// row block) when those workgroups alone occupy every compute unit (one chunk-pass
+// workgroup fits per CU); otherwise it runs chunks in parallel after a state pass.
+// GDN_CPR_BWD_SCHEDULE=sequences|chunks overrides; both give the same bits.
+bool bwd_sequences(const gdn_shape_t *sh) {
+  const char *env = std::getenv("GDN_CPR_BWD_SCHEDULE");
+  if (env && std::strcmp(env, "sequences") == 0) return true;
+  if (env && std::strcmp(env, "chunks") == 0) return false;
+  const int64_t items = (int64_t)sh->num_seqs * sh->num_v_heads * backward_row_blocks(sh->d_v);
+  return items >= device_simds() / 4;
+}
+
 // Decode streams every row once per step; 16 lanes per row keeps each lane's slice of the
 // 512-byte row at 32 bytes and gives the most loads in flight.
 int decode_lanes() {
@@ -375,10 +387,11 @@ GDN_EXPORT gdn_status_t gdn_cpr_trainer_bwd(
   args.partials = reinterpret_cast<float *>(w + ws.partials_off);
   if (shape->num_seqs == 0) return gdn::ok();
   const int L = gdn::bwd_state_lanes(fwd);
+  const bool seq = gdn::bwd_sequences(shape);
   if (gdn::backward_state_grid(args, L) > gdn::kMaxInt32 ||
-      gdn::backward_chunk_grid(args) > gdn::kMaxInt32)
+      gdn::backward_chunk_grid(args, seq) > gdn::kMaxInt32)
     return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": grid too large");
-  const hipError_t e = gdn::launch_backward(args, L, static_cast<hipStream_t>(stream));
+  const hipError_t e = gdn::launch_backward(args, L, seq, static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return gdn::fail(GDN_E_DEVICE, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
   return gdn::ok();

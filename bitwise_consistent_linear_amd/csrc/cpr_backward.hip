@@ -308,9 +308,15 @@ __device__ __forceinline__ void rows4_sum(const float (&pq)[M], const float (&pk
   y = (FULL || c2) ? a + b : a;
 }
 
+// The chunk pass, in one of two schedules with the same arithmetic (so the same bits):
+//   SEQ = false: one workgroup per (chunk slot, value head, row block); dL/ds at the chunk's
+//                end comes from the state pass (or dL/dS_final for a sequence's last chunk);
+//   SEQ = true:  one workgroup per (sequence, value head, row block), sweeping the
+//                sequence's chunks from last to first and carrying dL/ds in registers; it
+//                writes dv and dS0 itself, so the state pass does not run.
 // Checkpoints and a sub-block of recomputed states live in registers: allow up to 256
 // VGPRs (two waves per SIMD) rather than spill.
-template <int D, bool BF16>
+template <int D, bool BF16, bool SEQ>
 __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void cpr_bwd_chunk_kernel(const BwdArgs p) {
   constexpr int kThreads = kChunkThreads;
@@ -329,212 +335,259 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
   __shared__ float sv[2][V_ITEMS], sg[2][V_ITEMS], sa[2][SB], sb[2][SB];
   __shared__ __align__(16) float swave[SB][WAVES][PWP];  // wave sums of a sub-block's tokens
   __shared__ float sdif[kMaxSub * SB][ROWS];             // v_i - u of every token of the chunk
+  __shared__ float sdv[SEQ ? SB : 1][ROWS];               // dv of a sub-block (SEQ only)
+  __shared__ int s_len[SEQ ? kMaxRankedSeqs : 1];
+  __shared__ int s_pick;
 
-  const int tid = threadIdx.x, row = tid / L, lane = tid % L;
-  const int wave = tid / 64, wl = tid % 64, r4 = wl / L, c16 = wl % L;
   const int Hv = p.num_v_heads, Hk = p.num_qk_heads, dv = p.d_v, RB = p.row_blocks;
-  int pair, rblock;
-  block_work(blockIdx.x, p.slots_max * Hv, RB, pair, rblock);
-  const int slot = pair / Hv, h = pair % Hv;
-  if (slot >= p.plan[0]) return;  // uniform: this workgroup has no chunk
-  const int n = p.plan[kPlanHeader + 2 * slot], c = p.plan[kPlanHeader + 2 * slot + 1];
+  int pair, rblock, n, h, c_hi, c_lo;
   int64_t bos, eos;
-  seq_range(p.cu_seqlens, n, p.total_tokens, bos, eos);
-  const int64_t Tn = eos - bos, c0 = (int64_t)c * p.chunk;
-  if (c0 >= Tn) return;  // uniform
-  const int len = (int)(Tn - c0 < p.chunk ? Tn - c0 : p.chunk);
+  if constexpr (SEQ) {
+    block_work(blockIdx.x, p.num_seqs * Hv, RB, pair, rblock);
+    h = pair % Hv;
+    n = ranked_sequence(p.cu_seqlens, p.num_seqs, p.total_tokens, pair / Hv, s_len, &s_pick);
+    seq_range(p.cu_seqlens, n, p.total_tokens, bos, eos);
+    c_hi = (int)((eos - bos + p.chunk - 1) / p.chunk) - 1;
+    c_lo = 0;
+  } else {
+    block_work(blockIdx.x, p.slots_max * Hv, RB, pair, rblock);
+    const int slot = pair / Hv;
+    h = pair % Hv;
+    if (slot >= p.plan[0]) return;  // uniform: this workgroup has no chunk
+    n = p.plan[kPlanHeader + 2 * slot];
+    c_hi = c_lo = p.plan[kPlanHeader + 2 * slot + 1];
+    seq_range(p.cu_seqlens, n, p.total_tokens, bos, eos);
+    if ((int64_t)c_hi * p.chunk >= eos - bos) return;  // uniform
+  }
+  const int64_t Tn = eos - bos;
   const int64_t cbase = p.plan_cbase[n];
   const int hk = h / (Hv / Hk);
-  const int r0 = rblock * ROWS, i = r0 + row;
-  const bool valid = i < dv;
+  const int r0 = rblock * ROWS;
   const int64_t vstride = (int64_t)Hv * dv;
-  const int64_t row_off = (((int64_t)n * Hv + h) * dv + i) * D + lane * M;
-  const int wrow0 = r0 + wave * RPW;  // first row of this wave
-  const bool full4 = wrow0 + RPW - 1 < dv;
-  const bool c1 = r4 < 2 ? wrow0 + 1 < dv : wrow0 + 3 < dv, c2 = wrow0 + 2 < dv;
-  // where this lane stores its row sums in swave[j][wave][.] (see rows4_sum); computed once
-  int zofs = (M >= 2) ? ((r4 & 1) ? 0 : D) + c16 * M + (r4 < 2 ? H : 0) : ((r4 & 1) ? 0 : D) + c16;
-  int yofs = 2 * D + ((r4 & 1) ? 0 : 1);
-  asm volatile("" : "+v"(zofs), "+v"(yofs));  // keep them in registers, not recomputed per token
-  const bool zwrite = M >= 2 || r4 < 2, ywrite = c16 == 0 && r4 < 2;
+  auto row_offset = [&](int i, int lane) { return (((int64_t)n * Hv + h) * dv + i) * D + lane * M; };
 
-  // state at the chunk's start, dL/ds at its end
-  float s[M], sh[M];
+  // dL/ds after the last chunk processed here, carried from chunk to chunk
+  float sh[M];
 #pragma unroll
-  for (int e = 0; e < M; ++e) {
-    s[e] = 0.0f;
-    sh[e] = 0.0f;
-  }
-  if (valid) {
-    if (c == 0) {
-      if (p.initial_state) load_row<M>(p.initial_state + row_off, s);
-    } else if (cbase + c - 1 < p.total_chunks) {
-      load_row<M>(p.chunk_states + (((cbase + c - 1) * Hv + h) * dv + i) * D + lane * M, s);
-    }
-    if (c0 + p.chunk <= Tn) {
-      if (cbase + c < p.total_chunks)
-        load_row<M>(p.dsh_bnd + (((cbase + c) * Hv + h) * dv + i) * D + lane * M, sh);
-    } else if (p.d_final_state) {
-      load_row<M>(p.d_final_state + row_off, sh);
+  for (int e = 0; e < M; ++e) sh[e] = 0.0f;
+  {
+    const int lane = threadIdx.x % L, i = r0 + (int)threadIdx.x / L;
+    if (i < dv) {
+      if (!SEQ && ((int64_t)c_hi + 1) * p.chunk <= Tn) {
+        if (cbase + c_hi < p.total_chunks)
+          load_row<M>(p.dsh_bnd + (((cbase + c_hi) * Hv + h) * dv + i) * D + lane * M, sh);
+      } else if (p.d_final_state) {
+        load_row<M>(p.d_final_state + row_offset(i, lane), sh);
+      }
     }
   }
 
-  // Tokens [c0 + j0, c0 + j0 + nt) of the chunk: global memory -> registers (fetch), then
-  // registers -> LDS buffer (deposit), so the loads of the next sub-block overlap the
-  // arithmetic of this one. Items past nt repeat the last token and are never read.
   raw_t rk[KQ_PER], rq[KQ_PER];
   uint32_t rv = 0;
   float rg = 0.0f, ra = 0.0f, rb = 0.0f;
-  auto fetch = [&](int j0, int nt) {
+  for (int c = c_hi; c >= c_lo; --c) {
+    // Thread-derived values come from an opaque copy of the thread index, once per chunk,
+    // so that the addresses of the unrolled body are not held live across chunks.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int row = tid / L, lane = tid % L;
+    const int wave = tid / 64, wl = tid % 64, r4 = wl / L, c16 = wl % L;
+    const int i = r0 + row;
+    const bool valid = i < dv;
+    const int wrow0 = r0 + wave * RPW;  // first row of this wave
+    const bool full4 = wrow0 + RPW - 1 < dv;
+    const bool c1 = r4 < 2 ? wrow0 + 1 < dv : wrow0 + 3 < dv, c2 = wrow0 + 2 < dv;
+    // where this lane stores its row sums in swave[j][wave][.] (see rows4_sum)
+    int zofs = (M >= 2) ? ((r4 & 1) ? 0 : D) + c16 * M + (r4 < 2 ? H : 0)
+                        : ((r4 & 1) ? 0 : D) + c16;
+    int yofs = 2 * D + ((r4 & 1) ? 0 : 1);
+    asm volatile("" : "+v"(zofs), "+v"(yofs));  // kept in registers, not recomputed per token
+    const bool zwrite = M >= 2 || r4 < 2, ywrite = c16 == 0 && r4 < 2;
+
+    // the state at the chunk's start: the initial state or the trainer's chunk state
+    float s[M];
 #pragma unroll
-    for (int jj = 0; jj < KQ_PER; ++jj) {
-      const int g = (tid + jj * kThreads) % KQ_ITEMS;
-      const int tt = g / GROUPS < nt ? g / GROUPS : nt - 1;
-      const int64_t src = ((bos + c0 + j0 + tt) * Hk + hk) * D + 4 * (g % GROUPS);
-      rk[jj] = load_raw4<BF16>(p.k, src);
-      rq[jj] = load_raw4<BF16>(p.q, src);
-    }
-    {
-      const int e = tid % V_ITEMS;
-      const int tt = e / ROWS < nt ? e / ROWS : nt - 1;
-      const int r = r0 + e % ROWS < dv ? r0 + e % ROWS : dv - 1;
-      const int64_t at = (bos + c0 + j0 + tt) * vstride + (int64_t)h * dv + r;
-      rv = load_raw1<BF16>(p.v, at);
-      rg = p.d_o[at];
-    }
-    const int tt = tid % SB < nt ? tid % SB : nt - 1;
-    ra = p.a[(bos + c0 + j0 + tt) * Hv + h];
-    rb = p.b[(bos + c0 + j0 + tt) * Hv + h];
-  };
-  auto deposit = [&](int buf) {
-#pragma unroll
-    for (int jj = 0; jj < KQ_PER; ++jj) {
-      const int g = tid + jj * kThreads;
-      if (KQ_ITEMS % kThreads == 0 || g < KQ_ITEMS) {
-        const int off = (g / GROUPS) * D + stage_slot<D, L>(g % GROUPS);
-        *reinterpret_cast<float4 *>(&sk[buf][off]) = widen4<BF16>(rk[jj]);
-        *reinterpret_cast<float4 *>(&sq[buf][off]) = widen4<BF16>(rq[jj]);
+    for (int e = 0; e < M; ++e) s[e] = 0.0f;
+    if (valid) {
+      if (c == 0) {
+        if (p.initial_state) load_row<M>(p.initial_state + row_offset(i, lane), s);
+      } else if (cbase + c - 1 < p.total_chunks) {
+        load_row<M>(p.chunk_states + (((cbase + c - 1) * Hv + h) * dv + i) * D + lane * M, s);
       }
     }
-    if (tid < V_ITEMS) {
-      const bool ok = r0 + tid % ROWS < dv;
-      sv[buf][tid] = ok ? widen1<BF16>(rv) : 0.0f;
-      sg[buf][tid] = ok ? rg : 0.0f;
-    }
-    if (tid < SB) {
-      sa[buf][tid] = ra;
-      sb[buf][tid] = rb;
-    }
-  };
 
-  const int nsb = (len + SB - 1) / SB;
-  auto sub_len = [&](int sbi) { return len - sbi * SB < SB ? len - sbi * SB : SB; };
-  fetch(0, sub_len(0));
-  deposit(0);
-  __syncthreads();
-
-  // forward over the chunk, keeping the state at the start of every sub-block
-  float ck[kMaxSub][M];
-  static_for<kMaxSub>([&](auto sbi_c) {
-    constexpr int sbi = decltype(sbi_c)::value, buf = sbi & 1;
-    if (sbi < nsb) {
-      const bool next = sbi + 1 < nsb;
-      if (next) fetch((sbi + 1) * SB, sub_len(sbi + 1));
+    // Tokens [c0 + j0, c0 + j0 + nt) of the chunk: global memory -> registers (fetch), then
+    // registers -> LDS buffer (deposit), so the loads of the next sub-block overlap the
+    // arithmetic of this one. Items past nt repeat the last token and are never read.
+    auto fetch = [&](int64_t c0, int j0, int nt) {
 #pragma unroll
-      for (int e = 0; e < M; ++e) ck[sbi][e] = s[e];
-      const int nt = sub_len(sbi);
-      for (int j = 0; j < nt; ++j) {
-        float kr[M], x[M];
-        lds_slice<D, L>(&sk[buf][j * D], lane, kr);
-        row_decay<D, L>(s, sa[buf][j], x);
-        const float u = contract_dot<D, L>(x, kr);
-        const float dif = sv[buf][j * ROWS + row] - u;  // d = b (v_i - u), as row_delta
-        if (lane == 0) sdif[sbi * SB + j][row] = dif;
-        row_update<D, L>(s, sb[buf][j] * dif, kr, x);
+      for (int jj = 0; jj < KQ_PER; ++jj) {
+        const int g = (tid + jj * kThreads) % KQ_ITEMS;
+        const int tt = g / GROUPS < nt ? g / GROUPS : nt - 1;
+        const int64_t src = ((bos + c0 + j0 + tt) * Hk + hk) * D + 4 * (g % GROUPS);
+        rk[jj] = load_raw4<BF16>(p.k, src);
+        rq[jj] = load_raw4<BF16>(p.q, src);
       }
-      if (next) deposit(buf ^ 1);  // its last reader finished before the previous barrier
-      __syncthreads();
-    }
-  });
+      {
+        const int e = tid % V_ITEMS;
+        const int tt = e / ROWS < nt ? e / ROWS : nt - 1;
+        const int r = r0 + e % ROWS < dv ? r0 + e % ROWS : dv - 1;
+        const int64_t at = (bos + c0 + j0 + tt) * vstride + (int64_t)h * dv + r;
+        rv = load_raw1<BF16>(p.v, at);
+        rg = p.d_o[at];
+      }
+      const int tt = tid % SB < nt ? tid % SB : nt - 1;
+      ra = p.a[(bos + c0 + j0 + tt) * Hv + h];
+      rb = p.b[(bos + c0 + j0 + tt) * Hv + h];
+    };
+    auto deposit = [&](int buf) {
+#pragma unroll
+      for (int jj = 0; jj < KQ_PER; ++jj) {
+        const int g = tid + jj * kThreads;
+        if (KQ_ITEMS % kThreads == 0 || g < KQ_ITEMS) {
+          const int off = (g / GROUPS) * D + stage_slot<D, L>(g % GROUPS);
+          *reinterpret_cast<float4 *>(&sk[buf][off]) = widen4<BF16>(rk[jj]);
+          *reinterpret_cast<float4 *>(&sq[buf][off]) = widen4<BF16>(rq[jj]);
+        }
+      }
+      if (tid < V_ITEMS) {
+        const bool ok = r0 + tid % ROWS < dv;
+        sv[buf][tid] = ok ? widen1<BF16>(rv) : 0.0f;
+        sg[buf][tid] = ok ? rg : 0.0f;
+      }
+      if (tid < SB) {
+        sa[buf][tid] = ra;
+        sb[buf][tid] = rb;
+      }
+    };
 
-  // sub-blocks in reverse: recompute the states, run sh back, sum the shares over rows
-  static_for<kMaxSub, true>([&](auto sbi_c) {
-    constexpr int sbi = decltype(sbi_c)::value, buf = sbi & 1;
-    if (sbi < nsb) {
-      const int nt = sub_len(sbi);
-      if (sbi > 0) fetch((sbi - 1) * SB, SB);
-      float st[SB + 1][M], dif[SB], del[SB];
+    const int64_t c0 = (int64_t)c * p.chunk;
+    const int len = (int)(Tn - c0 < p.chunk ? Tn - c0 : p.chunk);
+    const int nsb = (len + SB - 1) / SB;
+    auto sub_len = [&](int sbi) { return len - sbi * SB < SB ? len - sbi * SB : SB; };
+    fetch(c0, 0, sub_len(0));
+    deposit(0);  // buffer 0's last reader (the previous chunk) finished before its barrier
+    __syncthreads();
+
+    // forward over the chunk, keeping the state at the start of every sub-block
+    float ck[kMaxSub][M];
+    static_for<kMaxSub>([&](auto sbi_c) {
+      constexpr int sbi = decltype(sbi_c)::value, buf = sbi & 1;
+      if (sbi < nsb) {
+        const bool next = sbi + 1 < nsb;
+        if (next) fetch(c0, (sbi + 1) * SB, sub_len(sbi + 1));
 #pragma unroll
-      for (int e = 0; e < M; ++e) st[0][e] = ck[sbi][e];
-#pragma unroll
-      for (int j = 0; j < SB; ++j) {
-        if (j < nt) {  // the forward sweep left v_i - u of each token: no dot product here
+        for (int e = 0; e < M; ++e) ck[sbi][e] = s[e];
+        const int nt = sub_len(sbi);
+        for (int j = 0; j < nt; ++j) {
           float kr[M], x[M];
           lds_slice<D, L>(&sk[buf][j * D], lane, kr);
-          row_decay<D, L>(st[j], sa[buf][j], x);
-          dif[j] = sdif[sbi * SB + j][row];
-          del[j] = sb[buf][j] * dif[j];
-#pragma unroll
-          for (int e = 0; e < M; ++e) st[j + 1][e] = st[j][e];
-          row_update<D, L>(st[j + 1], del[j], kr, x);
+          row_decay<D, L>(s, sa[buf][j], x);
+          const float u = contract_dot<D, L>(x, kr);
+          const float dif = sv[buf][j * ROWS + row] - u;  // d = b (v_i - u), as row_delta
+          if (lane == 0) sdif[sbi * SB + j][row] = dif;
+          row_update<D, L>(s, sb[buf][j] * dif, kr, x);
         }
+        if (next) deposit(buf ^ 1);  // its last reader finished before the previous barrier
+        __syncthreads();
       }
+    });
+
+    // sub-blocks in reverse: recompute the states, run sh back, sum the shares over rows
+    static_for<kMaxSub, true>([&](auto sbi_c) {
+      constexpr int sbi = decltype(sbi_c)::value, buf = sbi & 1;
+      if (sbi < nsb) {
+        const int nt = sub_len(sbi);
+        if (sbi > 0) fetch(c0, (sbi - 1) * SB, SB);
+        float st[SB + 1][M], dif[SB], del[SB];
 #pragma unroll
-      for (int j = SB - 1; j >= 0; --j) {
-        if (j < nt) {
-          float kr[M], qr[M], x[M], xh[M], pq[M], pk[M], dh;
-          lds_slice<D, L>(&sk[buf][j * D], lane, kr);
-          lds_slice<D, L>(&sq[buf][j * D], lane, qr);
-          const float g = sg[buf][j * ROWS + row], a = sa[buf][j], b = sb[buf][j];
-          row_bwd_absorb<D, L>(sh, g, qr);
+        for (int e = 0; e < M; ++e) st[0][e] = ck[sbi][e];
 #pragma unroll
-          for (int e = 0; e < M; ++e) pq[e] = g * st[j + 1][e];
-          const float dv_i = row_bwd_delta<D, L>(sh, kr, b, xh, dh);
-          const float pb = dh * dif[j];
-          const float uh = -dv_i;
-          row_decay<D, L>(st[j], a, x);
+        for (int j = 0; j < SB; ++j) {
+          if (j < nt) {  // the forward sweep left v_i - u of each token: no dot product here
+            float kr[M], x[M];
+            lds_slice<D, L>(&sk[buf][j * D], lane, kr);
+            row_decay<D, L>(st[j], sa[buf][j], x);
+            dif[j] = sdif[sbi * SB + j][row];
+            del[j] = sb[buf][j] * dif[j];
 #pragma unroll
-          for (int e = 0; e < M; ++e) {
-            const float ds = del[j] * sh[e];
-            pk[e] = __builtin_fmaf(uh, x[e], ds);
+            for (int e = 0; e < M; ++e) st[j + 1][e] = st[j][e];
+            row_update<D, L>(st[j + 1], del[j], kr, x);
           }
-          const float pa = contract_dot<D, L>(xh, st[j]);
-          row_bwd_decay<D, L>(sh, a, xh);
-          float z[H], y;
-          if (full4)
-            rows4_sum<M, true>(pq, pk, pa, pb, c1, c2, z, y);
-          else
-            rows4_sum<M, false>(pq, pk, pa, pb, c1, c2, z, y);
-          float *dst = &swave[j][wave][0];
-          if constexpr (H == 4) {
-            *reinterpret_cast<float4 *>(dst + zofs) = make_float4(z[0], z[1], z[2], z[3]);
-          } else if constexpr (H == 2) {
-            *reinterpret_cast<float2 *>(dst + zofs) = make_float2(z[0], z[1]);
-          } else {
-            if (zwrite) dst[zofs] = z[0];
-          }
-          if (ywrite) dst[yofs] = y;
         }
+#pragma unroll
+        for (int j = SB - 1; j >= 0; --j) {
+          if (j < nt) {
+            float kr[M], qr[M], x[M], xh[M], pq[M], pk[M], dh;
+            lds_slice<D, L>(&sk[buf][j * D], lane, kr);
+            lds_slice<D, L>(&sq[buf][j * D], lane, qr);
+            const float g = sg[buf][j * ROWS + row], a = sa[buf][j], b = sb[buf][j];
+            row_bwd_absorb<D, L>(sh, g, qr);
+#pragma unroll
+            for (int e = 0; e < M; ++e) pq[e] = g * st[j + 1][e];
+            const float dv_i = row_bwd_delta<D, L>(sh, kr, b, xh, dh);
+            if constexpr (SEQ) {
+              if (lane == 0) sdv[j][row] = dv_i;
+            }
+            const float pb = dh * dif[j];
+            const float uh = -dv_i;
+            row_decay<D, L>(st[j], a, x);
+#pragma unroll
+            for (int e = 0; e < M; ++e) {
+              const float ds = del[j] * sh[e];
+              pk[e] = __builtin_fmaf(uh, x[e], ds);
+            }
+            const float pa = contract_dot<D, L>(xh, st[j]);
+            row_bwd_decay<D, L>(sh, a, xh);
+            float z[H], y;
+            if (full4)
+              rows4_sum<M, true>(pq, pk, pa, pb, c1, c2, z, y);
+            else
+              rows4_sum<M, false>(pq, pk, pa, pb, c1, c2, z, y);
+            float *dst = &swave[j][wave][0];
+            if constexpr (H == 4) {
+              *reinterpret_cast<float4 *>(dst + zofs) = make_float4(z[0], z[1], z[2], z[3]);
+            } else if constexpr (H == 2) {
+              *reinterpret_cast<float2 *>(dst + zofs) = make_float2(z[0], z[1]);
+            } else {
+              if (zwrite) dst[zofs] = z[0];
+            }
+            if (ywrite) dst[yofs] = y;
+          }
+        }
+        __syncthreads();
+        // across the waves (wave w holds rows r0 + 4w .. r0 + 4w + 3), pairwise, pass-through
+        for (int e = tid; e < nt * PW; e += kThreads) {
+          const int j = e / PW, f = e % PW;
+          float w[WAVES];
+#pragma unroll
+          for (int x = 0; x < WAVES; ++x) w[x] = swave[j][x][f];
+#pragma unroll
+          for (int st = 1; st < WAVES; st *= 2)
+#pragma unroll
+            for (int x = 0; x + st < WAVES; x += 2 * st)
+              if (r0 + (x + st) * RPW < dv) w[x] = w[x] + w[x + st];
+          const int64_t t = bos + c0 + sbi * SB + j;
+          p.partials[((t * Hv + h) * RB + rblock) * PW + f] = w[0];
+        }
+        if constexpr (SEQ) {
+          for (int e = tid; e < nt * ROWS; e += kThreads) {
+            const int j = e / ROWS, r = e % ROWS;
+            if (r0 + r < dv)
+              p.dv[(bos + c0 + sbi * SB + j) * vstride + (int64_t)h * dv + r0 + r] = sdv[j][r];
+          }
+        }
+        if (sbi > 0) deposit(buf ^ 1);  // its last reader finished before the barrier above
+        __syncthreads();
       }
-      __syncthreads();
-      // across the waves (wave w holds rows r0 + 4w .. r0 + 4w + 3), pairwise, pass-through
-      for (int e = tid; e < nt * PW; e += kThreads) {
-        const int j = e / PW, f = e % PW;
-        float w[WAVES];
-#pragma unroll
-        for (int x = 0; x < WAVES; ++x) w[x] = swave[j][x][f];
-#pragma unroll
-        for (int st = 1; st < WAVES; st *= 2)
-#pragma unroll
-          for (int x = 0; x + st < WAVES; x += 2 * st)
-            if (r0 + (x + st) * RPW < dv) w[x] = w[x] + w[x + st];
-        const int64_t t = bos + c0 + sbi * SB + j;
-        p.partials[((t * Hv + h) * RB + rblock) * PW + f] = w[0];
-      }
-      if (sbi > 0) deposit(buf ^ 1);  // its last reader finished before the barrier above
-      __syncthreads();
-    }
-  });
+    });
+  }
+  if constexpr (SEQ) {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));  // recomputed here rather than held across the chunk loop
+    const int lane = t % L, i = r0 + t / L;
+    if (i < dv) store_row<M>(p.d_initial_state + row_offset(i, lane), sh);
+  }
 }
 
 // -------------------------------------------------------------------------- combine pass
@@ -609,9 +662,12 @@ const void *state_fn(int L, bool bf16) {
 }
 
 template <int D>
-const void *chunk_fn(bool bf16) {
-  return bf16 ? (const void *)cpr_bwd_chunk_kernel<D, true>
-              : (const void *)cpr_bwd_chunk_kernel<D, false>;
+const void *chunk_fn(bool bf16, bool seq) {
+  if (seq)
+    return bf16 ? (const void *)cpr_bwd_chunk_kernel<D, true, true>
+                : (const void *)cpr_bwd_chunk_kernel<D, false, true>;
+  return bf16 ? (const void *)cpr_bwd_chunk_kernel<D, true, false>
+              : (const void *)cpr_bwd_chunk_kernel<D, false, false>;
 }
 
 }  // namespace
@@ -642,24 +698,25 @@ int64_t backward_state_grid(const BwdArgs &a, int L) {
   return (int64_t)a.num_seqs * a.num_v_heads * ((a.d_v + rows - 1) / rows);
 }
 
-int64_t backward_chunk_grid(const BwdArgs &a) {
-  return (int64_t)a.slots_max * a.num_v_heads * a.row_blocks;
+int64_t backward_chunk_grid(const BwdArgs &a, bool seq) {
+  return (int64_t)(seq ? a.num_seqs : a.slots_max) * a.num_v_heads * a.row_blocks;
 }
 
-hipError_t launch_backward(const BwdArgs &a, int L, hipStream_t st) {
+hipError_t launch_backward(const BwdArgs &a, int L, bool seq, hipStream_t st) {
   if (a.row_blocks < 1 || a.row_blocks > 32) return hipErrorInvalidValue;  // d_v in [1, 1024]
   hipError_t e = launch1((const void *)cpr_bwd_plan_kernel, 1, a, st);
   if (e != hipSuccess) return e;
   const void *sf, *cf;
   switch (a.d_k) {
-    case 16: sf = state_fn<16>(L, a.bf16); cf = chunk_fn<16>(a.bf16); break;
-    case 32: sf = state_fn<32>(L, a.bf16); cf = chunk_fn<32>(a.bf16); break;
-    case 64: sf = state_fn<64>(L, a.bf16); cf = chunk_fn<64>(a.bf16); break;
-    case 128: sf = state_fn<128>(L, a.bf16); cf = chunk_fn<128>(a.bf16); break;
+    case 16: sf = state_fn<16>(L, a.bf16); cf = chunk_fn<16>(a.bf16, seq); break;
+    case 32: sf = state_fn<32>(L, a.bf16); cf = chunk_fn<32>(a.bf16, seq); break;
+    case 64: sf = state_fn<64>(L, a.bf16); cf = chunk_fn<64>(a.bf16, seq); break;
+    case 128: sf = state_fn<128>(L, a.bf16); cf = chunk_fn<128>(a.bf16, seq); break;
     default: return hipErrorInvalidValue;
   }
-  if ((e = launch1(sf, backward_state_grid(a, L), a, st)) != hipSuccess) return e;
-  if ((e = launch1(cf, backward_chunk_grid(a), a, st, kChunkThreads)) != hipSuccess) return e;
+  if (!seq && (e = launch1(sf, backward_state_grid(a, L), a, st)) != hipSuccess) return e;
+  if ((e = launch1(cf, backward_chunk_grid(a, seq), a, st, kChunkThreads)) != hipSuccess)
+    return e;
   const int64_t items = a.total_tokens * (a.num_qk_heads * (int64_t)a.d_k + a.num_v_heads);
   const int64_t grid = std::min<int64_t>((items + kThreads - 1) / kThreads, 65536);
   const void *comb;

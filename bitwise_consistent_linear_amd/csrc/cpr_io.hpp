@@ -139,7 +139,7 @@ __device__ inline int ranked_sequence(const int32_t *cu, int N, int64_t T, int r
     if (r == rank) *s_pick = j;
   }
   __syncthreads();
-  return *s_pick;
+  return __builtin_amdgcn_readfirstlane(*s_pick);  // the same in every lane: keep it scalar
 }
 
 // Workgroup -> (head pair, row block), XCD-aware. The dispatcher hands workgroups to the

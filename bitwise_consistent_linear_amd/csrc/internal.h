@@ -76,8 +76,10 @@ int backward_row_blocks(int d_v);
 BwdWorkspace backward_workspace(int64_t num_seqs, int64_t num_v_heads, int64_t d_k,
                                 int64_t d_v, int64_t total_tokens, int64_t total_chunks);
 int64_t backward_state_grid(const BwdArgs &args, int lanes_per_row);
-int64_t backward_chunk_grid(const BwdArgs &args);
-hipError_t launch_backward(const BwdArgs &args, int lanes_per_row, hipStream_t stream);
+// seq: one chunk-pass workgroup per (sequence, value head, row block), sweeping the
+// sequence's chunks in reverse (no state pass); else one per (chunk, value head, row block).
+int64_t backward_chunk_grid(const BwdArgs &args, bool seq);
+hipError_t launch_backward(const BwdArgs &args, int lanes_per_row, bool seq, hipStream_t stream);
 
 // Enqueue the kernels. lanes_per_row is 16, 8 or 4. Return the HIP launch status.
 hipError_t launch_scan(const ScanArgs &args, int lanes_per_row, hipStream_t stream);

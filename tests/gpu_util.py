@@ -73,6 +73,28 @@ class lanes:
             os.environ["GDN_CPR_LANES_PER_ROW"] = self.old
 
 
+class schedule:
+    """Context manager: run the backward's chunk pass with a given schedule, "chunks" (one
+    workgroup per chunk, after the state pass) or "sequences" (one per sequence, sweeping
+    its chunks in reverse)."""
+
+    def __init__(self, name):
+        self.name = name
+
+    def __enter__(self):
+        self.old = os.environ.get("GDN_CPR_BWD_SCHEDULE")
+        os.environ["GDN_CPR_BWD_SCHEDULE"] = self.name
+
+    def __exit__(self, *exc):
+        if self.old is None:
+            os.environ.pop("GDN_CPR_BWD_SCHEDULE", None)
+        else:
+            os.environ["GDN_CPR_BWD_SCHEDULE"] = self.old
+
+
+SCHEDULES = ("chunks", "sequences")
+
+
 def decode_steps(dev_steps, state, chunk, s_range=None, resync=True):
     """Run decode steps; yields (step index, o, resync tensor or None)."""
     S = dev_steps["q"].shape[0]

@@ -4,7 +4,9 @@ bit for bit.
 Small cases cover ragged and empty sequences, lengths that are and are not multiples of C
 and of the 8-token recompute sub-block, GQA, every d_k, f32 and bf16 storage, ragged d_v
 (row blocks that end part-way, d_v below 16, up to 1024 rows), initial states, dL/dS_final
-present or absent, C = 16, 32 and 64, and every lanes-per-row value of the state pass. The
+present or absent, C = 16, 32 and 64, every lanes-per-row value of the state pass, and both
+schedules of the chunk pass (one workgroup per chunk after the state pass, or one per
+sequence sweeping its chunks in reverse). The
 trainer-size configuration (4 x 4096 tokens, 16 heads, d = 128, C = 64) is compared with
 the oracle over every output. The chunk states fed to the backward are the oracle's, so
 these tests do not lean on the forward kernels.
@@ -18,7 +20,8 @@ import torch
 
 from bitwise_consistent_linear_amd import api
 from bitwise_consistent_linear_amd import workloads as W
-from gpu_util import DEV, LANES, assert_bits, assert_dev_equal, lanes, log, up, up_workload
+from gpu_util import (DEV, LANES, SCHEDULES, assert_bits, assert_dev_equal, lanes, log, schedule,
+                      up, up_workload)
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -86,10 +89,14 @@ def test_bwd_small_cases_match_oracle(case):
     ddsf = None if dsf is None else up(dsf)
     ds0 = None if s0 is None else up(s0)
     for L in LANES:
-        with lanes(L):
+        with lanes(L), schedule("chunks"):
             got = run_bwd(w, d, dcs, ddo, ddsf, ds0)
             torch.cuda.synchronize()
-        assert_grads(got, ref, f"{case[0]} L={L}")
+        assert_grads(got, ref, f"{case[0]} L={L} chunks")
+    with schedule("sequences"):
+        got = run_bwd(w, d, dcs, ddo, ddsf, ds0)
+        torch.cuda.synchronize()
+    assert_grads(got, ref, f"{case[0]} sequences")
 
 
 def test_bwd_many_sequences_plan_carry_and_unranked_state_pass():
@@ -101,9 +108,11 @@ def test_bwd_many_sequences_plan_carry_and_unranked_state_pass():
     log(f"bwd many sequences: N=1100 T={w.total_tokens}")
     ref, cs = oracle_bwd(w, s0, do, dsf)
     d = up_workload(w)
-    got = run_bwd(w, d, up(cs), up(do), up(dsf), up(s0))
-    torch.cuda.synchronize()
-    assert_grads(got, ref, "many sequences")
+    for sched in SCHEDULES:
+        with schedule(sched):
+            got = run_bwd(w, d, up(cs), up(do), up(dsf), up(s0))
+            torch.cuda.synchronize()
+        assert_grads(got, ref, f"many sequences, {sched}")
 
 
 def test_bwd_workspace_contents_do_not_matter():
@@ -117,10 +126,11 @@ def test_bwd_workspace_contents_do_not_matter():
     sh = api.GdnShape(w.num_seqs, 1, 2, 64, 40, 32, api.GDN_DTYPE_BF16)
     need = api.trainer_bwd_workspace_bytes(sh, w.total_tokens, w.total_chunks)
     ws = torch.full((need + 4096,), 0xFF, dtype=torch.uint8, device=DEV)
-    for _ in range(2):
-        got = run_bwd(w, d, up(cs), up(do), up(dsf), up(s0), workspace=ws)
-        torch.cuda.synchronize()
-        assert_grads(got, ref, "reused workspace")
+    for sched in SCHEDULES + SCHEDULES:
+        with schedule(sched):
+            got = run_bwd(w, d, up(cs), up(do), up(dsf), up(s0), workspace=ws)
+            torch.cuda.synchronize()
+        assert_grads(got, ref, f"reused workspace, {sched}")
     w2, s02, do2, dsf2 = case_workload("ws_reuse_small", [17], 1, 2, 64, 40, 32, True, True, True)
     ref2, cs2 = oracle_bwd(w2, s02, do2, dsf2)
     got2 = run_bwd(w2, up_workload(w2), up(cs2), up(do2), up(dsf2), up(s02), workspace=ws)
@@ -156,6 +166,9 @@ def trainer_case():
 
 
 def test_bwd_config_trainer_matches_oracle(trainer_case):
+    """Automatic choices (the sequence schedule here: 4 x 16 x 4 row blocks fill the
+    CUs), then the chunk schedule at every lanes-per-row value, all against the oracle or
+    the first result."""
     w, do, dsf, ref = trainer_case
     d = up_workload(w)
     o, cs = api.trainer_fwd(d["cu"], d["q"], d["k"], d["v"], d["a"], d["b"], chunk=w.chunk)
@@ -164,12 +177,15 @@ def test_bwd_config_trainer_matches_oracle(trainer_case):
     torch.cuda.synchronize()
     assert_grads(got, ref, "trainer config")
     again = run_bwd(w, d, cs, ddo, ddsf)
-    for L in (8, 4):
-        with lanes(L):
+    for L in LANES:
+        with lanes(L), schedule("chunks"):
             other = run_bwd(w, d, cs, ddo, ddsf)
         for g in GRADS:
-            assert_dev_equal(other[g], got[g], f"L={L} vs automatic {g}")
+            assert_dev_equal(other[g], got[g], f"chunks L={L} vs automatic {g}")
+    with schedule("sequences"):
+        other = run_bwd(w, d, cs, ddo, ddsf)
     for g in GRADS:
+        assert_dev_equal(other[g], got[g], f"sequences vs automatic {g}")
         assert_dev_equal(again[g], got[g], f"repeat {g}")
 
 

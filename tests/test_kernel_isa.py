@@ -30,7 +30,7 @@ def test_all_kernels_present(asm):
     assert sum("cpr_decode_kernel" in n for n in names) == 4 * 3 * 2
     assert sum("cpr_bwd_plan_kernel" in n for n in names) == 1
     assert sum("cpr_bwd_state_kernel" in n for n in names) == 4 * 3 * 2
-    assert sum("cpr_bwd_chunk_kernel" in n for n in names) == 4 * 2
+    assert sum("cpr_bwd_chunk_kernel" in n for n in names) == 4 * 2 * 2  # d_k, dtype, schedule
     assert sum("cpr_bwd_combine_kernel" in n for n in names) == 6
 
 
