@@ -30,7 +30,12 @@ HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, spec sheet
 FP32_FMA_PEAK_TFLOPS = 78.6       # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (no packed fp32)
 FP32_PACKED_PEAK_TFLOPS = 157.3   # spec-sheet figure with packed fp32 (not used by these kernels)
 METRIC = "GDN-CPR tokens/s (trainer_fwd, prefill), decode-step us, % of HBM peak"
-KERNEL_SOURCES = ["cpr_kernels.hip", "cpr_row.hpp", "cpr_io.hpp"]
+KERNEL_SOURCES = {  # sources whose hash a traffic summary must match to be used
+    "cpr_scan_trainer_fwd": ["cpr_kernels.hip", "cpr_row.hpp", "cpr_io.hpp"],
+    "cpr_bwd_trainer": ["cpr_backward.hip", "cpr_row.hpp", "cpr_io.hpp"],
+}
+PMC_COMMAND = ("rocprofv3 --pmc {counter} --output-format csv -d <dir> -o {name} -- python3 "
+               "bench.py --cases bwd --no-cpu-baseline --steps 3 --warmup 1 --copy-probe")
 COPY_PROBE_BYTES = 256 << 20  # read once and written once by the calibration copy
 
 
@@ -38,9 +43,9 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_digest():
+def kernel_source_digest(name="cpr_scan_trainer_fwd"):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[name]:
         with open(os.path.join(ROOT, "bitwise_consistent_linear_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -138,62 +143,82 @@ def traffic_for(name, launches_bytes_fn=None):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256") != kernel_source_digest():
+    if t.get("kernel_source_sha256") != kernel_source_digest(name):
         return None
     return int(t["hbm_bytes_per_launch"])
 
 
-def write_traffic(fetch_csv, write_csv, kernel_substr="cpr_scan_kernel", name="cpr_scan_trainer_fwd"):
-    """From two rocprofv3 --pmc runs of `bench.py --cases main --copy-probe` (FETCH_SIZE,
-    then WRITE_SIZE; KiB per dispatch), write profiles/<name>_traffic.json: the kernel's HBM
-    bytes per launch, each counter scaled by what it reads for the 256 MiB calibration copy
-    (read once, written once)."""
+def write_traffic(fetch_csv, write_csv):
+    """From two rocprofv3 --pmc runs of `bench.py --cases bwd --copy-probe` (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch), write profiles/cpr_scan_trainer_fwd_traffic.json and
+    profiles/cpr_bwd_trainer_traffic.json: HBM bytes per launch, each counter scaled by what
+    it reads for the 256 MiB calibration copy (read once, written once)."""
     import csv
     import statistics
 
-    def per_kernel(path, counter):
-        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        copy = [float(r["Counter_Value"]) for r in rows
-                if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) > 1024]
-        kern = [float(r["Counter_Value"]) for r in rows if kernel_substr in r["Kernel_Name"]]
-        knames = sorted({r["Kernel_Name"] for r in rows if kernel_substr in r["Kernel_Name"]})
-        if not copy or not kern:
-            raise SystemExit(f"{path}: no calibration copy or no {kernel_substr} dispatch")
-        return statistics.median(copy), statistics.median(kern), len(kern), knames
+    def rows(path, counter):
+        return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
 
-    cf, kf, nf, names = per_kernel(fetch_csv, "FETCH_SIZE")
-    cw, kw, nw, _ = per_kernel(write_csv, "WRITE_SIZE")
+    def copy_kib(rs):
+        c = [float(r["Counter_Value"]) for r in rs
+             if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) > 1024]
+        if not c:
+            raise SystemExit("no calibration copy in the counter files")
+        return statistics.median(c)
+
+    def per_kernel(rs, substr):
+        by = {}
+        for r in rs:
+            if substr in r["Kernel_Name"]:
+                by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: statistics.median(v) for k, v in by.items()}
+
+    fr, wr = rows(fetch_csv, "FETCH_SIZE"), rows(write_csv, "WRITE_SIZE")
+    cf, cw = copy_kib(fr), copy_kib(wr)
     fetch_scale = COPY_PROBE_BYTES / (cf * 1024)
     write_scale = COPY_PROBE_BYTES / (cw * 1024)
-    fetch_b = kf * 1024 * fetch_scale
-    write_b = kw * 1024 * write_scale
     from bitwise_consistent_linear_amd import workloads as W
     w = W.trainer_fwd()
-    out = {
-        "kernel": names,
-        "workload": "trainer_fwd: 4 x 4096 tokens, 16 heads, d=128, C=64, bf16 q/k/v",
-        "kernel_source_sha256": kernel_source_digest(),
-        "fetch_size_kib_per_launch": kf, "write_size_kib_per_launch": kw,
-        "dispatches_counted": [nf, nw],
-        "calibration_copy_bytes": COPY_PROBE_BYTES,
-        "calibration_fetch_kib": cf, "calibration_write_kib": cw,
-        "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
-        "hbm_fetch_bytes_per_launch": int(fetch_b), "hbm_write_bytes_per_launch": int(write_b),
-        "hbm_bytes_per_launch": int(fetch_b + write_b),
-        "algorithmic_bytes_per_launch": int(scan_bytes(w, chunk_states=w.total_chunks)),
-        "commands": [
-            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o fetch -- python3 bench.py "
-            "--cases main --no-cpu-baseline --steps 3 --warmup 1 --copy-probe",
-            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o write -- python3 bench.py "
-            "--cases main --no-cpu-baseline --steps 3 --warmup 1 --copy-probe",
-            "python3 bench.py --traffic-from <dir>/fetch_counter_collection.csv "
-            "<dir>/write_counter_collection.csv"],
-    }
-    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
-    with open(path, "w") as f:
-        json.dump(out, f, indent=1)
-        f.write("\n")
-    print(json.dumps(out, indent=1))
+    targets = [
+        ("cpr_scan_trainer_fwd", "cpr_scan_kernel",
+         "trainer_fwd: 4 x 4096 tokens, 16 heads, d=128, C=64, bf16 q/k/v",
+         scan_bytes(w, chunk_states=w.total_chunks)),
+        ("cpr_bwd_trainer", "cpr_bwd_",
+         "trainer_bwd on the trainer_fwd workload (every backward kernel of one call)",
+         bwd_bytes(w)),
+    ]
+    for name, substr, workload, alg in targets:
+        kf, kw = per_kernel(fr, substr), per_kernel(wr, substr)
+        if not kf or not kw:
+            raise SystemExit(f"no {substr} dispatch in the counter files")
+        kernels = {k: {"fetch_kib": kf[k], "write_kib": kw.get(k, 0.0),
+                       "hbm_bytes": int(kf[k] * 1024 * fetch_scale
+                                        + kw.get(k, 0.0) * 1024 * write_scale)}
+                   for k in sorted(kf)}
+        fetch_b = sum(v["fetch_kib"] for v in kernels.values()) * 1024 * fetch_scale
+        write_b = sum(v["write_kib"] for v in kernels.values()) * 1024 * write_scale
+        out = {
+            "kernels": kernels,
+            "workload": workload,
+            "kernel_source_sha256": kernel_source_digest(name),
+            "calibration_copy_bytes": COPY_PROBE_BYTES,
+            "calibration_fetch_kib": cf, "calibration_write_kib": cw,
+            "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+            "hbm_fetch_bytes_per_launch": int(fetch_b),
+            "hbm_write_bytes_per_launch": int(write_b),
+            "hbm_bytes_per_launch": int(fetch_b + write_b),
+            "algorithmic_bytes_per_launch": int(alg),
+            "commands": [PMC_COMMAND.format(counter="FETCH_SIZE", name="fetch"),
+                         PMC_COMMAND.format(counter="WRITE_SIZE", name="write"),
+                         "python3 bench.py --traffic-from <dir>/fetch_counter_collection.csv "
+                         "<dir>/write_counter_collection.csv"],
+        }
+        path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+        with open(path, "w") as f:
+            json.dump(out, f, indent=1)
+            f.write("\n")
+        print(name, out["hbm_bytes_per_launch"], "bytes per launch;",
+              out["algorithmic_bytes_per_launch"], "algorithmic")
 
 
 # ------------------------------------------------------------------------------ cases
@@ -281,7 +306,8 @@ def bench_trainer_bwd(steps, warmup, fwd_kernel_ms):
             "ms_per_call": round(wall / steps * 1e3, 4), "kernel_ms": round(ms, 4),
             "fwd_plus_bwd_kernel_ms": round(fwd_kernel_ms + ms, 4),
             "workspace_bytes": int(need), "steps": steps,
-            "roofline": roofline_alu(flops, ms), "hbm": hbm(bwd_bytes(w), ms)}
+            "roofline": dict(roofline_alu(flops, ms), traffic=traffic_for("cpr_bwd_trainer")),
+            "hbm": hbm(bwd_bytes(w), ms)}
 
 
 def bench_decode_after_prefill(w, prefix, nsteps, warmup_steps, label):
@@ -413,8 +439,8 @@ def main():
                     help="also run a plain 256 MiB device copy (untimed), the known-size "
                          "reference that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/cpr_scan_trainer_fwd_traffic.json from two rocprofv3 "
-                         "counter CSVs and exit (no GPU needed)")
+                    help="write profiles/*_traffic.json from two rocprofv3 counter CSVs and "
+                         "exit (no GPU needed)")
     args = ap.parse_args()
     if args.traffic_from:
         write_traffic(*args.traffic_from)
