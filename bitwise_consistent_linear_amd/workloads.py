@@ -194,6 +194,19 @@ def cotangents(w: Workload, seed: int, with_final: bool = True, final_scale: flo
     return do, dsf
 
 
+def make_linear(M: int, N: int, K: int, bf16: bool, seed: int):
+    """Inputs of the linear region: x [M, K] ~ N(0, 1) and w [K, N] ~ N(0, 1/K) (the usual
+    scale of a layer's weights), from the first two children of SeedSequence(seed), drawn
+    as above (bf16 as uint16 bit patterns). Row m of x is drawn from the same stream
+    positions whatever M is, so a smaller M gives a prefix of the same rows."""
+    st = np.random.SeedSequence(seed).spawn(2)
+    x = _draw(st[0], (M, K), "normal", bf16)
+    w32 = _draw(st[1], (K, N), "normal")
+    w32 *= np.float32(1.0 / np.sqrt(K))
+    w = f32_to_bf16_bits(w32) if bf16 else w32
+    return x, w
+
+
 # ----------------------------------------------------------------------------------------
 # The five workload configurations.
 

@@ -477,3 +477,71 @@ int oracle_backward(int N, int Hk, int Hv, int dk, int dv, int C, int dtype,
   for (int w = 1; w < nt; ++w) pthread_join(th[w], NULL);
   return 0;
 }
+
+/* ========================================================================================
+ * Linear region: Y = X W, every output the contract dot product above.
+ *
+ * The IsoExec pages make a tensor-parallel matrix product invariant by splitting its K
+ * dimension into contiguous leaves, accumulating each leaf in binary32 in a fixed schedule
+ * and combining the leaves in a fixed order (agentlenshq.com, section on achieving parallel
+ * invariance: tensor parallelism). Reading taken: the leaves and their combination are
+ * those of the contract dot, so
+ *   Y[m, n] = dot(X[m, 0..K), W[0..K, n])      (16 leaves of K/16; leaf = rounded first
+ *                                               product, then fmaf ascending; pairwise tree)
+ * with X [M, K] and W [K, N] row-major, binary32 or bf16 (widened exactly), Y [M, N]
+ * binary32. Row m of Y depends on row m of X and on W only (batch invariance).
+ * ======================================================================================== */
+
+typedef struct {
+  int M, N, K;
+  const float *xf; /* X widened, [M, K] */
+  const void *w;
+  int wdtype;
+  float *y;
+  int n0, n1;
+} lin_job;
+
+static void *lin_worker(void *arg) {
+  const lin_job *J = (const lin_job *)arg;
+  float *col = (float *)malloc((size_t)J->K * sizeof(float));
+  if (!col) return (void *)1;
+  for (int n = J->n0; n < J->n1; ++n) {
+    for (int k = 0; k < J->K; ++k) col[k] = load_widened(J->w, (int64_t)k * J->N + n, J->wdtype);
+    for (int m = 0; m < J->M; ++m)
+      J->y[(int64_t)m * J->N + n] = contract_dot(J->xf + (int64_t)m * J->K, col, J->K);
+  }
+  free(col);
+  return NULL;
+}
+
+int oracle_linear(int M, int N, int K, int xdtype, int wdtype, const void *x, const void *w,
+                  float *y, int nthreads) {
+  if (M < 0 || N < 0 || K < ORACLE_LEAVES || K % ORACLE_LEAVES != 0) return -1;
+  if ((xdtype != 0 && xdtype != 1) || (wdtype != 0 && wdtype != 1)) return -1;
+  if (M == 0 || N == 0) return 0;
+  float *xf = (float *)malloc((size_t)M * K * sizeof(float));
+  if (!xf) return -2;
+  for (int64_t e = 0; e < (int64_t)M * K; ++e) xf[e] = load_widened(x, e, xdtype);
+  int nt = nthreads < 1 ? 1 : (nthreads > 256 ? 256 : nthreads);
+  if (N < nt) nt = N;
+  pthread_t th[256];
+  lin_job jobs[256];
+  for (int t = 0; t < nt; ++t) {
+    lin_job j = {M, N, K, xf, w, wdtype, y, (int)((int64_t)N * t / nt),
+                 (int)((int64_t)N * (t + 1) / nt)};
+    jobs[t] = j;
+  }
+  int rc = 0, started = 1;
+  for (; started < nt; ++started)
+    if (pthread_create(&th[started], NULL, lin_worker, &jobs[started]) != 0) break;
+  for (int t = started; t < nt; ++t)  /* a thread that could not start: its share runs here */
+    if (lin_worker(&jobs[t]) != NULL) rc = -2;
+  if (lin_worker(&jobs[0]) != NULL) rc = -2;
+  for (int t = 1; t < started; ++t) {
+    void *ret = NULL;
+    pthread_join(th[t], &ret);
+    if (ret != NULL) rc = -2;
+  }
+  free(xf);
+  return rc;
+}

@@ -54,6 +54,8 @@ class Oracle:
         lib.oracle_decode_step.restype = I
         lib.oracle_backward.argtypes = [I] * 7 + [P] * 15 + [I]
         lib.oracle_backward.restype = I
+        lib.oracle_linear.argtypes = [I, I, I, I, I, P, P, P, I]
+        lib.oracle_linear.restype = I
         lib.oracle_dot.argtypes = [P, P, I]
         lib.oracle_dot.restype = ctypes.c_float
         self.lib = lib
@@ -162,6 +164,22 @@ class Oracle:
             raise ValueError(f"oracle_backward rejected its arguments (rc={rc})")
         return out
 
+    def linear(self, x, w, *, nthreads=None):
+        """Y = X W of the linear region: X [M, K], W [K, N] (float32, or bfloat16 as uint16
+        bit patterns); every Y[m, n] is the contract dot of row m of X and column n of W.
+        Returns Y float32 [M, N]."""
+        x, w = _c(x), _c(w)
+        M, K = x.shape
+        K2, N = w.shape
+        if K2 != K:
+            raise ValueError(f"x is [{M}, {K}] but w is [{K2}, {N}]")
+        y = np.zeros((M, N), np.float32)
+        rc = self.lib.oracle_linear(M, N, K, _dtype_code(x), _dtype_code(w), _ptr(x), _ptr(w),
+                                    _ptr(y), nthreads or default_threads())
+        if rc != 0:
+            raise ValueError(f"oracle_linear rejected its arguments (rc={rc})")
+        return y
+
     def decode_step(self, pos, q, k, v, a, b, state, *, chunk, want_resync=True):
         """One decode step; updates ``state`` in place and returns (o, resync or None).
 
@@ -242,3 +260,7 @@ def decode_step(*args, **kw):
 
 def backward(*args, **kw):
     return get().backward(*args, **kw)
+
+
+def linear(*args, **kw):
+    return get().linear(*args, **kw)

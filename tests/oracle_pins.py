@@ -7,7 +7,9 @@ oracle disagrees with what the mathematics or a hand derivation fixes:
   * exact closed forms with one-hot keys and queries, a in {1, 1/2}, b in {0, 1};
   * invariants: b=0 and a=1 leave S unchanged; unit k with b=1 makes S k = v;
   * an exact-rational binary32 emulator of the stated operation order (bitwise);
-  * structural identities of the three cases (resume, chunk states, decode, packing).
+  * structural identities of the three cases (resume, chunk states, decode, packing);
+  * for the linear region: the inner-product error bound against float64, the exact
+    emulator, one-hot rows and batch invariance.
 The same pins run against deliberately broken builds of the oracle (test_oracle_mutants),
 which must each fail at least one of them.
 """
@@ -420,6 +422,74 @@ def pin_bwd_chunk_invariance(orc):
             ref = r
         for key in GRAD_KEYS:
             assert same_bits(r[key], ref[key]), f"C={C} changed {key}"
+
+
+# --------------------------------------------------------------------------- linear region
+
+def _widen(a):
+    a = np.asarray(a)
+    return W.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a.astype(np.float32)
+
+
+def linear_error_bound(x, w):
+    """Forward error bound of the contract dot with leaves of m = K/16 elements: every
+    product and partial sum passes through at most m + 4 roundings (m in a leaf, 4 tree
+    levels), so |y - x.w| <= gamma_{m+4} * sum_k |x_k w_k| with gamma_n = n u / (1 - n u),
+    u = 2^-24 (the standard inner-product bound, Higham, Accuracy and Stability of
+    Numerical Algorithms, section 3.1)."""
+    K = x.shape[1]
+    n = K // 16 + 4
+    u = 2.0 ** -24
+    gamma = n * u / (1 - n * u)
+    return gamma * (np.abs(_widen(x).astype(np.float64)) @ np.abs(_widen(w).astype(np.float64)))
+
+
+def pin_linear_vs_f64(orc):
+    for M, N, K, bf16, seed in [(17, 23, 512, True, 41), (9, 5, 96, False, 42), (3, 64, 4096, True, 43)]:
+        x, w = W.make_linear(M, N, K, bf16, seed)
+        y = orc.linear(x, w)
+        y64 = _widen(x).astype(np.float64) @ _widen(w).astype(np.float64)
+        err = np.abs(y.astype(np.float64) - y64)
+        bound = linear_error_bound(x, w)
+        assert np.all(err <= bound), f"linear ({M},{N},{K}): err exceeds the bound"
+        assert err.max() > 0, "no rounding at all: suspicious"
+
+
+def pin_linear_exact_emulator(orc):
+    # spread exponents so that the leaf chains, the fused steps and the tree all round
+    g = np.random.default_rng(44)
+    for K in (16, 48):
+        x = (g.standard_normal((3, K)) * 2.0 ** g.integers(-12, 12, (3, K))).astype(np.float32)
+        w = (g.standard_normal((K, 4)) * 2.0 ** g.integers(-12, 12, (K, 4))).astype(np.float32)
+        y = orc.linear(x, w)
+        for m in range(3):
+            for n in range(4):
+                want = exact_fp32.dot([float(v) for v in x[m]], [float(v) for v in w[:, n]])
+                assert same_bits(y[m, n], np.float32(want)), f"emulator K={K} ({m},{n})"
+
+
+def pin_linear_onehot_rows(orc):
+    # a one-hot row of x selects a row of w exactly: catches a transposed w or shifted rows
+    K = N = 64
+    g = np.random.default_rng(45)
+    w = g.standard_normal((K, N)).astype(np.float32)
+    w[w == 0] = 1.0
+    picks = g.permutation(K)[:10]
+    x = np.zeros((10, K), np.float32)
+    x[np.arange(10), picks] = 1.0
+    y = orc.linear(x, w)
+    assert same_bits(y, w[picks]), "one-hot rows do not select the rows of w"
+
+
+def pin_linear_batch_invariance(orc):
+    # a row's output does not depend on the other rows or on the column split
+    x, w = W.make_linear(40, 24, 256, True, 46)
+    y = orc.linear(x, w)
+    assert same_bits(orc.linear(x[13:14], w), y[13:14]), "single row differs"
+    assert same_bits(orc.linear(x[5:29], w), y[5:29]), "row slice differs"
+    assert same_bits(orc.linear(x, np.ascontiguousarray(w[:, 7:19])), y[:, 7:19]), "column slice"
+    x2, _ = W.make_linear(7, 24, 256, True, 46)
+    assert same_bits(x2, x[:7]), "the generator's rows are not a prefix"
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

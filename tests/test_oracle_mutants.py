@@ -79,6 +79,13 @@ MUTANTS = {
       }""")],
     "bwd_final_state_gradient_ignored": [("sh[(int64_t)i * dk + e] = J->dSf ? J->dSf[",
                                           "sh[(int64_t)i * dk + e] = J->dSf ? 0.0f * J->dSf[")],
+    # linear region
+    "linear_w_transposed": [("col[k] = load_widened(J->w, (int64_t)k * J->N + n, J->wdtype);",
+                             "col[k] = load_widened(J->w, ((int64_t)n * J->K + k) % "
+                             "((int64_t)J->K * J->N), J->wdtype);")],
+    "linear_x_rows_shifted": [("contract_dot(J->xf + (int64_t)m * J->K, col, J->K);",
+                               "contract_dot(J->xf + (int64_t)(m > 0 ? m - 1 : 0) * J->K, col, "
+                               "J->K);")],
 }
 
 
@@ -97,9 +104,11 @@ def test_mutant_is_caught(name, tmp_path):
     lib = O.build(force=True, src=str(mutant_src), out=str(tmp_path / f"lib{name}.so"))
     orc = O.Oracle(lib)
     # backward mutants are most quickly caught by the backward pins: try those first
+    def family(n):
+        return "bwd" if "bwd" in n else ("linear" if "linear" in n else "fwd")
+
     pins = sorted(oracle_pins.ALL_PINS,
-                  key=lambda p: (not (name.startswith("bwd") == p.__name__.startswith("pin_bwd")),
-                                 p.__name__))
+                  key=lambda p: (family(name) != family(p.__name__), p.__name__))
     caught = None
     for pin in pins:
         try:
