@@ -28,6 +28,11 @@ class GdnShape(ctypes.Structure):
                 ("qkv_dtype", ctypes.c_int32)]
 
 
+class GdnLinearShape(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("x_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32)]
+
+
 class GdnError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
@@ -70,6 +75,8 @@ def lib():
         L.gdn_cpr_trainer_bwd.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_char_p, P, I64,
                                           P, P, P, P, P, P, P, I64, P, P,
                                           P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.gdn_linear_fwd.restype = I32
+        L.gdn_linear_fwd.argtypes = [ctypes.POINTER(GdnLinearShape), ctypes.c_char_p, P, P, P, P]
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_last_error.argtypes = []
         _lib = L
@@ -324,3 +331,28 @@ def trainer_bwd(cu_seqlens, q, k, v, a, b, chunk_states, d_o, *, chunk, initial_
         _ptr(out["dv"]), _ptr(out["da"]), _ptr(out["db"]), _ptr(out["dS0"]),
         _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+def linear_fwd(x, w, *, y=None, identity=None, stream=None):
+    """gdn_linear_fwd: Y = X W of the linear region. x [M, K], w [K, N] (float32 or
+    bfloat16, contiguous GPU tensors); returns y float32 [M, N]. The identity defaults to
+    the contract identity of (chunk 64, d_k 128); the linear rule is in every one."""
+    torch = _torch()
+    dt = (torch.float32, torch.bfloat16)
+    _need(x, "x", dt, 2)
+    _need(w, "w", dt, 2)
+    M, K = x.shape
+    if w.shape[0] != K:
+        raise ValueError(f"x is {tuple(x.shape)} but w is {tuple(w.shape)}")
+    N = w.shape[1]
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _need(y, "y", (torch.float32,), 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError(f"y must be [{M}, {N}]")
+    code = {torch.float32: GDN_DTYPE_F32, torch.bfloat16: GDN_DTYPE_BF16}
+    shape = GdnLinearShape(M, N, K, code[x.dtype], code[w.dtype])
+    ident = identity if identity is not None else contract_identity(64, 128)
+    _check(lib().gdn_linear_fwd(ctypes.byref(shape), ident, _ptr(x), _ptr(w), _ptr(y),
+                                _stream(stream)))
+    return y

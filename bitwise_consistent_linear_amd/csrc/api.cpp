@@ -397,4 +397,53 @@ GDN_EXPORT gdn_status_t gdn_cpr_trainer_bwd(
   return gdn::ok();
 }
 
+GDN_EXPORT gdn_status_t gdn_linear_fwd(const gdn_linear_shape_t *shape,
+                                       const uint8_t *expected_identity, const void *x,
+                                       const void *w, float *y, void *stream) {
+  const char *fn = "gdn_linear_fwd";
+  if (!shape) return gdn::fail(GDN_E_NULL, std::string(fn) + ": shape is NULL");
+  if (!expected_identity)
+    return gdn::fail(GDN_E_NULL, std::string(fn) + ": expected_identity is NULL");
+  // the linear rule is part of every contract text: accept the identity of any admitted one
+  bool known = false;
+  const int32_t chunks[] = {16, 32, 64, 128, 256}, dks[] = {16, 32, 64, 128};
+  for (int32_t c : chunks)
+    for (int32_t d : dks) {
+      uint8_t digest[GDN_CPR_IDENTITY_BYTES];
+      const std::string text = gdn::contract_text(c, d);
+      gdn::sha256(reinterpret_cast<const uint8_t *>(text.data()), text.size(), digest);
+      known = known || std::memcmp(digest, expected_identity, sizeof digest) == 0;
+    }
+  if (!known)
+    return gdn::fail(GDN_E_IDENTITY, std::string(fn) + ": expected_identity is not this library's "
+                                         "contract");
+  if (shape->m < 0 || shape->n < 0 || shape->m > gdn::kMaxInt32 || shape->n > gdn::kMaxInt32)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": m and n must be in [0, 2^31)");
+  if (!gdn::linear_k_admitted(shape->k))
+    return gdn::fail(GDN_E_UNSUPPORTED, std::string(fn) + ": k must be a positive multiple of 512 "
+                                            "up to 2^24");
+  if ((shape->x_dtype != GDN_DTYPE_F32 && shape->x_dtype != GDN_DTYPE_BF16) ||
+      (shape->w_dtype != GDN_DTYPE_F32 && shape->w_dtype != GDN_DTYPE_BF16))
+    return gdn::fail(GDN_E_UNSUPPORTED, std::string(fn) + ": dtypes must be F32 or BF16");
+  if (shape->m == 0 || shape->n == 0) return gdn::ok();
+  if (!x || !w || !y) return gdn::fail(GDN_E_NULL, std::string(fn) + ": x, w and y are required");
+  if (!gdn::aligned(x, 16) || !gdn::aligned(w, 16) || !gdn::aligned(y, 4))
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": x and w must be 16-byte aligned, y 4-byte");
+  gdn::LinearArgs args{};
+  args.m = shape->m;
+  args.n = shape->n;
+  args.k = (int32_t)shape->k;
+  args.x_bf16 = shape->x_dtype == GDN_DTYPE_BF16;
+  args.w_bf16 = shape->w_dtype == GDN_DTYPE_BF16;
+  args.x = x;
+  args.w = w;
+  args.y = y;
+  if (gdn::linear_grid(args) > gdn::kMaxInt32)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": m * n too large");
+  const hipError_t e = gdn::launch_linear(args, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return gdn::fail(GDN_E_DEVICE, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
+  return gdn::ok();
+}
+
 }  // extern "C"

@@ -118,7 +118,8 @@ bool admitted_dk(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; 
 std::string contract_text(int32_t chunk, int32_t d_k) {
   std::string s;
   s += "contract=isoexec-gdn-cpr\n";
-  s += "version=2\n";
+  s += "version=3\n";
+  s += "regions=gated_delta_rule,linear\n";
   s += "region=gated_delta_rule\n";
   s += "cases=trainer_fwd,trainer_bwd,engine_prefill,engine_decode\n";
   s += "recurrence=S_t=a_t*S_{t-1}*(I-b_t*k_t*k_t^T)+b_t*v_t*k_t^T;o_t=S_t*q_t\n";
@@ -138,6 +139,9 @@ std::string contract_text(int32_t chunk, int32_t d_k) {
        "xh_e=fma(-dv_i,k_e,sh_e);pk_e=fma(-dv_i,x_e,d*sh_e);pa=dot(xh,s_prev);sh_e=a*xh_e\n";
   s += "bwd_rows=dq,dk,da,db:pairwise over rows in natural order;unpaired passes through\n";
   s += "bwd_gqa=dq,dk:value heads of the group added in ascending order\n";
+  s += "region=linear\n";
+  s += "linear=y[m,n]=dot(x[m,:],w[:,n]) over K;dot as above with leaf K/16;"
+       "inputs=x,w:binary32|bfloat16 widened exactly;output=binary32;rows independent\n";
   s += "chunk=" + std::to_string(chunk) + "\n";
   s += "d_k=" + std::to_string(d_k) + "\n";
   return s;

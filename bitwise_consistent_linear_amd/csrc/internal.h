@@ -81,6 +81,18 @@ int64_t backward_state_grid(const BwdArgs &args, int lanes_per_row);
 int64_t backward_chunk_grid(const BwdArgs &args, bool seq);
 hipError_t launch_backward(const BwdArgs &args, int lanes_per_row, bool seq, hipStream_t stream);
 
+// Arguments of one linear-region launch (Y = X W); validated on the host.
+struct LinearArgs {
+  int64_t m, n;
+  int32_t k;
+  int32_t x_bf16, w_bf16;
+  const void *x, *w;
+  float *y;
+};
+bool linear_k_admitted(int64_t k);
+int64_t linear_grid(const LinearArgs &args);
+hipError_t launch_linear(const LinearArgs &args, hipStream_t stream);
+
 // Enqueue the kernels. lanes_per_row is 16, 8 or 4. Return the HIP launch status.
 hipError_t launch_scan(const ScanArgs &args, int lanes_per_row, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &args, int lanes_per_row, hipStream_t stream);

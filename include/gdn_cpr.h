@@ -229,6 +229,33 @@ gdn_status_t gdn_cpr_trainer_bwd(const gdn_shape_t *shape, const uint8_t *expect
                                  float *d_initial_state, void *workspace,
                                  size_t workspace_bytes, void *stream);
 
+/* Host struct of the linear region: Y [m, n] = X [m, k] W [k, n], all row-major.
+ * Admitted: 0 <= m, n < 2^31; k a positive multiple of 512 up to 2^24; x_dtype and w_dtype
+ * GDN_DTYPE_F32 or GDN_DTYPE_BF16. */
+typedef struct gdn_linear_shape {
+  int64_t m, n, k;
+  int32_t x_dtype, w_dtype;
+} gdn_linear_shape_t;
+
+/* linear: Y = X W in which every output is the contract dot of a row of X and a column of
+ * W, so its bits depend on that row and column only: not on m (batch invariance), the tile
+ * or the schedule. This is the second region of the contract: the IsoExec pages make a
+ * tensor-parallel matrix product invariant by splitting K into contiguous leaves, each
+ * accumulated in binary32 on the matrix units in a fixed schedule, combined in a fixed
+ * order (agentlenshq.com, section on achieving parallel invariance: tensor parallelism).
+ * Here the 16 leaves of k/16 run on gfx950's binary32 matrix instructions, whose every
+ * step is a fused multiply-add in ascending k, and are added by the dot's pairwise tree.
+ *   shape, expected_identity : host pointers; the identity of any admitted (chunk, d_k)
+ *                              (the linear rule is part of every contract text)
+ *   x  [m, k], w [k, n]      : binary32, or bfloat16 widened exactly; 16-byte aligned
+ *   y  [m, n]                : binary32 output, 4-byte aligned; must not alias x or w
+ *   stream                   : hipStream_t or NULL.
+ * Errors: GDN_E_NULL, GDN_E_IDENTITY, GDN_E_SHAPE (sizes, alignment),
+ * GDN_E_UNSUPPORTED (k or dtype not admitted), GDN_E_DEVICE. m == 0 or n == 0 does
+ * nothing. */
+gdn_status_t gdn_linear_fwd(const gdn_linear_shape_t *shape, const uint8_t *expected_identity,
+                            const void *x, const void *w, float *y, void *stream);
+
 /* Text describing the calling thread's last non-GDN_OK status ("" if none). The pointer
  * stays valid until the thread's next call into the library. Host only. */
 const char *gdn_last_error(void);

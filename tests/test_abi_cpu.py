@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\s[TW]\s+(gdn_\w+)$", out, flags=re.M))
@@ -140,6 +140,13 @@ def bwd(L, sh, identity=None, T=128, total_chunks=2, ws_bytes=1 << 30, **ptrs):
                                  p["ds0"], p["ws"], ws_bytes, None)
 
 
+def linear(L, m=64, n=64, k=512, xdt=api.GDN_DTYPE_BF16, wdt=api.GDN_DTYPE_BF16, identity=None,
+           x=FAKE, w=FAKE, y=FAKE, shape_ok=True):
+    sh = api.GdnLinearShape(m, n, k, xdt, wdt)
+    idb = api.contract_identity(64, 128) if identity is None else identity
+    return L.gdn_linear_fwd(ctypes.byref(sh) if shape_ok else None, idb, x, w, y, None)
+
+
 def decode(L, sh, identity=None, **ptrs):
     p = dict(pos=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, state=FAKE, o=FAKE, rs=None)
     p.update(ptrs)
@@ -199,6 +206,16 @@ REFUSALS = [
     ("bwd misaligned dq", lambda L: bwd(L, shape(), dq=FAKE + 2), api.GDN_E_SHAPE),
     ("bwd null q", lambda L: bwd(L, shape(), q=None), api.GDN_E_NULL),
     ("bwd heads not a multiple", lambda L: bwd(L, shape(num_qk_heads=3)), api.GDN_E_SHAPE),
+    ("linear null shape", lambda L: linear(L, shape_ok=False), api.GDN_E_NULL),
+    ("linear wrong identity", lambda L: linear(L, identity=bytes(32)), api.GDN_E_IDENTITY),
+    ("linear k not a multiple of 512", lambda L: linear(L, k=768), api.GDN_E_UNSUPPORTED),
+    ("linear k zero", lambda L: linear(L, k=0), api.GDN_E_UNSUPPORTED),
+    ("linear dtype not admitted", lambda L: linear(L, xdt=5), api.GDN_E_UNSUPPORTED),
+    ("linear negative m", lambda L: linear(L, m=-1), api.GDN_E_SHAPE),
+    ("linear m too large", lambda L: linear(L, m=2**31), api.GDN_E_SHAPE),
+    ("linear null x", lambda L: linear(L, x=None), api.GDN_E_NULL),
+    ("linear null y", lambda L: linear(L, y=None), api.GDN_E_NULL),
+    ("linear misaligned w", lambda L: linear(L, w=FAKE + 8), api.GDN_E_SHAPE),
 ]
 
 
@@ -206,7 +223,7 @@ REFUSALS = [
 def test_refused_before_launch(L, name, call, status):
     assert call(L) == status
     msg = L.gdn_last_error().decode()
-    assert msg.startswith("gdn_cpr_"), msg
+    assert msg.startswith(("gdn_cpr_", "gdn_linear_")), msg
 
 
 def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
@@ -241,3 +258,12 @@ def test_bwd_workspace_size(L):
     assert L.gdn_cpr_trainer_bwd_workspace(ctypes.byref(sh), 100, 4,
                                            ctypes.byref(n)) == api.GDN_E_SHAPE
     assert L.gdn_cpr_trainer_bwd_workspace(ctypes.byref(sh), 100, 2, None) == api.GDN_E_NULL
+
+
+def test_linear_accepts_every_contract_identity_and_empty_sizes(L):
+    """The linear rule is part of every contract text; m == 0 or n == 0 launches nothing
+    (fake pointers are never touched)."""
+    for c in CHUNKS:
+        for d in DKS:
+            assert linear(L, m=0, identity=api.contract_identity(c, d)) == api.GDN_OK
+    assert linear(L, n=0, x=None, w=None, y=None) == api.GDN_OK
