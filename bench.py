@@ -7,10 +7,11 @@ C = 64, bf16 q/k/v, fp32 a/b/state/o. `value` is tokens/s of that step with inpu
 in HBM. The same line also reports, under "cases", engine_prefill tokens/s (64 varlen
 sequences, 262144 tokens, 16 q/k / 32 v heads), the engine_decode step time (256
 sequences after a 1000-token prefill, 512 steps), the backward (gdn_cpr_trainer_bwd) on
-the trainer workload and the long-context runs, each with its
+the trainer workload, the long-context runs and the linear region (a 16384 x 4096 x 4096
+batch-invariant matrix product on the matrix cores), each with its
 fraction of the relevant peak, plus the CPU oracle timed on the host as a baseline.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cases all|main|bwd]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cases all|main|bwd|linear]
                        [--no-cpu-baseline]
 """
 
@@ -29,6 +30,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, spec sheet
 FP32_FMA_PEAK_TFLOPS = 78.6       # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (no packed fp32)
 FP32_PACKED_PEAK_TFLOPS = 157.3   # spec-sheet figure with packed fp32 (not used by these kernels)
+FP32_MFMA_PEAK_TFLOPS = 157.3     # dense binary32 matrix instructions (the linear region)
 METRIC = "GDN-CPR tokens/s (trainer_fwd, prefill), decode-step us, % of HBM peak"
 KERNEL_SOURCES = {  # sources whose hash a traffic summary must match to be used
     "cpr_scan_trainer_fwd": ["cpr_kernels.hip", "cpr_row.hpp", "cpr_io.hpp"],
@@ -310,6 +312,30 @@ def bench_trainer_bwd(steps, warmup, fwd_kernel_ms):
             "hbm": hbm(bwd_bytes(w), ms)}
 
 
+def bench_linear(steps, warmup, M=16384, N=4096, K=4096):
+    """gdn_linear_fwd: Y = X W with every output the contract dot, on the matrix cores."""
+    import torch
+    from bitwise_consistent_linear_amd import api
+    from bitwise_consistent_linear_amd import workloads as W
+    log(f"linear: {M} x {N} x {K}, bf16 inputs")
+    x, w = W.make_linear(M, N, K, True, 31)
+    dx, dw = up(x), up(w)
+    y = api.linear_fwd(dx, dw)
+    wall, per = timed(lambda: api.linear_fwd(dx, dw, y=y), steps, warmup)
+    ms = sum(per) / len(per)
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    nbytes = M * K * 2 + K * N * 2 + M * N * 4
+    del dx, dw, y
+    return {"workload": f"linear region: Y[{M}, {N}] = X[{M}, {K}] W[{K}, {N}], bf16 X and W "
+                        "(widened exactly), binary32 Y, each output the 16-leaf contract dot",
+            "ms_per_call": round(wall / steps * 1e3, 4), "kernel_ms": round(ms, 4),
+            "steps": steps,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                         "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4)},
+            "hbm": hbm(nbytes, ms)}
+
+
 def bench_decode_after_prefill(w, prefix, nsteps, warmup_steps, label):
     """Prefill `prefix` tokens of every sequence, then time decode steps one by one."""
     import torch
@@ -431,9 +457,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cases", choices=["all", "main", "bwd"], default="all",
-                    help="all: every case; main: trainer_fwd only; bwd: trainer_fwd and the "
-                         "backward (for profiling)")
+    ap.add_argument("--cases", choices=["all", "main", "bwd", "linear"], default="all",
+                    help="all: every case; main: trainer_fwd only; bwd / linear: trainer_fwd "
+                         "and the backward / the linear region (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (untimed), the known-size "
@@ -504,9 +530,13 @@ def main():
         torch.cuda.empty_cache()
         cases["long_context"] = bench_long(max(2, args.steps // 10))
         torch.cuda.empty_cache()
+        cases["linear"] = bench_linear(max(3, args.steps // 4), 1)
+        torch.cuda.empty_cache()
         out["cases"] = cases
     elif args.cases == "bwd":
         out["cases"] = {"trainer_bwd": bench_trainer_bwd(max(3, args.steps // 4), 1, kernel_ms)}
+    elif args.cases == "linear":
+        out["cases"] = {"linear": bench_linear(max(3, args.steps // 4), 1)}
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the trainer_fwd workload")
         out["cpu_baseline"] = cpu_baseline(w)

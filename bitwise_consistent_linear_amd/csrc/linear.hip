@@ -11,10 +11,10 @@
 // combined by the same pairwise tree as the gated delta rule's dots. The bits of Y[m, n]
 // therefore depend on neither the tile, nor the number of rows M, nor the schedule.
 //
-// Workgroup: 4 waves, a 64 x 128 tile of Y; wave (wm, wn) owns rows 32 wm .. 32 wm + 31 and
-// columns 64 wn .. 64 wn + 63 as two 32 x 32 blocks that share the A operand. K is staged
-// 32 at a time into LDS as binary32 (k-major, double-buffered, the next stage's global loads
-// in registers while the current one computes).
+// Workgroup: 8 waves, a 128 x 128 tile of Y; wave (wm, wn) owns rows 32 wm .. 32 wm + 31 and
+// columns 64 wn .. 64 wn + 63 as two 32 x 32 blocks that share the A operand; two waves per
+// SIMD. K is staged 32 at a time into LDS as binary32 (k-major, double-buffered, the next
+// stage's global loads in registers while the current one computes).
 
 #include "internal.h"
 
@@ -23,33 +23,37 @@ namespace {
 
 using f32x16 = float __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
-constexpr int TM = 64, TN = 128, KS = 32;      // workgroup tile, k per stage
-constexpr int XS = TM + 32, WS = TN + 32;      // LDS row strides: k and k+1 land 32 banks apart
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int TM = 128, TN = 128, KS = 32;     // workgroup tile, k per stage
+constexpr int XS = TM + 1, WS = TN + 4;        // LDS row strides (conflict-free deposits)
 constexpr int kLeaves = 16;
+constexpr int XPT = TM * KS / kThreads;        // staged X values per thread (8)
+constexpr int WPT = KS * TN / kThreads;        // staged W values per thread (8)
+static_assert(XPT == 8 && WPT == 8, "staging assumes 8 values per thread");
 
 __device__ __forceinline__ float widen_bf16(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 template <bool XBF16, bool WBF16>
-__global__ __launch_bounds__(kThreads) void linear_leaf_kernel(const LinearArgs p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void linear_leaf_kernel(const LinearArgs p) {
   __shared__ __align__(16) float sx[2][KS][XS];  // sx[buf][k][row]
   __shared__ __align__(16) float sw[2][KS][WS];  // sw[buf][k][col]
 
   const int tid = threadIdx.x, wave = tid / 64, l = tid % 64;
-  const int wm = wave / 2, wn = wave % 2;
+  const int wm = wave / 2, wn = wave % 2;  // 4 x 2 waves of 32 x 64
   const int64_t M = p.m, N = p.n;
   const int K = p.k;
   const int64_t tiles_n = (N + TN - 1) / TN;
   const int64_t tile_m = blockIdx.x / tiles_n, tile_n = blockIdx.x % tiles_n;
   const int64_t m0 = tile_m * TM, n0 = tile_n * TN;
 
-  // staging: X tile [64 rows x 32 k] = 8 values per thread (one row, 8 consecutive k);
-  //          W tile [32 k x 128 cols] = 16 values per thread (one k, 16 consecutive cols)
+  // staging: X tile [128 rows x 32 k]: one row, 8 consecutive k per thread;
+  //          W tile [32 k x 128 cols]: one k, 8 consecutive columns per thread
   const int xr = tid / 4, xk = (tid % 4) * 8;
-  const int wk = tid / 8, wc = (tid % 8) * 16;
+  const int wk = tid / 16, wc = (tid % 16) * 8;
   const int64_t xrow = m0 + xr < M ? m0 + xr : M - 1;  // rows past M repeat the last row
   const bool w_vec = N % (WBF16 ? 8 : 4) == 0;           // every W row 16-byte aligned
-  float xv[8], wv[16];
+  float xv[XPT], wv[WPT];
   auto fetch = [&](int k0) {
     const int64_t xo = xrow * K + k0 + xk;
     if constexpr (XBF16) {
@@ -67,14 +71,13 @@ __global__ __launch_bounds__(kThreads) void linear_leaf_kernel(const LinearArgs 
       xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
     }
     const int64_t wrow = (int64_t)(k0 + wk) * N;
-    if (w_vec && n0 + wc + 16 <= N) {  // 16 columns in range, rows 16-byte aligned
+    if (w_vec && n0 + wc + WPT <= N) {  // all columns in range, rows 16-byte aligned
       if constexpr (WBF16) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.w) +
-                                                           wrow + n0 + wc);
-        const uint4 r0 = src[0], r1 = src[1];
-        const uint32_t u[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+        const uint4 r = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.w) +
+                                                         wrow + n0 + wc);
+        const uint32_t u[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4; ++e) {
           wv[2 * e] = widen_bf16(u[e] & 0xFFFFu);
           wv[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
         }
@@ -82,14 +85,14 @@ __global__ __launch_bounds__(kThreads) void linear_leaf_kernel(const LinearArgs 
         const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(p.w) +
                                                              wrow + n0 + wc);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < 2; ++e) {
           const float4 r = src[e];
           wv[4 * e] = r.x; wv[4 * e + 1] = r.y; wv[4 * e + 2] = r.z; wv[4 * e + 3] = r.w;
         }
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {  // columns past N repeat the last column
+      for (int e = 0; e < WPT; ++e) {  // columns past N repeat the last column
         const int64_t c = n0 + wc + e < N ? n0 + wc + e : N - 1;
         if constexpr (WBF16)
           wv[e] = widen_bf16(static_cast<const uint16_t *>(p.w)[wrow + c]);
@@ -100,9 +103,9 @@ __global__ __launch_bounds__(kThreads) void linear_leaf_kernel(const LinearArgs 
   };
   auto deposit = [&](int buf) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sx[buf][xk + e][xr] = xv[e];
+    for (int e = 0; e < XPT; ++e) sx[buf][xk + e][xr] = xv[e];
 #pragma unroll
-    for (int e = 0; e < 16; e += 4)
+    for (int e = 0; e < WPT; e += 4)
       *reinterpret_cast<float4 *>(&sw[buf][wk][wc + e]) =
           make_float4(wv[e], wv[e + 1], wv[e + 2], wv[e + 3]);
   };
