@@ -545,3 +545,243 @@ int oracle_linear(int M, int N, int K, int xdtype, int wdtype, const void *x, co
   free(xf);
   return rc;
 }
+
+/* ========================================================================================
+ * Two-level CPR: the IsoExec pages' literal reading of CPR, in which chunk-boundary states
+ * come from a chunkwise transition and the outputs inside a chunk from the recurrence run
+ * in parallel between chunks, and decode resynchronises its state every C tokens
+ * (agentlenshq.com, section "Chunkwise-Parallel Recurrent (CPR) Gated DeltaNet").
+ *
+ * Readings taken (per sequence n and value head h; chunk c = in-sequence tokens
+ * [cC, min((c+1)C, T_n))):
+ *  - transition of a full chunk: S_end = S_start A_c + B_c with
+ *      A_c [d_k, d_k]: row j starts as the unit row e_j and absorbs the chunk's tokens with
+ *                      v_i = +0 through the contract row update (x = a s; u = dot(x, k);
+ *                      d = b (0 - u); s = fmaf(d, k, x));
+ *      B_c [d_v, d_k]: row i starts at +0 and absorbs the chunk's tokens with v_i;
+ *  - boundary states: S_0 = the initial state; after every full chunk
+ *      S_{c+1}[i, j] = B_c[i, j] + sum_k S_c[i, k] A_c[k, j]   as fused multiply-adds in
+ *      ascending k with B_c[i, j] first (the order of the binary32 matrix instructions);
+ *      S_{c+1} is the chunk state;
+ *  - outputs: the rows restart from S_c at every chunk start and absorb the chunk's tokens
+ *    through the contract row update, o_t = dot(s_t, q_t);
+ *  - final state: S after the last chunk when T_n is a multiple of C, else the restarted
+ *    rows after the last (partial) chunk's last token;
+ *  - decode: the running rows restart from the boundary state at every chunk start; each
+ *    step writes its token to a C-slot cache; after a chunk's last token the step rebuilds
+ *    A_c and B_c from the cache, sets the boundary state and the running rows to S_{c+1}
+ *    and writes it as the resync checkpoint.
+ * ======================================================================================== */
+
+/* One token on a row without the readout (the transitions keep no output). */
+static void row_absorb(float *s, int dk, float a, float b, float v_i, const float *key) {
+  float x[ORACLE_MAX_D];
+  for (int e = 0; e < dk; ++e) x[e] = a * s[e];
+  float u = contract_dot(x, key, dk);
+  float diff = v_i - u;
+  float delta = b * diff;
+  for (int e = 0; e < dk; ++e) s[e] = fmaf(delta, key[e], x[e]);
+}
+
+/* S_next[i, :] = B[i, :] + S[i, :] A, fused multiply-adds in ascending k from B. */
+static void boundary_step(const float *S, const float *A, const float *B, float *S_next,
+                          int dv, int dk) {
+  for (int i = 0; i < dv; ++i)
+    for (int j = 0; j < dk; ++j) {
+      float acc = B[(int64_t)i * dk + j];
+      for (int kk = 0; kk < dk; ++kk) acc = fmaf(S[(int64_t)i * dk + kk], A[(int64_t)kk * dk + j], acc);
+      S_next[(int64_t)i * dk + j] = acc;
+    }
+}
+
+/* A_c and B_c of the tokens given as arrays: k [n_tok][dk], v [n_tok][dv], a, b [n_tok]. */
+static void chunk_transition(const float *k, const float *v, const float *a, const float *b,
+                             int n_tok, int dk, int dv, float *A, float *B) {
+  for (int j = 0; j < dk; ++j)
+    for (int e = 0; e < dk; ++e) A[(int64_t)j * dk + e] = j == e ? 1.0f : 0.0f;
+  memset(B, 0, sizeof(float) * (size_t)dv * dk);
+  for (int t = 0; t < n_tok; ++t) {
+    const float *kt = k + (int64_t)t * dk;
+    for (int j = 0; j < dk; ++j) row_absorb(A + (int64_t)j * dk, dk, a[t], b[t], 0.0f, kt);
+    for (int i = 0; i < dv; ++i)
+      row_absorb(B + (int64_t)i * dk, dk, a[t], b[t], v[(int64_t)t * dv + i], kt);
+  }
+}
+
+typedef struct {
+  int N, Hk, Hv, dk, dv, C, dtype;
+  const int32_t *cu;
+  const void *q, *k, *v;
+  const float *a, *b, *S0;
+  float *o, *cs, *fs;
+  int npairs, nthreads;
+} cpr2_job;
+
+typedef struct {
+  const cpr2_job *job;
+  int begin, end;
+  int rc;
+} cpr2_slice;
+
+static int cpr2_pair(const cpr2_job *J, int pair) {
+  const int n = pair / J->Hv, h = pair % J->Hv, hk = h / (J->Hv / J->Hk);
+  const int dk = J->dk, dv = J->dv, C = J->C;
+  const int64_t bos = J->cu[n], eos = J->cu[n + 1];
+  int64_t cbase = 0; /* chunk states of earlier sequences */
+  for (int m = 0; m < n; ++m) cbase += (J->cu[m + 1] - J->cu[m]) / C;
+  const size_t st = (size_t)dv * dk;
+  float *S = (float *)malloc(sizeof(float) * st), *R = (float *)malloc(sizeof(float) * st);
+  float *Sn = (float *)malloc(sizeof(float) * st), *B = (float *)malloc(sizeof(float) * st);
+  float *A = (float *)malloc(sizeof(float) * (size_t)dk * dk);
+  float *kb = (float *)malloc(sizeof(float) * (size_t)C * dk);
+  float *qb = (float *)malloc(sizeof(float) * (size_t)C * dk);
+  float *vb = (float *)malloc(sizeof(float) * (size_t)C * dv);
+  float ab[256], bb[256];
+  if (!S || !R || !Sn || !B || !A || !kb || !qb || !vb || C > 256) {
+    free(S); free(R); free(Sn); free(B); free(A); free(kb); free(qb); free(vb);
+    return -2;
+  }
+  for (size_t e = 0; e < st; ++e)
+    S[e] = J->S0 ? J->S0[((int64_t)n * J->Hv + h) * (int64_t)st + (int64_t)e] : 0.0f;
+  memcpy(R, S, sizeof(float) * st);
+  int64_t c = 0;
+  for (int64_t t0 = bos; t0 < eos; t0 += C, ++c) {
+    const int n_tok = (int)(eos - t0 < C ? eos - t0 : C);
+    for (int t = 0; t < n_tok; ++t) {
+      const int64_t qk_off = ((t0 + t) * J->Hk + hk) * (int64_t)dk;
+      for (int e = 0; e < dk; ++e) {
+        kb[(int64_t)t * dk + e] = load_widened(J->k, qk_off + e, J->dtype);
+        qb[(int64_t)t * dk + e] = load_widened(J->q, qk_off + e, J->dtype);
+      }
+      for (int i = 0; i < dv; ++i)
+        vb[(int64_t)t * dv + i] = load_widened(J->v, ((t0 + t) * J->Hv + h) * (int64_t)dv + i, J->dtype);
+      ab[t] = J->a[(t0 + t) * J->Hv + h];
+      bb[t] = J->b[(t0 + t) * J->Hv + h];
+    }
+    /* outputs: the rows restart from the boundary state S */
+    memcpy(R, S, sizeof(float) * st);
+    for (int t = 0; t < n_tok; ++t)
+      for (int i = 0; i < dv; ++i) {
+        float o_i = row_token(R + (int64_t)i * dk, dk, ab[t], bb[t], vb[(int64_t)t * dv + i],
+                              kb + (int64_t)t * dk, qb + (int64_t)t * dk);
+        if (J->o) J->o[((t0 + t) * J->Hv + h) * (int64_t)dv + i] = o_i;
+      }
+    if (n_tok == C) { /* a full chunk: the next boundary state through the transition */
+      chunk_transition(kb, vb, ab, bb, C, dk, dv, A, B);
+      boundary_step(S, A, B, Sn, dv, dk);
+      memcpy(S, Sn, sizeof(float) * st);
+      if (J->cs)
+        memcpy(J->cs + ((cbase + c) * J->Hv + h) * (int64_t)st, S, sizeof(float) * st);
+    }
+  }
+  if (J->fs) {
+    const int64_t Tn = eos - bos;
+    const float *fin = (Tn % C == 0) ? S : R;
+    memcpy(J->fs + ((int64_t)n * J->Hv + h) * (int64_t)st, fin, sizeof(float) * st);
+  }
+  free(S); free(R); free(Sn); free(B); free(A); free(kb); free(qb); free(vb);
+  return 0;
+}
+
+static void *cpr2_worker(void *arg) {
+  cpr2_slice *sl = (cpr2_slice *)arg;
+  for (int p = sl->begin; p < sl->end; ++p)
+    if (cpr2_pair(sl->job, p) != 0) sl->rc = -2;
+  return NULL;
+}
+
+int oracle_cpr2_scan(int N, int Hk, int Hv, int dk, int dv, int C, int dtype,
+                     const int32_t *cu_seqlens, const void *q, const void *k, const void *v,
+                     const float *a, const float *b, const float *S0, float *o,
+                     float *chunk_states, float *final_state, int nthreads) {
+  if (check_dims(N, Hk, Hv, dk, dv, C, dtype) || C > 256) return -1;
+  cpr2_job J = {N, Hk, Hv, dk, dv, C, dtype, cu_seqlens, q, k, v, a, b, S0,
+                o, chunk_states, final_state, N * Hv, nthreads};
+  int nt = nthreads < 1 ? 1 : (nthreads > 256 ? 256 : nthreads);
+  if (J.npairs < nt) nt = J.npairs > 0 ? J.npairs : 1;
+  pthread_t th[256];
+  cpr2_slice sl[256];
+  for (int w = 0; w < nt; ++w) {
+    sl[w].job = &J;
+    sl[w].begin = (int)((int64_t)J.npairs * w / nt);
+    sl[w].end = (int)((int64_t)J.npairs * (w + 1) / nt);
+    sl[w].rc = 0;
+  }
+  int started = 1;
+  for (; started < nt; ++started)
+    if (pthread_create(&th[started], NULL, cpr2_worker, &sl[started]) != 0) break;
+  for (int w = started; w < nt; ++w) cpr2_worker(&sl[w]);
+  cpr2_worker(&sl[0]);
+  for (int w = 1; w < started; ++w) pthread_join(th[w], NULL);
+  for (int w = 0; w < nt; ++w)
+    if (sl[w].rc) return sl[w].rc;
+  return 0;
+}
+
+/* One decode step of the two-level reading for N sequences (pos[n] < 0: idle slot).
+ * state: running rows [N, Hv, dv, dk]; boundary: S_c [N, Hv, dv, dk]; the cache holds the
+ * current chunk's tokens, widened: ck [N, C, Hk, dk], cv [N, C, Hv, dv], ca, cb [N, C, Hv]. */
+int oracle_cpr2_decode_step(int N, int Hk, int Hv, int dk, int dv, int C, int dtype,
+                            const int32_t *pos, const void *q, const void *k, const void *v,
+                            const float *a, const float *b, float *state, float *boundary,
+                            float *ck, float *cv, float *ca, float *cb, float *o,
+                            float *resync) {
+  if (check_dims(N, Hk, Hv, dk, dv, C, dtype) || C > 256) return -1;
+  const size_t st = (size_t)dv * dk;
+  float *A = (float *)malloc(sizeof(float) * (size_t)dk * dk);
+  float *B = (float *)malloc(sizeof(float) * st), *Sn = (float *)malloc(sizeof(float) * st);
+  float *kb = (float *)malloc(sizeof(float) * (size_t)C * dk);
+  float *vb = (float *)malloc(sizeof(float) * (size_t)C * dv);
+  float ab[256], bb[256], kq[ORACLE_MAX_D], qq[ORACLE_MAX_D];
+  if (!A || !B || !Sn || !kb || !vb) {
+    free(A); free(B); free(Sn); free(kb); free(vb);
+    return -2;
+  }
+  const int group = Hv / Hk;
+  for (int n = 0; n < N; ++n) {
+    if (pos[n] < 0) continue;
+    const int slot = pos[n] % C;
+    for (int hk = 0; hk < Hk; ++hk)
+      for (int e = 0; e < dk; ++e)
+        ck[(((int64_t)n * C + slot) * Hk + hk) * dk + e] =
+            load_widened(k, ((int64_t)n * Hk + hk) * dk + e, dtype);
+    for (int h = 0; h < Hv; ++h) {
+      for (int i = 0; i < dv; ++i)
+        cv[(((int64_t)n * C + slot) * Hv + h) * dv + i] =
+            load_widened(v, ((int64_t)n * Hv + h) * dv + i, dtype);
+      ca[((int64_t)n * C + slot) * Hv + h] = a[(int64_t)n * Hv + h];
+      cb[((int64_t)n * C + slot) * Hv + h] = b[(int64_t)n * Hv + h];
+    }
+    for (int h = 0; h < Hv; ++h) {
+      const int hk = h / group;
+      for (int e = 0; e < dk; ++e) {
+        kq[e] = load_widened(k, ((int64_t)n * Hk + hk) * dk + e, dtype);
+        qq[e] = load_widened(q, ((int64_t)n * Hk + hk) * dk + e, dtype);
+      }
+      float *R = state + ((int64_t)n * Hv + h) * (int64_t)st;
+      const float an = a[(int64_t)n * Hv + h], bn = b[(int64_t)n * Hv + h];
+      for (int i = 0; i < dv; ++i)
+        o[((int64_t)n * Hv + h) * dv + i] =
+            row_token(R + (int64_t)i * dk, dk, an, bn,
+                      load_widened(v, ((int64_t)n * Hv + h) * dv + i, dtype), kq, qq);
+      if ((pos[n] + 1) % C == 0) { /* the chunk is complete: resynchronise */
+        for (int t = 0; t < C; ++t) {
+          for (int e = 0; e < dk; ++e)
+            kb[(int64_t)t * dk + e] = ck[(((int64_t)n * C + t) * Hk + hk) * dk + e];
+          for (int i = 0; i < dv; ++i)
+            vb[(int64_t)t * dv + i] = cv[(((int64_t)n * C + t) * Hv + h) * dv + i];
+          ab[t] = ca[((int64_t)n * C + t) * Hv + h];
+          bb[t] = cb[((int64_t)n * C + t) * Hv + h];
+        }
+        chunk_transition(kb, vb, ab, bb, C, dk, dv, A, B);
+        float *S = boundary + ((int64_t)n * Hv + h) * (int64_t)st;
+        boundary_step(S, A, B, Sn, dv, dk);
+        memcpy(S, Sn, sizeof(float) * st);
+        memcpy(R, Sn, sizeof(float) * st);
+        if (resync) memcpy(resync + ((int64_t)n * Hv + h) * (int64_t)st, Sn, sizeof(float) * st);
+      }
+    }
+  }
+  free(A); free(B); free(Sn); free(kb); free(vb);
+  return 0;
+}

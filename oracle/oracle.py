@@ -54,6 +54,10 @@ class Oracle:
         lib.oracle_decode_step.restype = I
         lib.oracle_backward.argtypes = [I] * 7 + [P] * 15 + [I]
         lib.oracle_backward.restype = I
+        lib.oracle_cpr2_scan.argtypes = [I] * 7 + [P] * 10 + [I]
+        lib.oracle_cpr2_scan.restype = I
+        lib.oracle_cpr2_decode_step.argtypes = [I] * 7 + [P] * 14
+        lib.oracle_cpr2_decode_step.restype = I
         lib.oracle_linear.argtypes = [I, I, I, I, I, P, P, P, I]
         lib.oracle_linear.restype = I
         lib.oracle_dot.argtypes = [P, P, I]
@@ -164,6 +168,56 @@ class Oracle:
             raise ValueError(f"oracle_backward rejected its arguments (rc={rc})")
         return out
 
+    def cpr2_scan(self, cu_seqlens, q, k, v, a, b, *, chunk, initial_state=None,
+                  nthreads=None):
+        """Two-level CPR over a packed batch. Returns (o [T, Hv, dv], chunk_states
+        [sum floor(T_n/C), Hv, dv, dk], final_state [N, Hv, dv, dk]), all float32."""
+        cu = _c(cu_seqlens, np.int32)
+        q, k, v = _c(q), _c(k), _c(v)
+        a, b = _c(a, np.float32), _c(b, np.float32)
+        dt = _dtype_code(q)
+        N = cu.size - 1
+        T, Hk, dk = k.shape
+        Hv, dv = v.shape[1], v.shape[2]
+        s0 = _c(initial_state, np.float32)
+        total_chunks = int(((cu[1:].astype(np.int64) - cu[:-1]) // chunk).sum())
+        o = np.zeros((T, Hv, dv), np.float32)
+        cs = np.zeros((total_chunks, Hv, dv, dk), np.float32)
+        fs = np.zeros((N, Hv, dv, dk), np.float32)
+        rc = self.lib.oracle_cpr2_scan(N, Hk, Hv, dk, dv, chunk, dt, _ptr(cu), _ptr(q), _ptr(k),
+                                       _ptr(v), _ptr(a), _ptr(b), _ptr(s0), _ptr(o), _ptr(cs),
+                                       _ptr(fs), nthreads or default_threads())
+        if rc != 0:
+            raise ValueError(f"oracle_cpr2_scan rejected its arguments (rc={rc})")
+        return o, cs, fs
+
+    def cpr2_decoder(self, N, Hk, Hv, dk, dv, *, chunk, initial_state=None):
+        """State of a two-level decode: running rows, boundary state and the token cache."""
+        st = np.zeros((N, Hv, dv, dk), np.float32) if initial_state is None else \
+            np.array(initial_state, np.float32, copy=True)
+        return {"state": st, "boundary": st.copy(),
+                "ck": np.zeros((N, chunk, Hk, dk), np.float32),
+                "cv": np.zeros((N, chunk, Hv, dv), np.float32),
+                "ca": np.zeros((N, chunk, Hv), np.float32),
+                "cb": np.zeros((N, chunk, Hv), np.float32), "chunk": chunk}
+
+    def cpr2_decode_step(self, dec, pos, q, k, v, a, b):
+        """One two-level decode step; updates ``dec`` in place; returns (o, resync)."""
+        pos = _c(pos, np.int32)
+        q, k, v = _c(q), _c(k), _c(v)
+        a, b = _c(a, np.float32), _c(b, np.float32)
+        N, Hk, dk = k.shape
+        Hv, dv = v.shape[1], v.shape[2]
+        o = np.zeros((N, Hv, dv), np.float32)
+        rs = np.zeros((N, Hv, dv, dk), np.float32)
+        rc = self.lib.oracle_cpr2_decode_step(
+            N, Hk, Hv, dk, dv, dec["chunk"], _dtype_code(q), _ptr(pos), _ptr(q), _ptr(k),
+            _ptr(v), _ptr(a), _ptr(b), _ptr(dec["state"]), _ptr(dec["boundary"]),
+            _ptr(dec["ck"]), _ptr(dec["cv"]), _ptr(dec["ca"]), _ptr(dec["cb"]), _ptr(o), _ptr(rs))
+        if rc != 0:
+            raise ValueError(f"oracle_cpr2_decode_step rejected its arguments (rc={rc})")
+        return o, rs
+
     def linear(self, x, w, *, nthreads=None):
         """Y = X W of the linear region: X [M, K], W [K, N] (float32, or bfloat16 as uint16
         bit patterns); every Y[m, n] is the contract dot of row m of X and column n of W.
@@ -264,3 +318,7 @@ def backward(*args, **kw):
 
 def linear(*args, **kw):
     return get().linear(*args, **kw)
+
+
+def cpr2_scan(*args, **kw):
+    return get().cpr2_scan(*args, **kw)

@@ -184,3 +184,64 @@ def backward(cu, q, k, v, a, b, do, s0, dsf, Hk):
                     out["dq"][t][hk][e] = aq
                     out["dk"][t][hk][e] = ak
     return out
+
+
+def cpr2_scan(cu, q, k, v, a, b, s0, chunk, Hk):
+    """Two-level CPR on tiny inputs (nested lists of binary32 Python floats): transitions by
+    the row update from unit rows (v = +0) and from zero rows, boundary states as fused
+    multiply-adds in ascending k from B, outputs from rows restarted at every boundary.
+    Returns (o [T][Hv][dv], chunk states [list of [Hv][dv][d]], final [N][Hv][dv][d])."""
+    T, Hv, dv, d = len(q), len(v[0]), len(v[0][0]), len(q[0][0])
+    G = Hv // Hk
+    N = len(cu) - 1
+    o = [[[0.0] * dv for _ in range(Hv)] for _ in range(T)]
+    final = [[None] * Hv for _ in range(N)]
+    states = []
+
+    def absorb(s, at, bt, vi, kt):
+        x = [mul(at, se) for se in s]
+        u = dot(x, kt)
+        delta = mul(bt, sub(vi, u))
+        return [fma(delta, ke, xe) for ke, xe in zip(kt, x)]
+
+    per_seq_states = []
+    for n in range(N):
+        bos, eos = cu[n], cu[n + 1]
+        seq_states = []
+        for h in range(Hv):
+            hk = h // G
+            S = [list(s0[n][h][i]) for i in range(dv)]
+            R = [list(r) for r in S]
+            hs = []
+            for t0 in range(bos, eos, chunk):
+                t1 = min(t0 + chunk, eos)
+                R = [list(r) for r in S]
+                for t in range(t0, t1):
+                    for i in range(dv):
+                        R[i], o[t][h][i] = token(R[i], a[t][h], b[t][h], v[t][h][i], k[t][hk],
+                                                 q[t][hk])
+                if t1 - t0 == chunk:
+                    A = [[1.0 if j == e else 0.0 for e in range(d)] for j in range(d)]
+                    B = [[0.0] * d for _ in range(dv)]
+                    for t in range(t0, t1):
+                        A = [absorb(A[j], a[t][h], b[t][h], 0.0, k[t][hk]) for j in range(d)]
+                        B = [absorb(B[i], a[t][h], b[t][h], v[t][h][i], k[t][hk])
+                             for i in range(dv)]
+                    Sn = []
+                    for i in range(dv):
+                        row = []
+                        for j in range(d):
+                            acc = B[i][j]
+                            for kk in range(d):
+                                acc = fma(S[i][kk], A[kk][j], acc)
+                            row.append(acc)
+                        Sn.append(row)
+                    S = Sn
+                    hs.append([list(r) for r in S])
+            final[n][h] = S if (eos - bos) % chunk == 0 else R
+            seq_states.append(hs)
+        per_seq_states.append(seq_states)
+    for n in range(N):
+        for c in range(len(per_seq_states[n][0]) if per_seq_states[n] else 0):
+            states.append([per_seq_states[n][h][c] for h in range(Hv)])
+    return o, states, final

@@ -9,7 +9,9 @@ oracle disagrees with what the mathematics or a hand derivation fixes:
   * an exact-rational binary32 emulator of the stated operation order (bitwise);
   * structural identities of the three cases (resume, chunk states, decode, packing);
   * for the linear region: the inner-product error bound against float64, the exact
-    emulator, one-hot rows and batch invariance.
+    emulator, one-hot rows and batch invariance;
+  * for the two-level CPR reading: the canonical bits when no chunk completes, float64,
+    the exact emulator, identity transitions, decode with resync equal to the scan.
 The same pins run against deliberately broken builds of the oracle (test_oracle_mutants),
 which must each fail at least one of them.
 """
@@ -422,6 +424,80 @@ def pin_bwd_chunk_invariance(orc):
             ref = r
         for key in GRAD_KEYS:
             assert same_bits(r[key], ref[key]), f"C={C} changed {key}"
+
+
+# ------------------------------------------------------------------------ two-level CPR
+
+def pin_cpr2_single_chunk_is_canonical(orc):
+    # with no full chunk, the rows never leave the recurrence from S0: same bits as the
+    # token-serial contract, outputs and final state alike
+    w, s0 = small_case(51, [37, 0, 5, 63], Hk=2, Hv=4, d=32, chunk=64, bf16=True, with_s0=True)
+    o, cs, fs = orc.cpr2_scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=64, initial_state=s0)
+    ro, _, rfs = orc.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=64, initial_state=s0,
+                          want_chunk_states=True, want_final_state=True)
+    assert cs.shape[0] == 0, "no chunk state expected"
+    assert same_bits(o, ro) and same_bits(fs, rfs), "single partial chunk differs from canonical"
+
+
+def pin_cpr2_vs_f64(orc):
+    # the two-level reading is the same mathematics: within the f64 tolerance
+    for seed, lengths, Hk, Hv, d, C, bf16 in [(52, [50, 16, 7], 1, 2, 32, 16, False),
+                                              (53, [64, 33], 2, 4, 16, 8, True),
+                                              (54, [96], 1, 1, 64, 32, True)]:
+        w, s0 = small_case(seed, lengths, Hk=Hk, Hv=Hv, d=d, chunk=C, bf16=bf16, with_s0=True)
+        o, cs, fs = orc.cpr2_scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=C,
+                                  initial_state=s0)
+        o64, cs64, fs64 = brute_f64.scan_f64(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, C, s0)
+        _check_f64(o, cs, fs, o64, cs64, fs64, w.cu_seqlens, f"cpr2 case {seed}")
+
+
+def pin_cpr2_exact_emulator(orc):
+    # 3 rows, C = 2, sequences of 5 (a tail) and 4 (ends on a boundary), two value heads
+    w, s0 = small_case(55, [5, 4], Hk=1, Hv=2, d=16, chunk=2, with_s0=True)
+    w.v = W.make_packed("v3", [5, 4], Hk=2, Hv=2, d=3, chunk=2, bf16=False, seed=55).v
+    s0 = (0.3 * np.random.default_rng(55).standard_normal((2, 2, 3, 16))).astype(np.float32)
+    o, cs, fs = orc.cpr2_scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=2, initial_state=s0)
+    tl = lambda x: np.asarray(x, np.float64).tolist()  # noqa: E731
+    eo, ecs, efs = exact_fp32.cpr2_scan([int(c) for c in w.cu_seqlens], tl(w.q), tl(w.k),
+                                        tl(w.v), tl(w.a), tl(w.b), tl(s0), 2, Hk=1)
+    assert same_bits(o, np.array(eo, np.float32)), "cpr2 outputs"
+    assert same_bits(cs, np.array(ecs, np.float32)), "cpr2 chunk states"
+    assert same_bits(fs, np.array(efs, np.float32)), "cpr2 final states"
+
+
+def pin_cpr2_identity_transition(orc):
+    # a = 1, b = 0: every transition is exactly the identity and B = 0, so every boundary
+    # state equals S0 and every output is the contract dot of S0's row with q
+    w, s0 = small_case(56, [24, 16], Hk=1, Hv=2, d=32, chunk=8, with_s0=True)
+    w.a[:] = 1.0
+    w.b[:] = 0.0
+    s0[s0 == 0] = 0.5
+    o, cs, fs = orc.cpr2_scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=8, initial_state=s0)
+    ro, _, _ = orc.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=8, initial_state=s0,
+                        want_chunk_states=True, want_final_state=True)
+    assert same_bits(o, ro), "outputs with identity transitions"
+    want = np.concatenate([np.repeat(s0[0:1], 3, 0), np.repeat(s0[1:2], 2, 0)])
+    assert np.array_equal(cs, want) and np.array_equal(fs, s0), "boundary states moved"
+
+
+def pin_cpr2_decode_equals_scan(orc):
+    # token-by-token decode with resync from the cache gives the scan's bits: outputs, every
+    # resync checkpoint, and the final state (sequences ending on and off a boundary)
+    for T in (24, 27):
+        w, s0 = small_case(57, [T, T], Hk=2, Hv=4, d=32, chunk=8, bf16=True, with_s0=True)
+        o, cs, fs = orc.cpr2_scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=8,
+                                  initial_state=s0)
+        _, steps = W.split_for_decode(w, 0)
+        dec = orc.cpr2_decoder(2, 2, 4, 32, 32, chunk=8, initial_state=s0)
+        c = 0
+        for t in range(T):
+            od, rs = orc.cpr2_decode_step(dec, steps["pos"][t], steps["q"][t], steps["k"][t],
+                                          steps["v"][t], steps["a"][t], steps["b"][t])
+            assert same_bits(od, o.reshape(2, T, 4, 32)[:, t]), f"decode o at t={t}"
+            if (t + 1) % 8 == 0:
+                assert same_bits(rs[0], cs[c]) and same_bits(rs[1], cs[T // 8 + c]), "resync"
+                c += 1
+        assert same_bits(dec["state"], fs), f"decode final state T={T}"
 
 
 # --------------------------------------------------------------------------- linear region

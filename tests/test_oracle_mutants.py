@@ -79,6 +79,15 @@ MUTANTS = {
       }""")],
     "bwd_final_state_gradient_ignored": [("sh[(int64_t)i * dk + e] = J->dSf ? J->dSf[",
                                           "sh[(int64_t)i * dk + e] = J->dSf ? 0.0f * J->dSf[")],
+    # two-level CPR
+    "cpr2_B_added_last": [("      float acc = B[(int64_t)i * dk + j];\n      for (int kk = 0; kk < dk; ++kk) acc = fmaf(S[(int64_t)i * dk + kk], A[(int64_t)kk * dk + j], acc);",
+                           "      float acc = 0.0f;\n      for (int kk = 0; kk < dk; ++kk) acc = fmaf(S[(int64_t)i * dk + kk], A[(int64_t)kk * dk + j], acc);\n      acc = acc + B[(int64_t)i * dk + j];")],
+    "cpr2_transition_absorbs_v": [("row_absorb(A + (int64_t)j * dk, dk, a[t], b[t], 0.0f, kt);",
+                                   "row_absorb(A + (int64_t)j * dk, dk, a[t], b[t], v[(int64_t)t * dv + (j % dv)], kt);")],
+    "cpr2_outputs_from_next_boundary": [("    /* outputs: the rows restart from the boundary state S */\n    memcpy(R, S, sizeof(float) * st);",
+                                         "    /* outputs: the rows restart from the boundary state S */\n    memcpy(R, S, sizeof(float) * st);\n    if (n_tok == C && c > 0) { chunk_transition(kb, vb, ab, bb, C, dk, dv, A, B); boundary_step(S, A, B, R, dv, dk); }")],
+    "cpr2_final_always_recurrent": [("const float *fin = (Tn % C == 0) ? S : R;", "const float *fin = R;")],
+    "cpr2_decode_cache_slot_shifted": [("const int slot = pos[n] % C;", "const int slot = (pos[n] + 1) % C;")],
     # linear region
     "linear_w_transposed": [("col[k] = load_widened(J->w, (int64_t)k * J->N + n, J->wdtype);",
                              "col[k] = load_widened(J->w, ((int64_t)n * J->K + k) % "
@@ -105,7 +114,10 @@ def test_mutant_is_caught(name, tmp_path):
     orc = O.Oracle(lib)
     # backward mutants are most quickly caught by the backward pins: try those first
     def family(n):
-        return "bwd" if "bwd" in n else ("linear" if "linear" in n else "fwd")
+        for f in ("bwd", "linear", "cpr2"):
+            if f in n:
+                return f
+        return "fwd"
 
     pins = sorted(oracle_pins.ALL_PINS,
                   key=lambda p: (family(name) != family(p.__name__), p.__name__))
