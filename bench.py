@@ -7,11 +7,13 @@ C = 64, bf16 q/k/v, fp32 a/b/state/o. `value` is tokens/s of that step with inpu
 in HBM. The same line also reports, under "cases", engine_prefill tokens/s (64 varlen
 sequences, 262144 tokens, 16 q/k / 32 v heads), the engine_decode step time (256
 sequences after a 1000-token prefill, 512 steps), the backward (gdn_cpr_trainer_bwd) on
-the trainer workload, the long-context runs and the linear region (a 16384 x 4096 x 4096
-batch-invariant matrix product on the matrix cores), each with its
+the trainer workload, the long-context runs, the linear region (a 16384 x 4096 x 4096
+batch-invariant matrix product on the matrix cores) and the two-level reading of CPR
+(chunk transitions, a boundary sweep on the matrix cores, outputs), each with its
 fraction of the relevant peak, plus the CPU oracle timed on the host as a baseline.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cases all|main|bwd|linear]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--cases all|main|bwd|linear|cpr2]
                        [--no-cpu-baseline]
 """
 
@@ -336,6 +338,116 @@ def bench_linear(steps, warmup, M=16384, N=4096, K=4096):
             "hbm": hbm(nbytes, ms)}
 
 
+def cpr2_flops(w):
+    """Flops of one two-level call: each full chunk's transition runs d_k + d_v rows through
+    the row update (5 d_k + 1 flop per row and token), its boundary step is a d_v x d_k x
+    d_k multiply-add (on the matrix units), and the outputs repeat the recurrence from the
+    boundary states (7 d_k per row and token, as in the one-level scan)."""
+    dk, dv, C, Hv = w.d_k, w.d_v, w.chunk, w.num_v_heads
+    trans = w.total_chunks * Hv * (dk + dv) * C * (5 * dk + 1)
+    boundary = w.total_chunks * Hv * dv * dk * dk * 2
+    outputs = flops_per_token_head(dk, dv) * w.total_tokens * Hv
+    return trans, boundary, outputs
+
+
+def bench_cpr2(steps, warmup):
+    """The two-level reading of CPR (gdn_cpr2_*): trainer_fwd and prefill on the trainer
+    workload, decode steps on the engine-decode workload from a chunk-aligned prefix."""
+    import torch
+    from bitwise_consistent_linear_amd import api
+    from bitwise_consistent_linear_amd import workloads as W
+    w = W.trainer_fwd()
+    log("cpr2: two-level trainer_fwd and prefill on the trainer workload")
+    cu, q, k, v, a, b = (up(x) for x in (w.cu_seqlens, w.q, w.k, w.v, w.a, w.b))
+    tc = w.total_chunks
+    T, Hv, dv, dk = w.total_tokens, w.num_v_heads, w.d_v, w.d_k
+    o = torch.empty((T, Hv, dv), dtype=torch.float32, device="cuda")
+    cs = torch.empty((tc, Hv, dv, dk), dtype=torch.float32, device="cuda")
+    fs = torch.empty((w.num_seqs, Hv, dv, dk), dtype=torch.float32, device="cuda")
+    shape = api.GdnShape(w.num_seqs, w.num_qk_heads, Hv, dk, dv, w.chunk, api.GDN_DTYPE_BF16)
+    need = api.cpr2_workspace_bytes(shape, T, tc, False)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    wall_t, per_t = timed(lambda: api.cpr2_trainer_fwd(cu, q, k, v, a, b, chunk=w.chunk, o=o,
+                                                       chunk_states=cs, total_chunks=tc,
+                                                       workspace=ws), steps, warmup)
+    wall_p, per_p = timed(lambda: api.cpr2_prefill(cu, q, k, v, a, b, chunk=w.chunk, o=o,
+                                                   final_state=fs, total_chunks=tc,
+                                                   workspace=ws), steps, warmup)
+    mt, mp = sum(per_t) / len(per_t), sum(per_p) / len(per_p)
+    trans, boundary, outputs = cpr2_flops(w)
+    del q, k, v, o, cs, fs, ws
+    torch.cuda.empty_cache()
+    dec = bench_cpr2_decode()
+    roof = roofline_alu(trans + boundary + outputs, mt)
+    roof["scope"] = ("whole call (plan, transitions, boundary sweep, outputs); the boundary "
+                     "sweep's flops run on the matrix units")
+    return {"workload": "two-level CPR on the trainer_fwd workload (4 x 4096 tokens, 16 heads, "
+                        "d=128, C=64, bf16 q/k/v): o, the 256 chunk states (trainer) or the "
+                        "final states (prefill)",
+            "trainer_fwd_tokens_per_s": round(T / (wall_t / steps), 1),
+            "trainer_fwd_kernel_ms": round(mt, 4),
+            "prefill_tokens_per_s": round(T / (wall_p / steps), 1),
+            "prefill_kernel_ms": round(mp, 4),
+            "flops": {"transitions": trans, "boundary_sweep": boundary, "outputs": outputs},
+            "workspace_bytes": int(need), "steps": steps, "roofline": roof,
+            "decode": dec}
+
+
+def bench_cpr2_decode(prefix=960, nsteps=504, warmup_steps=8):
+    """Two-level decode on the engine-decode workload: a two-level prefill of a chunk-aligned
+    prefix (so state = boundary and the token cache is empty), then steps timed one by one;
+    every 64th step rebuilds the chunk transition from the cache and sets the boundary."""
+    import torch
+    from bitwise_consistent_linear_amd import api
+    from bitwise_consistent_linear_amd import workloads as W
+    w = W.engine_decode()
+    N, Hk, Hv, dk, dv, C = w.num_seqs, w.num_qk_heads, w.num_v_heads, w.d_k, w.d_v, w.chunk
+    log(f"cpr2 decode: N={N}, two-level prefill of {prefix} tokens, {nsteps} decode steps")
+    pre, steps = W.split_for_decode(w, prefix)
+    dp = {key: up(getattr(pre, key)) for key in ("q", "k", "v", "a", "b")}
+    _, fs = api.cpr2_prefill(up(pre.cu_seqlens), dp["q"], dp["k"], dp["v"], dp["a"], dp["b"],
+                             chunk=C, total_chunks=pre.total_chunks)
+    del dp
+    torch.cuda.empty_cache()
+    dec = api.Cpr2Decoder(N, Hk, Hv, dk, dv, C, torch.bfloat16, "cuda", initial_state=fs)
+    del fs
+    ds = {key: up(x) for key, x in steps.items()}
+    rs = torch.empty_like(dec.state)
+    o = torch.empty((N, Hv, dv), dtype=torch.float32, device="cuda")
+    it = iter(range(ds["q"].shape[0]))
+
+    def step():
+        s = next(it)
+        dec.step(ds["pos"][s], ds["q"][s], ds["k"][s], ds["v"][s], ds["a"][s], ds["b"][s],
+                 o=o, resync_states=rs)
+
+    wall, per = timed(step, nsteps, warmup_steps)
+    ms = sum(per) / len(per)
+    el = 2
+    state = N * Hv * dv * dk * 4
+    tok = N * (Hk * dk * el + Hv * dv * el + Hv * 8)
+    # every step: the running rows (decode_step_bytes without its resync share) and the token
+    # into the cache; every C steps: the cache read back, A_c and B_c written and read, the
+    # boundary read and the state, boundary and resync written
+    trans = N * Hv * (dk + dv) * dk * 4
+    per_step = (decode_step_bytes(N, Hk, Hv, dk, dv, el, C) - state / C + tok
+                + (C * tok + 2 * trans + 4 * state) / C)
+    gbs = per_step / (ms * 1e-3) / 1e9
+    boundary_steps = [p for s, p in enumerate(per) if (prefix + warmup_steps + s + 1) % C == 0]
+    other = [p for s, p in enumerate(per) if (prefix + warmup_steps + s + 1) % C != 0]
+    del dec, ds
+    return {"workload": f"engine_decode workload (256 sequences, 16 q/k / 32 v heads, d=128, "
+                        f"C=64), two-level prefill of {prefix} tokens, then {nsteps} steps "
+                        f"({warmup_steps} untimed)",
+            "us_per_step_kernel": round(ms * 1e3, 2),
+            "us_per_step_wall": round(wall / nsteps * 1e6, 2),
+            "us_boundary_step": round(sum(boundary_steps) / max(1, len(boundary_steps)) * 1e3, 2),
+            "us_other_step": round(sum(other) / max(1, len(other)) * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "algorithmic_bytes_per_step": int(per_step)}
+
+
 def bench_decode_after_prefill(w, prefix, nsteps, warmup_steps, label):
     """Prefill `prefix` tokens of every sequence, then time decode steps one by one."""
     import torch
@@ -457,9 +569,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cases", choices=["all", "main", "bwd", "linear"], default="all",
-                    help="all: every case; main: trainer_fwd only; bwd / linear: trainer_fwd "
-                         "and the backward / the linear region (for profiling)")
+    ap.add_argument("--cases", choices=["all", "main", "bwd", "linear", "cpr2"], default="all",
+                    help="all: every case; main: trainer_fwd only; bwd / linear / cpr2: "
+                         "trainer_fwd and the backward / the linear region / the two-level "
+                         "reading (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (untimed), the known-size "
@@ -532,11 +645,15 @@ def main():
         torch.cuda.empty_cache()
         cases["linear"] = bench_linear(max(3, args.steps // 4), 1)
         torch.cuda.empty_cache()
+        cases["two_level"] = bench_cpr2(max(3, args.steps // 4), 1)
+        torch.cuda.empty_cache()
         out["cases"] = cases
     elif args.cases == "bwd":
         out["cases"] = {"trainer_bwd": bench_trainer_bwd(max(3, args.steps // 4), 1, kernel_ms)}
     elif args.cases == "linear":
         out["cases"] = {"linear": bench_linear(max(3, args.steps // 4), 1)}
+    elif args.cases == "cpr2":
+        out["cases"] = {"two_level": bench_cpr2(max(3, args.steps // 4), 1)}
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the trainer_fwd workload")
         out["cpu_baseline"] = cpu_baseline(w)

@@ -77,6 +77,24 @@ def lib():
                                           P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.gdn_linear_fwd.restype = I32
         L.gdn_linear_fwd.argtypes = [ctypes.POINTER(GdnLinearShape), ctypes.c_char_p, P, P, P, P]
+        L.gdn_cpr2_contract_string.restype = I32
+        L.gdn_cpr2_contract_string.argtypes = [I32, I32, ctypes.c_char_p, ctypes.c_size_t,
+                                               ctypes.POINTER(ctypes.c_size_t)]
+        L.gdn_cpr2_contract_identity.restype = I32
+        L.gdn_cpr2_contract_identity.argtypes = [I32, I32, ctypes.c_char_p]
+        L.gdn_cpr2_workspace.restype = I32
+        L.gdn_cpr2_workspace.argtypes = [ctypes.POINTER(GdnShape), I64, I64, I32,
+                                         ctypes.POINTER(ctypes.c_size_t)]
+        L.gdn_cpr2_trainer_fwd.restype = I32
+        L.gdn_cpr2_trainer_fwd.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_char_p, P, I64,
+                                           P, P, P, P, P, P, P, P, I64, P, ctypes.c_size_t, P]
+        L.gdn_cpr2_prefill.restype = I32
+        L.gdn_cpr2_prefill.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_char_p, P, I64,
+                                       P, P, P, P, P, P, P, P, I64, P, ctypes.c_size_t, P]
+        L.gdn_cpr2_decode_step.restype = I32
+        L.gdn_cpr2_decode_step.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_char_p, P,
+                                           P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                           ctypes.c_size_t, P]
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_last_error.argtypes = []
         _lib = L
@@ -356,3 +374,139 @@ def linear_fwd(x, w, *, y=None, identity=None, stream=None):
     _check(lib().gdn_linear_fwd(ctypes.byref(shape), ident, _ptr(x), _ptr(w), _ptr(y),
                                 _stream(stream)))
     return y
+
+
+# ---------------------------------------------------------------- two-level reading of CPR
+
+def cpr2_contract_string(chunk: int, d_k: int) -> str:
+    n = ctypes.c_size_t(0)
+    st = lib().gdn_cpr2_contract_string(chunk, d_k, None, 0, ctypes.byref(n))
+    if st not in (GDN_OK, GDN_E_SHAPE):
+        _check(st)
+    buf = ctypes.create_string_buffer(n.value + 1)
+    _check(lib().gdn_cpr2_contract_string(chunk, d_k, buf, n.value + 1, ctypes.byref(n)))
+    return buf.value.decode()
+
+
+@lru_cache(maxsize=None)
+def cpr2_contract_identity(chunk: int, d_k: int) -> bytes:
+    out = ctypes.create_string_buffer(32)
+    _check(lib().gdn_cpr2_contract_identity(chunk, d_k, out))
+    return out.raw
+
+
+def cpr2_workspace_bytes(shape: GdnShape, total_tokens: int, total_chunks: int,
+                         decode: bool) -> int:
+    """gdn_cpr2_workspace: device bytes a two-level call needs for these sizes."""
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_cpr2_workspace(ctypes.byref(shape), total_tokens, total_chunks,
+                                    1 if decode else 0, ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(workspace, need, device):
+    torch = _torch()
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _need(workspace, "workspace", (torch.uint8,), 1)
+    return workspace
+
+
+def _cpr2_batch(prefill_case, cu_seqlens, q, k, v, a, b, chunk, initial_state, o, out_state,
+                total_chunks, workspace, identity, stream):
+    torch = _torch()
+    dt = _qkv(q, k, v)
+    _need(cu_seqlens, "cu_seqlens", (torch.int32,), 1)
+    N = cu_seqlens.shape[0] - 1
+    T, Hv, dv, dk = q.shape[0], v.shape[1], v.shape[2], q.shape[2]
+    _ab(a, b, T, Hv)
+    _state(initial_state, "initial_state", N, Hv, dv, dk)
+    if total_chunks is None:
+        total_chunks = count_chunks(cu_seqlens, chunk)
+    if o is None:
+        o = torch.empty((T, Hv, dv), dtype=torch.float32, device=q.device)
+    _need(o, "o", (torch.float32,), 3)
+    if prefill_case:
+        if out_state is None:
+            out_state = torch.empty((N, Hv, dv, dk), dtype=torch.float32, device=q.device)
+        _state(out_state, "final_state", N, Hv, dv, dk)
+    else:
+        if out_state is None:
+            out_state = torch.empty((total_chunks, Hv, dv, dk), dtype=torch.float32,
+                                    device=q.device)
+        _need(out_state, "chunk_states", (torch.float32,), 4)
+        if out_state.shape[0] < total_chunks:
+            raise ValueError("chunk_states has fewer rows than total_chunks")
+    shape = _shape(N, q, v, chunk, dt)
+    workspace = _workspace(workspace, cpr2_workspace_bytes(shape, T, total_chunks, False),
+                           q.device)
+    ident = identity if identity is not None else cpr2_contract_identity(chunk, dk)
+    fn = lib().gdn_cpr2_prefill if prefill_case else lib().gdn_cpr2_trainer_fwd
+    state_ptr = _ptr(out_state) if (prefill_case or total_chunks) else None
+    _check(fn(ctypes.byref(shape), ident, _ptr(cu_seqlens), T, _ptr(q), _ptr(k), _ptr(v),
+              _ptr(a), _ptr(b), _ptr(initial_state), _ptr(o), state_ptr, total_chunks,
+              _ptr(workspace), workspace.numel(), _stream(stream)))
+    return o, out_state
+
+
+def cpr2_trainer_fwd(cu_seqlens, q, k, v, a, b, *, chunk, initial_state=None, o=None,
+                     chunk_states=None, total_chunks=None, workspace=None, identity=None,
+                     stream=None):
+    """gdn_cpr2_trainer_fwd. Returns (o [T, Hv, dv], chunk_states [total_chunks, Hv, dv, dk])."""
+    return _cpr2_batch(False, cu_seqlens, q, k, v, a, b, chunk, initial_state, o,
+                       chunk_states, total_chunks, workspace, identity, stream)
+
+
+def cpr2_prefill(cu_seqlens, q, k, v, a, b, *, chunk, initial_state=None, o=None,
+                 final_state=None, total_chunks=None, workspace=None, identity=None,
+                 stream=None):
+    """gdn_cpr2_prefill. Returns (o [T, Hv, dv], final_state [N, Hv, dv, dk])."""
+    return _cpr2_batch(True, cu_seqlens, q, k, v, a, b, chunk, initial_state, o,
+                       final_state, total_chunks, workspace, identity, stream)
+
+
+class Cpr2Decoder:
+    """The per-sequence buffers of gdn_cpr2_decode_step for N slots: running state,
+    boundary state, the C-token cache and the workspace, all on one GPU. ``step`` applies
+    one token to every slot whose pos is >= 0 and returns o [N, Hv, dv]."""
+
+    def __init__(self, N, Hk, Hv, dk, dv, chunk, dtype, device, initial_state=None):
+        torch = _torch()
+        self.N, self.Hk, self.Hv, self.dk, self.dv, self.chunk = N, Hk, Hv, dk, dv, chunk
+        self.dtype = dtype
+        f32 = dict(dtype=torch.float32, device=device)
+        self.state = torch.zeros((N, Hv, dv, dk), **f32)
+        if initial_state is not None:
+            self.state.copy_(initial_state)
+        self.boundary = self.state.clone()
+        self.cache_k = torch.zeros((N, chunk, Hk, dk), dtype=dtype, device=device)
+        self.cache_v = torch.zeros((N, chunk, Hv, dv), dtype=dtype, device=device)
+        self.cache_a = torch.zeros((N, chunk, Hv), **f32)
+        self.cache_b = torch.zeros((N, chunk, Hv), **f32)
+        code = GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32
+        self.shape = GdnShape(N, Hk, Hv, dk, dv, chunk, code)
+        self.workspace = _workspace(None, cpr2_workspace_bytes(self.shape, 0, 0, True), device)
+
+    def step(self, pos, q, k, v, a, b, *, o=None, resync_states=None, identity=None,
+             stream=None):
+        torch = _torch()
+        _qkv(q, k, v)
+        _need(pos, "pos", (torch.int32,), 1)
+        if (pos.shape[0], q.shape[0], v.shape[0]) != (self.N,) * 3 or q.dtype != self.dtype:
+            raise ValueError("pos, q, k and v must have one row per slot, in the decoder's dtype")
+        if tuple(q.shape[1:]) != (self.Hk, self.dk) or tuple(v.shape[1:]) != (self.Hv, self.dv):
+            raise ValueError("q, k or v does not match the decoder's heads and widths")
+        _ab(a, b, self.N, self.Hv)
+        _state(resync_states, "resync_states", self.N, self.Hv, self.dv, self.dk)
+        if o is None:
+            o = torch.empty((self.N, self.Hv, self.dv), dtype=torch.float32, device=q.device)
+        _need(o, "o", (torch.float32,), 3)
+        ident = identity if identity is not None else cpr2_contract_identity(self.chunk,
+                                                                             self.dk)
+        _check(lib().gdn_cpr2_decode_step(
+            ctypes.byref(self.shape), ident, _ptr(pos), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+            _ptr(b), _ptr(self.state), _ptr(self.boundary), _ptr(self.cache_k),
+            _ptr(self.cache_v), _ptr(self.cache_a), _ptr(self.cache_b), _ptr(o),
+            _ptr(resync_states), _ptr(self.workspace), self.workspace.numel(),
+            _stream(stream)))
+        return o

@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn_cpr.so")
 
-SOURCES = ["cpr_kernels.hip", "cpr_backward.hip", "linear.hip", "api.cpp", "contract.cpp"]
+SOURCES = ["cpr_kernels.hip", "cpr_backward.hip", "cpr2.hip", "linear.hip", "api.cpp",
+           "contract.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950",

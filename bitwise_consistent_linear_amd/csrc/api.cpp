@@ -5,10 +5,13 @@
 // (IsoExec, aihirek.info, section on the contract and common model; agentlenshq.com,
 // section on contract structure: claims and identities).
 
+#include <algorithm>
+#include <array>
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 
@@ -93,7 +96,8 @@ int decode_lanes() {
   return 16;
 }
 
-gdn_status_t check_shape(const char *fn, const gdn_shape_t *sh, const uint8_t *identity) {
+gdn_status_t check_shape(const char *fn, const gdn_shape_t *sh, const uint8_t *identity,
+                         bool two_level = false) {
   if (!sh) return fail(GDN_E_NULL, std::string(fn) + ": shape is NULL");
   if (!identity) return fail(GDN_E_NULL, std::string(fn) + ": expected_identity is NULL");
   if (sh->num_seqs < 0 || sh->num_qk_heads < 1 || sh->num_v_heads < 1)
@@ -102,6 +106,8 @@ gdn_status_t check_shape(const char *fn, const gdn_shape_t *sh, const uint8_t *i
     return fail(GDN_E_SHAPE, std::string(fn) + ": num_v_heads must be a multiple of num_qk_heads");
   if (!admitted_dk(sh->d_k))
     return fail(GDN_E_UNSUPPORTED, std::string(fn) + ": d_k must be 16, 32, 64 or 128");
+  if (two_level && !cpr2_dk_admitted(sh->d_k))
+    return fail(GDN_E_UNSUPPORTED, std::string(fn) + ": the two-level reading admits d_k 32, 64 or 128");
   if (sh->d_v < 1 || sh->d_v > 1024)
     return fail(GDN_E_UNSUPPORTED, std::string(fn) + ": d_v must be in [1, 1024]");
   if (!admitted_chunk(sh->chunk))
@@ -109,7 +115,8 @@ gdn_status_t check_shape(const char *fn, const gdn_shape_t *sh, const uint8_t *i
   if (sh->qkv_dtype != GDN_DTYPE_F32 && sh->qkv_dtype != GDN_DTYPE_BF16)
     return fail(GDN_E_UNSUPPORTED, std::string(fn) + ": qkv_dtype must be F32 or BF16");
   uint8_t mine[32];
-  const std::string text = contract_text(sh->chunk, sh->d_k);
+  const std::string text = two_level ? cpr2_contract_text(sh->chunk, sh->d_k)
+                                     : contract_text(sh->chunk, sh->d_k);
   sha256(reinterpret_cast<const uint8_t *>(text.data()), text.size(), mine);
   if (std::memcmp(mine, identity, 32) != 0)
     return fail(GDN_E_IDENTITY, std::string(fn) + ": expected_identity differs from this "
@@ -138,8 +145,8 @@ gdn_status_t check_state(const char *fn, const char *name, const float *p) {
 gdn_status_t scan_common(const char *fn, const gdn_shape_t *sh, const uint8_t *identity,
                          const int32_t *cu, int64_t T, const void *q, const void *k,
                          const void *v, const float *a, const float *b, const float *s0,
-                         float *o, ScanArgs &args) {
-  gdn_status_t st = check_shape(fn, sh, identity);
+                         float *o, ScanArgs &args, bool two_level = false) {
+  gdn_status_t st = check_shape(fn, sh, identity, two_level);
   if (st != GDN_OK) return st;
   if (T < 0 || T > kMaxInt32)
     return fail(GDN_E_SHAPE, std::string(fn) + ": total_tokens must be in [0, 2^31)");
@@ -397,6 +404,193 @@ GDN_EXPORT gdn_status_t gdn_cpr_trainer_bwd(
   return gdn::ok();
 }
 
+// ------------------------------------------------------------------- two-level reading
+
+static gdn_status_t cpr2_claims(const char *fn, const gdn_shape_t *sh, int64_t T,
+                                int64_t total_chunks) {
+  if (!sh) return gdn::fail(GDN_E_NULL, std::string(fn) + ": shape is NULL");
+  if (T < 0 || T > gdn::kMaxInt32)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": total_tokens must be in [0, 2^31)");
+  if (sh->chunk < 1 || total_chunks < 0 || total_chunks > T / sh->chunk)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": total_chunks must be in [0, total_tokens / chunk]");
+  return GDN_OK;
+}
+
+GDN_EXPORT gdn_status_t gdn_cpr2_workspace(const gdn_shape_t *shape, int64_t total_tokens,
+                                           int64_t total_chunks, int32_t decode, size_t *bytes) {
+  const char *fn = "gdn_cpr2_workspace";
+  if (!bytes) return gdn::fail(GDN_E_NULL, std::string(fn) + ": bytes is NULL");
+  gdn_status_t st = cpr2_claims(fn, shape, decode ? 0 : total_tokens, decode ? 0 : total_chunks);
+  if (st != GDN_OK) return st;
+  if (shape->num_seqs < 0 || shape->num_v_heads < 1 || !gdn::cpr2_dk_admitted(shape->d_k) ||
+      shape->d_v < 1 || shape->d_v > 1024)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": bad num_seqs, num_v_heads, d_k or d_v");
+  *bytes = (size_t)gdn::cpr2_layout(shape->num_seqs, shape->num_v_heads, shape->d_k, shape->d_v,
+                                    decode ? 0 : total_chunks, decode != 0, !decode).total;
+  return gdn::ok();
+}
+
+static gdn_status_t cpr2_scan(const char *fn, const gdn_shape_t *shape,
+                              const uint8_t *expected_identity, const int32_t *cu_seqlens,
+                              int64_t total_tokens, const void *q, const void *k, const void *v,
+                              const float *a, const float *b, const float *initial_state, float *o,
+                              float *chunk_states, float *final_state, int64_t total_chunks,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  gdn::ScanArgs fwd;
+  gdn_status_t st = gdn::scan_common(fn, shape, expected_identity, cu_seqlens, total_tokens, q,
+                                     k, v, a, b, initial_state, o, fwd, true);
+  if (st != GDN_OK) return st;
+  if ((st = cpr2_claims(fn, shape, total_tokens, total_chunks)) != GDN_OK) return st;
+  if ((st = gdn::check_state(fn, "chunk_states", chunk_states)) != GDN_OK) return st;
+  if ((st = gdn::check_state(fn, "final_state", final_state)) != GDN_OK) return st;
+  const bool trainer = final_state == nullptr;
+  if (final_state && final_state == initial_state)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": final_state must not alias initial_state");
+  if (trainer && total_chunks > 0 && !chunk_states)
+    return gdn::fail(GDN_E_NULL, std::string(fn) + ": chunk_states is required");
+  const gdn::Cpr2Layout ws = gdn::cpr2_layout(shape->num_seqs, shape->num_v_heads, shape->d_k,
+                                              shape->d_v, total_chunks, false, !trainer);
+  if (!workspace) return gdn::fail(GDN_E_NULL, std::string(fn) + ": workspace is NULL");
+  if (!gdn::aligned(workspace, 256))
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": workspace must be 256-byte aligned");
+  if ((int64_t)workspace_bytes < ws.total)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": workspace smaller than gdn_cpr2_workspace reports");
+  if (total_chunks + shape->num_seqs > gdn::kMaxInt32)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": too many chunks");
+  gdn::Cpr2Args args{};
+  args.num_seqs = shape->num_seqs;
+  args.num_qk_heads = shape->num_qk_heads;
+  args.num_v_heads = shape->num_v_heads;
+  args.d_k = shape->d_k;
+  args.d_v = shape->d_v;
+  args.chunk = shape->chunk;
+  args.bf16 = shape->qkv_dtype == GDN_DTYPE_BF16;
+  args.slots_max = (int32_t)(total_chunks + shape->num_seqs);
+  args.total_tokens = total_tokens;
+  args.total_chunks = total_chunks;
+  args.cu_seqlens = cu_seqlens;
+  args.q = q;
+  args.k = k;
+  args.v = v;
+  args.a = a;
+  args.b = b;
+  args.initial_state = initial_state;
+  args.o = o;
+  char *w = static_cast<char *>(workspace);
+  args.plan = reinterpret_cast<int32_t *>(w + ws.plan_off);
+  args.plan_cbase = reinterpret_cast<int32_t *>(w + ws.cbase_off);
+  args.trans_a = reinterpret_cast<float *>(w + ws.ta_off);
+  args.trans_b = reinterpret_cast<float *>(w + ws.tb_off);
+  args.chunk_states = trainer ? chunk_states : reinterpret_cast<float *>(w + ws.cs_off);
+  args.final_state = final_state;
+  if (shape->num_seqs == 0) return gdn::ok();
+  if (gdn::cpr2_max_grid(args) > gdn::kMaxInt32)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": grid too large");
+  const hipError_t e = gdn::launch_cpr2_scan(args, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return gdn::fail(GDN_E_DEVICE, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
+  return gdn::ok();
+}
+
+GDN_EXPORT gdn_status_t gdn_cpr2_trainer_fwd(
+    const gdn_shape_t *shape, const uint8_t *expected_identity, const int32_t *cu_seqlens,
+    int64_t total_tokens, const void *q, const void *k, const void *v, const float *a,
+    const float *b, const float *initial_state, float *o, float *chunk_states,
+    int64_t total_chunks, void *workspace, size_t workspace_bytes, void *stream) {
+  return cpr2_scan("gdn_cpr2_trainer_fwd", shape, expected_identity, cu_seqlens, total_tokens, q,
+                   k, v, a, b, initial_state, o, chunk_states, nullptr, total_chunks, workspace,
+                   workspace_bytes, stream);
+}
+
+GDN_EXPORT gdn_status_t gdn_cpr2_prefill(
+    const gdn_shape_t *shape, const uint8_t *expected_identity, const int32_t *cu_seqlens,
+    int64_t total_tokens, const void *q, const void *k, const void *v, const float *a,
+    const float *b, const float *initial_state, float *o, float *final_state,
+    int64_t total_chunks, void *workspace, size_t workspace_bytes, void *stream) {
+  const char *fn = "gdn_cpr2_prefill";
+  if (!final_state) return gdn::fail(GDN_E_NULL, std::string(fn) + ": final_state is required");
+  return cpr2_scan(fn, shape, expected_identity, cu_seqlens, total_tokens, q, k, v, a, b,
+                   initial_state, o, nullptr, final_state, total_chunks, workspace,
+                   workspace_bytes, stream);
+}
+
+GDN_EXPORT gdn_status_t gdn_cpr2_decode_step(
+    const gdn_shape_t *shape, const uint8_t *expected_identity, const int32_t *pos, const void *q,
+    const void *k, const void *v, const float *a, const float *b, float *state, float *boundary,
+    void *cache_k, void *cache_v, float *cache_a, float *cache_b, float *o, float *resync_states,
+    void *workspace, size_t workspace_bytes, void *stream) {
+  const char *fn = "gdn_cpr2_decode_step";
+  gdn_status_t st = gdn::check_shape(fn, shape, expected_identity, true);
+  if (st != GDN_OK) return st;
+  if (shape->num_seqs > 0) {
+    if (!pos) return gdn::fail(GDN_E_NULL, std::string(fn) + ": pos is NULL");
+    if ((st = gdn::check_inputs(fn, shape, q, k, v, a, b)) != GDN_OK) return st;
+    if (!state || !boundary || !o || !cache_k || !cache_v || !cache_a || !cache_b)
+      return gdn::fail(GDN_E_NULL, std::string(fn) + ": state, boundary, o and the caches are required");
+    if (!gdn::aligned(pos, 4) || !gdn::aligned(o, 4) || !gdn::aligned(cache_a, 4) ||
+        !gdn::aligned(cache_b, 4) || !gdn::aligned(cache_k, 16) || !gdn::aligned(cache_v, 4))
+      return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": pos, o or a cache misaligned");
+  }
+  const float *f16[] = {state, boundary, resync_states};
+  for (const float *ptr : f16)
+    if ((st = gdn::check_state(fn, "a state buffer", ptr)) != GDN_OK) return st;
+  const gdn::Cpr2Layout ws = gdn::cpr2_layout(shape->num_seqs, shape->num_v_heads, shape->d_k,
+                                              shape->d_v, 0, true, false);
+  if (!workspace) return gdn::fail(GDN_E_NULL, std::string(fn) + ": workspace is NULL");
+  if (!gdn::aligned(workspace, 256))
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": workspace must be 256-byte aligned");
+  if ((int64_t)workspace_bytes < ws.total)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": workspace smaller than gdn_cpr2_workspace reports");
+  if (shape->num_seqs == 0) return gdn::ok();
+  // the running rows: one token through the decode kernel (no resync of its own)
+  gdn::DecodeArgs d{};
+  d.num_seqs = shape->num_seqs;
+  d.num_qk_heads = shape->num_qk_heads;
+  d.num_v_heads = shape->num_v_heads;
+  d.d_k = shape->d_k;
+  d.d_v = shape->d_v;
+  d.chunk = shape->chunk;
+  d.bf16 = shape->qkv_dtype == GDN_DTYPE_BF16;
+  d.pos = pos;
+  d.q = q;
+  d.k = k;
+  d.v = v;
+  d.a = a;
+  d.b = b;
+  d.state = state;
+  d.o = o;
+  d.resync_states = nullptr;
+  const int L = gdn::decode_lanes();
+  gdn::Cpr2Args args{};
+  args.num_seqs = shape->num_seqs;
+  args.num_qk_heads = shape->num_qk_heads;
+  args.num_v_heads = shape->num_v_heads;
+  args.d_k = shape->d_k;
+  args.d_v = shape->d_v;
+  args.chunk = shape->chunk;
+  args.bf16 = d.bf16;
+  args.decode = 1;
+  args.pos = pos;
+  args.state = state;
+  args.boundary = boundary;
+  args.resync = resync_states;
+  args.cache_k = cache_k;
+  args.cache_v = cache_v;
+  args.cache_a = cache_a;
+  args.cache_b = cache_b;
+  char *w = static_cast<char *>(workspace);
+  args.trans_a = reinterpret_cast<float *>(w + ws.ta_off);
+  args.trans_b = reinterpret_cast<float *>(w + ws.tb_off);
+  if (gdn::decode_grid(d, L) > gdn::kMaxInt32 || gdn::cpr2_max_grid(args) > gdn::kMaxInt32)
+    return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": grid too large");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = gdn::launch_decode(d, L, s);
+  if (e == hipSuccess) e = gdn::launch_cpr2_decode_tail(args, k, v, a, b, s);
+  if (e != hipSuccess)
+    return gdn::fail(GDN_E_DEVICE, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
+  return gdn::ok();
+}
+
 GDN_EXPORT gdn_status_t gdn_linear_fwd(const gdn_linear_shape_t *shape,
                                        const uint8_t *expected_identity, const void *x,
                                        const void *w, float *y, void *stream) {
@@ -404,16 +598,25 @@ GDN_EXPORT gdn_status_t gdn_linear_fwd(const gdn_linear_shape_t *shape,
   if (!shape) return gdn::fail(GDN_E_NULL, std::string(fn) + ": shape is NULL");
   if (!expected_identity)
     return gdn::fail(GDN_E_NULL, std::string(fn) + ": expected_identity is NULL");
-  // the linear rule is part of every contract text: accept the identity of any admitted one
+  // the linear rule is part of every contract text, one- or two-level: accept the identity
+  // of any admitted one (the digests are computed once per process)
+  static const std::vector<std::array<uint8_t, GDN_CPR_IDENTITY_BYTES>> digests = [] {
+    std::vector<std::array<uint8_t, GDN_CPR_IDENTITY_BYTES>> all;
+    const int32_t chunks[] = {16, 32, 64, 128, 256}, dks[] = {16, 32, 64, 128};
+    for (int32_t c : chunks)
+      for (int32_t d : dks)
+        for (int two = 0; two < 2; ++two) {
+          if (two && !gdn::cpr2_dk_admitted(d)) continue;
+          const std::string text = two ? gdn::cpr2_contract_text(c, d) : gdn::contract_text(c, d);
+          std::array<uint8_t, GDN_CPR_IDENTITY_BYTES> digest;
+          gdn::sha256(reinterpret_cast<const uint8_t *>(text.data()), text.size(), digest.data());
+          all.push_back(digest);
+        }
+    return all;
+  }();
   bool known = false;
-  const int32_t chunks[] = {16, 32, 64, 128, 256}, dks[] = {16, 32, 64, 128};
-  for (int32_t c : chunks)
-    for (int32_t d : dks) {
-      uint8_t digest[GDN_CPR_IDENTITY_BYTES];
-      const std::string text = gdn::contract_text(c, d);
-      gdn::sha256(reinterpret_cast<const uint8_t *>(text.data()), text.size(), digest);
-      known = known || std::memcmp(digest, expected_identity, sizeof digest) == 0;
-    }
+  for (const auto &digest : digests)
+    known = known || std::memcmp(digest.data(), expected_identity, digest.size()) == 0;
   if (!known)
     return gdn::fail(GDN_E_IDENTITY, std::string(fn) + ": expected_identity is not this library's "
                                          "contract");

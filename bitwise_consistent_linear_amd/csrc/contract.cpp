@@ -134,6 +134,7 @@ std::string contract_text(int32_t chunk, int32_t d_k) {
   s += "gqa=qk_head=v_head/(Hv/Hk)\n";
   s += "chunk_state=after in-sequence index j with (j+1)%C==0;floor(T_n/C) per sequence\n";
   s += "decode_resync=state after token pos when (pos+1)%C==0\n";
+  s += "cpr=one_level;rows absorb every token in order;chunk states are those rows\n";
   s += "bwd_order=reverse tokens;sh=dL/dS_final or 0;dS0=sh after the first token\n";
   s += "bwd_row=sh_e=fma(g,q_e,sh_e);pq_e=g*s_e;dh=dot(sh,k);dv_i=b*dh;pb=dh*(v_i-u);"
        "xh_e=fma(-dv_i,k_e,sh_e);pk_e=fma(-dv_i,x_e,d*sh_e);pa=dot(xh,s_prev);sh_e=a*xh_e\n";
@@ -144,6 +145,25 @@ std::string contract_text(int32_t chunk, int32_t d_k) {
        "inputs=x,w:binary32|bfloat16 widened exactly;output=binary32;rows independent\n";
   s += "chunk=" + std::to_string(chunk) + "\n";
   s += "d_k=" + std::to_string(d_k) + "\n";
+  return s;
+}
+
+// The two-level reading: the same region and row update, other state path.
+std::string cpr2_contract_text(int32_t chunk, int32_t d_k) {
+  std::string s = contract_text(chunk, d_k);
+  const std::string one = "cpr=one_level;rows absorb every token in order;chunk states are those rows\n";
+  const size_t at = s.find(one);
+  std::string two;
+  two += "cpr=two_level\n";
+  two += "two_level_transition=full chunk:S_end=S_start*A_c+B_c;A_c rows from unit rows e_j with "
+         "v=+0,B_c rows from +0 rows with v,through row_update over the chunk's tokens\n";
+  two += "two_level_boundary=S_0=initial;S_{c+1}[i,j]=fma chain over k ascending from B_c[i,j] "
+         "of S_c[i,k]*A_c[k,j];chunk states are S_{c+1}\n";
+  two += "two_level_outputs=rows restart from S_c at each chunk start;o=dot(s,q) after row_update\n";
+  two += "two_level_final=S after the last chunk if T_n%C==0 else the restarted rows\n";
+  two += "two_level_decode=running rows from the boundary state;C-token cache;after a chunk's "
+         "last token rows=boundary=resync=S_{c+1} from the cache\n";
+  s.replace(at, one.size(), two);
   return s;
 }
 
@@ -174,6 +194,31 @@ GDN_EXPORT gdn_status_t gdn_contract_string(int32_t chunk, int32_t d_k, char *bu
 GDN_EXPORT gdn_status_t gdn_sha256(const void *msg, size_t len, uint8_t digest[32]) {
   if (!digest || (!msg && len > 0)) return gdn::fail(GDN_E_NULL, "gdn_sha256: NULL pointer");
   gdn::sha256(static_cast<const uint8_t *>(msg), len, digest);
+  return gdn::ok();
+}
+
+GDN_EXPORT gdn_status_t gdn_cpr2_contract_string(int32_t chunk, int32_t d_k, char *buf,
+                                                 size_t buf_len, size_t *out_len) {
+  if (!out_len) return gdn::fail(GDN_E_NULL, "gdn_cpr2_contract_string: out_len is NULL");
+  if (!gdn::admitted_chunk(chunk) || !gdn::cpr2_dk_admitted(d_k))
+    return gdn::fail(GDN_E_UNSUPPORTED, "gdn_cpr2_contract_string: chunk or d_k not admitted");
+  std::string s = gdn::cpr2_contract_text(chunk, d_k);
+  *out_len = s.size();
+  if (buf_len < s.size() + 1) {
+    if (buf && buf_len) std::memcpy(buf, s.data(), buf_len);
+    return gdn::fail(GDN_E_SHAPE, "gdn_cpr2_contract_string: buffer too small");
+  }
+  if (!buf) return gdn::fail(GDN_E_NULL, "gdn_cpr2_contract_string: buf is NULL");
+  std::memcpy(buf, s.c_str(), s.size() + 1);
+  return gdn::ok();
+}
+
+GDN_EXPORT gdn_status_t gdn_cpr2_contract_identity(int32_t chunk, int32_t d_k, uint8_t digest[32]) {
+  if (!digest) return gdn::fail(GDN_E_NULL, "gdn_cpr2_contract_identity: digest is NULL");
+  if (!gdn::admitted_chunk(chunk) || !gdn::cpr2_dk_admitted(d_k))
+    return gdn::fail(GDN_E_UNSUPPORTED, "gdn_cpr2_contract_identity: chunk or d_k not admitted");
+  std::string s = gdn::cpr2_contract_text(chunk, d_k);
+  gdn::sha256(reinterpret_cast<const uint8_t *>(s.data()), s.size(), digest);
   return gdn::ok();
 }
 

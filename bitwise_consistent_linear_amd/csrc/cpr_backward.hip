@@ -41,7 +41,6 @@ constexpr int kChunkLanes = 16;                   // lanes per row in the chunk 
 constexpr int kChunkWaves = 8;                    // waves per chunk-kernel workgroup
 constexpr int kChunkThreads = 64 * kChunkWaves;
 constexpr int kChunkRows = kChunkThreads / kChunkLanes;
-constexpr int kPlanHeader = 4;                    // int32 slots before the (n, c) pairs
 
 // f(std::integral_constant<int, i>) for i = 0 .. N-1 (REVERSE: N-1 .. 0), each with its own
 // compile-time index, so register arrays indexed by i stay in registers.
@@ -56,55 +55,9 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 // --------------------------------------------------------------------------------- plan
 
-// Sums run in 64 bits: lengths come from device memory the host cannot check, and whatever
-// they hold, every slot and chunk-state base written below stays inside its buffer.
 __global__ __launch_bounds__(kThreads) void cpr_bwd_plan_kernel(const BwdArgs p) {
-  __shared__ int64_t s_ceil[kThreads], s_floor[kThreads];
-  __shared__ int64_t s_carry_ceil, s_carry_floor;
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    s_carry_ceil = 0;
-    s_carry_floor = 0;
-  }
-  __syncthreads();
-  for (int base = 0; base < p.num_seqs; base += kThreads) {
-    const int m = base + tid;
-    int64_t len = 0;
-    if (m < p.num_seqs) {
-      int64_t b, e;
-      seq_range(p.cu_seqlens, m, p.total_tokens, b, e);
-      len = e - b;
-    }
-    const int64_t nc = (len + p.chunk - 1) / p.chunk, nf = len / p.chunk;
-    s_ceil[tid] = nc;
-    s_floor[tid] = nf;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off *= 2) {  // inclusive scan
-      const int64_t vc = tid >= off ? s_ceil[tid - off] : 0;
-      const int64_t vf = tid >= off ? s_floor[tid - off] : 0;
-      __syncthreads();
-      s_ceil[tid] += vc;
-      s_floor[tid] += vf;
-      __syncthreads();
-    }
-    const int64_t ex_ceil = s_carry_ceil + s_ceil[tid] - nc;
-    const int64_t ex_floor = s_carry_floor + s_floor[tid] - nf;
-    if (m < p.num_seqs) {
-      p.plan_cbase[m] = (int32_t)(ex_floor < p.total_chunks ? ex_floor : p.total_chunks);
-      for (int64_t c = 0; c < nc && ex_ceil + c < p.slots_max; ++c) {
-        const int64_t slot = ex_ceil + c;
-        p.plan[kPlanHeader + 2 * slot] = m;
-        p.plan[kPlanHeader + 2 * slot + 1] = (int32_t)c;
-      }
-    }
-    __syncthreads();
-    if (tid == kThreads - 1) {
-      s_carry_ceil += s_ceil[tid];
-      s_carry_floor += s_floor[tid];
-    }
-    __syncthreads();
-  }
-  if (tid == 0) p.plan[0] = (int32_t)(s_carry_ceil < p.slots_max ? s_carry_ceil : p.slots_max);
+  chunk_plan(p.cu_seqlens, p.num_seqs, p.total_tokens, p.chunk, p.total_chunks, p.slots_max,
+             p.plan, p.plan_cbase);
 }
 
 // ---------------------------------------------------------------------------- state pass

@@ -161,6 +161,66 @@ __device__ __forceinline__ void block_work(int b, int pairs, int rblocks, int &p
   }
 }
 
+// The chunk slots of a packed batch, listed by one workgroup of 256 threads:
+// plan[0] = slots used (at most slots_max); slot s holds (sequence, chunk) in
+// plan[kPlanHeader + 2 s], plan[kPlanHeader + 2 s + 1], sequences in order, one slot per
+// chunk including a last partial one; cbase[n] = sum over m < n of floor(T_m / C), the
+// index of sequence n's first chunk state, clamped to total_chunks. The sums run in 64 bits:
+// lengths come from device memory the host cannot check, and whatever they hold, every slot
+// and base written stays inside its buffer.
+constexpr int kPlanHeader = 4;
+
+__device__ inline void chunk_plan(const int32_t *cu, int N, int64_t T, int C, int64_t total_chunks,
+                                  int slots_max, int32_t *plan, int32_t *cbase) {
+  constexpr int kThreads = 256;
+  __shared__ int64_t s_ceil[kThreads], s_floor[kThreads];
+  __shared__ int64_t s_carry_ceil, s_carry_floor;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    s_carry_ceil = 0;
+    s_carry_floor = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < N; base += kThreads) {
+    const int m = base + tid;
+    int64_t len = 0;
+    if (m < N) {
+      int64_t b, e;
+      seq_range(cu, m, T, b, e);
+      len = e - b;
+    }
+    const int64_t nc = (len + C - 1) / C, nf = len / C;
+    s_ceil[tid] = nc;
+    s_floor[tid] = nf;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off *= 2) {  // inclusive scan
+      const int64_t vc = tid >= off ? s_ceil[tid - off] : 0;
+      const int64_t vf = tid >= off ? s_floor[tid - off] : 0;
+      __syncthreads();
+      s_ceil[tid] += vc;
+      s_floor[tid] += vf;
+      __syncthreads();
+    }
+    const int64_t ex_ceil = s_carry_ceil + s_ceil[tid] - nc;
+    const int64_t ex_floor = s_carry_floor + s_floor[tid] - nf;
+    if (m < N) {
+      cbase[m] = (int32_t)(ex_floor < total_chunks ? ex_floor : total_chunks);
+      for (int64_t c = 0; c < nc && ex_ceil + c < slots_max; ++c) {
+        const int64_t slot = ex_ceil + c;
+        plan[kPlanHeader + 2 * slot] = m;
+        plan[kPlanHeader + 2 * slot + 1] = (int32_t)c;
+      }
+    }
+    __syncthreads();
+    if (tid == kThreads - 1) {
+      s_carry_ceil += s_ceil[tid];
+      s_carry_floor += s_floor[tid];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) plan[0] = (int32_t)(s_carry_ceil < slots_max ? s_carry_ceil : slots_max);
+}
+
 // Index of sequence n's first chunk-boundary state: sum over m < n of floor(T_m / C).
 __device__ inline int64_t first_chunk_slot(const int32_t *cu, int n, int64_t T, int C, int *s_acc) {
   if (threadIdx.x == 0) *s_acc = 0;

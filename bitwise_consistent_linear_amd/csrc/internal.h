@@ -81,6 +81,38 @@ int64_t backward_state_grid(const BwdArgs &args, int lanes_per_row);
 int64_t backward_chunk_grid(const BwdArgs &args, bool seq);
 hipError_t launch_backward(const BwdArgs &args, int lanes_per_row, bool seq, hipStream_t stream);
 
+// Arguments of the two-level CPR kernels (scan: trainer / prefill; or one decode step);
+// validated on the host.
+struct Cpr2Args {
+  int32_t num_seqs, num_qk_heads, num_v_heads, d_k, d_v, chunk;
+  int32_t bf16;
+  int32_t decode;     // 1: one decode step (tokens from the cache), 0: a packed batch
+  int32_t slots_max;  // chunk slots the plan may fill: total_chunks + num_seqs
+  int64_t total_tokens, total_chunks;
+  const int32_t *cu_seqlens, *pos;
+  const void *q, *k, *v;
+  const float *a, *b, *initial_state;
+  float *o, *chunk_states, *final_state;  // chunk_states: S after each full chunk
+  float *trans_a, *trans_b;               // A_c [.., Hv, d_k, d_k], B_c [.., Hv, d_v, d_k]
+  float *state, *boundary, *resync;       // decode
+  void *cache_k, *cache_v;                // decode: [N * C, Hk, d_k], [N * C, Hv, d_v]
+  float *cache_a, *cache_b;               // decode: [N * C, Hv]
+  int32_t *plan, *plan_cbase;
+};
+bool cpr2_dk_admitted(int d_k);
+// Byte offsets of a two-level workspace: the plan and chunk bases (batch only), A_c, B_c
+// (one per full chunk; decode: one per sequence) and, for prefill, the boundary states.
+struct Cpr2Layout {
+  int64_t plan_off, cbase_off, ta_off, tb_off, cs_off, total;
+};
+Cpr2Layout cpr2_layout(int64_t num_seqs, int64_t num_v_heads, int64_t d_k, int64_t d_v,
+                       int64_t total_chunks, bool decode, bool need_states);
+int64_t cpr2_max_grid(const Cpr2Args &args);
+hipError_t launch_cpr2_scan(const Cpr2Args &args, hipStream_t stream);
+hipError_t launch_cpr2_decode_tail(const Cpr2Args &args, const void *k, const void *v,
+                                   const float *a, const float *b, hipStream_t stream);
+std::string cpr2_contract_text(int32_t chunk, int32_t d_k);
+
 // Arguments of one linear-region launch (Y = X W); validated on the host.
 struct LinearArgs {
   int64_t m, n;

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GDN_CPR_ABI_VERSION 2
+#define GDN_CPR_ABI_VERSION 3
 #define GDN_CPR_LEAVES 16
 #define GDN_CPR_IDENTITY_BYTES 32
 
@@ -245,8 +245,8 @@ typedef struct gdn_linear_shape {
  * order (agentlenshq.com, section on achieving parallel invariance: tensor parallelism).
  * Here the 16 leaves of k/16 run on gfx950's binary32 matrix instructions, whose every
  * step is a fused multiply-add in ascending k, and are added by the dot's pairwise tree.
- *   shape, expected_identity : host pointers; the identity of any admitted (chunk, d_k)
- *                              (the linear rule is part of every contract text)
+ *   shape, expected_identity : host pointers; the identity of any admitted (chunk, d_k),
+ *                              one- or two-level (the linear rule is in every contract text)
  *   x  [m, k], w [k, n]      : binary32, or bfloat16 widened exactly; 16-byte aligned
  *   y  [m, n]                : binary32 output, 4-byte aligned; must not alias x or w
  *   stream                   : hipStream_t or NULL.
@@ -255,6 +255,97 @@ typedef struct gdn_linear_shape {
  * nothing. */
 gdn_status_t gdn_linear_fwd(const gdn_linear_shape_t *shape, const uint8_t *expected_identity,
                             const void *x, const void *w, float *y, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * TWO-LEVEL READING of CPR. The IsoExec pages describe CPR as the recurrence made primary
+ * but parallelised across chunks, with decode resynchronising its hidden state every C
+ * tokens (agentlenshq.com, section "Chunkwise-Parallel Recurrent (CPR) Gated DeltaNet").
+ * Read literally, the state at each chunk boundary comes from a chunkwise transition and
+ * the outputs from the recurrence restarted at each boundary, all chunks in parallel. The
+ * rows' update over a full chunk of C tokens is affine, S_end = S_start A_c + B_c, where
+ *   A_c [d_k, d_k]: unit rows e_j that absorb the chunk's tokens with v = +0,
+ *   B_c [d_v, d_k]: +0 rows that absorb them with the chunk's v,
+ * both through the contract row update above. Then, per sequence and value head,
+ *   S_0 = initial state;  S_{c+1}[i, j] = B_c[i, j] + sum_k S_c[i, k] A_c[k, j]
+ * as one fused multiply-add per k, k ascending, starting from B_c[i, j] (on gfx950's
+ * binary32 matrix instructions); the outputs of chunk c are those of rows that restart from
+ * S_c and absorb its tokens; the final state is S after the last full chunk when T_n is a
+ * multiple of C, else the restarted rows after the last token. Decode runs the rows from
+ * the boundary state token by token, keeps the chunk's tokens in a C-slot cache, and after
+ * a chunk's last token rebuilds A_c and B_c from the cache and sets the running state, the
+ * boundary state and the resync checkpoint to S_{c+1}. The three cases give the same bits
+ * (outputs, boundary states, final state) as one another, not as the one-level calls: the
+ * reading has its own contract text and identity. Admitted d_k: 32, 64 or 128.
+ * ------------------------------------------------------------------------------------ */
+
+/* Contract text and SHA-256 identity of the two-level reading for (chunk, d_k): the
+ * canonical text with its "cpr=" line replaced by the two-level lines. Host only. Errors
+ * as for gdn_contract_string / gdn_contract_identity; GDN_E_UNSUPPORTED also for d_k 16. */
+gdn_status_t gdn_cpr2_contract_string(int32_t chunk, int32_t d_k, char *buf, size_t buf_len,
+                                      size_t *out_len);
+gdn_status_t gdn_cpr2_contract_identity(int32_t chunk, int32_t d_k, uint8_t digest[32]);
+
+/* Bytes of device workspace that the two-level calls need, into *bytes (host). decode == 0:
+ * for gdn_cpr2_trainer_fwd and gdn_cpr2_prefill over total_tokens tokens and total_chunks
+ * full chunks (the prefill figure also holds its boundary states, so it is the larger);
+ * decode != 0: for gdn_cpr2_decode_step (total_tokens, total_chunks ignored). Host only.
+ * Errors: GDN_E_NULL, GDN_E_SHAPE. */
+gdn_status_t gdn_cpr2_workspace(const gdn_shape_t *shape, int64_t total_tokens,
+                                int64_t total_chunks, int32_t decode, size_t *bytes);
+
+/* trainer_fwd, two-level: o for every token and chunk_states [total_chunks, Hv, d_v, d_k]
+ * = S_1, S_2, ... of every sequence, laid out as for gdn_cpr_trainer_fwd.
+ *   expected_identity : gdn_cpr2_contract_identity(chunk, d_k)
+ *   workspace         : device, 256-byte aligned, at least gdn_cpr2_workspace(decode = 0)
+ *                       bytes; its contents on entry do not matter
+ * Other arguments and errors as for gdn_cpr_trainer_fwd, plus GDN_E_SHAPE when the
+ * workspace is short or misaligned. Launches four kernels on the stream: the chunk plan,
+ * the transitions of all full chunks, the boundary sweep, the outputs. */
+gdn_status_t gdn_cpr2_trainer_fwd(const gdn_shape_t *shape, const uint8_t *expected_identity,
+                                  const int32_t *cu_seqlens, int64_t total_tokens,
+                                  const void *q, const void *k, const void *v, const float *a,
+                                  const float *b, const float *initial_state, float *o,
+                                  float *chunk_states, int64_t total_chunks, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* engine_prefill, two-level: o for every token and final_state [N, Hv, d_v, d_k]
+ * (required; must not alias initial_state). total_chunks = sum_n floor(T_n / C) sizes the
+ * boundary states, which live in the workspace. Other arguments as for
+ * gdn_cpr2_trainer_fwd. */
+gdn_status_t gdn_cpr2_prefill(const gdn_shape_t *shape, const uint8_t *expected_identity,
+                              const int32_t *cu_seqlens, int64_t total_tokens, const void *q,
+                              const void *k, const void *v, const float *a, const float *b,
+                              const float *initial_state, float *o, float *final_state,
+                              int64_t total_chunks, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* engine_decode, two-level: one token for each of N sequences.
+ *   pos                 int32 [N], tokens already absorbed (pos[n] < 0: idle slot, nothing
+ *                       of it is read or written)
+ *   q, k, v, a, b       the step's token, layouts as for gdn_cpr_decode_step
+ *   state               float [N, Hv, d_v, d_k], in/out: the running rows
+ *   boundary            float [N, Hv, d_v, d_k], in/out: S_c of the chunk in progress
+ *   cache_k [N, C, Hk, d_k], cache_v [N, C, Hv, d_v] (qkv dtype), cache_a, cache_b
+ *                       float [N, C, Hv]: in/out, the chunk's tokens so far (slot pos % C);
+ *                       contents before a sequence's first step do not matter
+ *   o                   float [N, Hv, d_v] output
+ *   resync_states       float [N, Hv, d_v, d_k] or NULL: written with S_{c+1} iff
+ *                       (pos[n] + 1) % C == 0
+ *   workspace           device, 256-byte aligned, gdn_cpr2_workspace(decode != 0) bytes
+ * A sequence starts with pos = 0 and state = boundary = its initial state; to continue
+ * after a two-level prefill of P tokens, set state = its final state, boundary = the last
+ * chunk state S_{floor(P/C)} (gdn_cpr2_trainer_fwd's, or the initial state if P < C) and
+ * cache slots 0 .. P % C - 1 = the tokens after that boundary. After a step
+ * with (pos[n] + 1) % C == 0, state = boundary = resync = S_{c+1}, equal bit for bit to
+ * gdn_cpr2_trainer_fwd's chunk state there. Overlapping calls that share the workspace
+ * race. Errors as for gdn_cpr_decode_step, plus the workspace and cache checks. */
+gdn_status_t gdn_cpr2_decode_step(const gdn_shape_t *shape, const uint8_t *expected_identity,
+                                  const int32_t *pos, const void *q, const void *k,
+                                  const void *v, const float *a, const float *b, float *state,
+                                  float *boundary, void *cache_k, void *cache_v,
+                                  float *cache_a, float *cache_b, float *o,
+                                  float *resync_states, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /* Text describing the calling thread's last non-GDN_OK status ("" if none). The pointer
  * stays valid until the thread's next call into the library. Host only. */

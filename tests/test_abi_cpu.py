@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 17, names
     out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\s[TW]\s+(gdn_\w+)$", out, flags=re.M))
@@ -155,6 +155,33 @@ def decode(L, sh, identity=None, **ptrs):
                                  p["a"], p["b"], p["state"], p["o"], p["rs"], None)
 
 
+def cpr2_ident(sh):
+    if sh is None or sh.chunk not in CHUNKS or sh.d_k not in DKS[1:]:
+        return bytes(32)
+    return api.cpr2_contract_identity(sh.chunk, sh.d_k)
+
+
+def cpr2_batch(L, sh, prefill_case=False, identity=None, T=128, total_chunks=2,
+               ws_bytes=1 << 30, **ptrs):
+    p = dict(cu=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s0=None, o=FAKE, out=FAKE,
+             ws=FAKE)
+    p.update(ptrs)
+    idb = cpr2_ident(sh) if identity is None else identity
+    fn = L.gdn_cpr2_prefill if prefill_case else L.gdn_cpr2_trainer_fwd
+    return fn(ctypes.byref(sh), idb, p["cu"], T, p["q"], p["k"], p["v"], p["a"], p["b"],
+              p["s0"], p["o"], p["out"], total_chunks, p["ws"], ws_bytes, None)
+
+
+def cpr2_decode(L, sh, identity=None, ws_bytes=1 << 30, **ptrs):
+    p = dict(pos=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, state=FAKE, bnd=FAKE,
+             ck=FAKE, cv=FAKE, ca=FAKE, cb=FAKE, o=FAKE, rs=None, ws=FAKE)
+    p.update(ptrs)
+    idb = cpr2_ident(sh) if identity is None else identity
+    return L.gdn_cpr2_decode_step(ctypes.byref(sh), idb, p["pos"], p["q"], p["k"], p["v"],
+                                  p["a"], p["b"], p["state"], p["bnd"], p["ck"], p["cv"],
+                                  p["ca"], p["cb"], p["o"], p["rs"], p["ws"], ws_bytes, None)
+
+
 REFUSALS = [
     ("null shape", lambda L: trainer(L, None), api.GDN_E_NULL),
     ("null identity", lambda L: L.gdn_cpr_trainer_fwd(ctypes.byref(shape()), None, FAKE, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 2, None), api.GDN_E_NULL),
@@ -206,6 +233,23 @@ REFUSALS = [
     ("bwd misaligned dq", lambda L: bwd(L, shape(), dq=FAKE + 2), api.GDN_E_SHAPE),
     ("bwd null q", lambda L: bwd(L, shape(), q=None), api.GDN_E_NULL),
     ("bwd heads not a multiple", lambda L: bwd(L, shape(num_qk_heads=3)), api.GDN_E_SHAPE),
+    ("cpr2 one-level identity", lambda L: cpr2_batch(L, shape(), identity=api.contract_identity(64, 64)), api.GDN_E_IDENTITY),
+    ("one-level call, two-level identity", lambda L: trainer(L, shape(), identity=api.cpr2_contract_identity(64, 64)), api.GDN_E_IDENTITY),
+    ("cpr2 d_k 16", lambda L: cpr2_batch(L, shape(d_k=16)), api.GDN_E_UNSUPPORTED),
+    ("cpr2 more chunks than T/C", lambda L: cpr2_batch(L, shape(), total_chunks=3), api.GDN_E_SHAPE),
+    ("cpr2 null chunk_states", lambda L: cpr2_batch(L, shape(), out=None), api.GDN_E_NULL),
+    ("cpr2 null workspace", lambda L: cpr2_batch(L, shape(), ws=None), api.GDN_E_NULL),
+    ("cpr2 misaligned workspace", lambda L: cpr2_batch(L, shape(), ws=FAKE + 16), api.GDN_E_SHAPE),
+    ("cpr2 workspace too small", lambda L: cpr2_batch(L, shape(), ws_bytes=1024), api.GDN_E_SHAPE),
+    ("cpr2 prefill null final", lambda L: cpr2_batch(L, shape(), True, out=None), api.GDN_E_NULL),
+    ("cpr2 prefill final aliases initial", lambda L: cpr2_batch(L, shape(), True, s0=FAKE), api.GDN_E_SHAPE),
+    ("cpr2 prefill null v", lambda L: cpr2_batch(L, shape(), True, v=None), api.GDN_E_NULL),
+    ("cpr2 decode null boundary", lambda L: cpr2_decode(L, shape(), bnd=None), api.GDN_E_NULL),
+    ("cpr2 decode null cache", lambda L: cpr2_decode(L, shape(), cv=None), api.GDN_E_NULL),
+    ("cpr2 decode misaligned cache_k", lambda L: cpr2_decode(L, shape(), ck=FAKE + 8), api.GDN_E_SHAPE),
+    ("cpr2 decode misaligned boundary", lambda L: cpr2_decode(L, shape(), bnd=FAKE + 4), api.GDN_E_SHAPE),
+    ("cpr2 decode workspace too small", lambda L: cpr2_decode(L, shape(), ws_bytes=256), api.GDN_E_SHAPE),
+    ("cpr2 decode one-level identity", lambda L: cpr2_decode(L, shape(), identity=api.contract_identity(64, 64)), api.GDN_E_IDENTITY),
     ("linear null shape", lambda L: linear(L, shape_ok=False), api.GDN_E_NULL),
     ("linear wrong identity", lambda L: linear(L, identity=bytes(32)), api.GDN_E_IDENTITY),
     ("linear k not a multiple of 512", lambda L: linear(L, k=768), api.GDN_E_UNSUPPORTED),
@@ -223,7 +267,7 @@ REFUSALS = [
 def test_refused_before_launch(L, name, call, status):
     assert call(L) == status
     msg = L.gdn_last_error().decode()
-    assert msg.startswith(("gdn_cpr_", "gdn_linear_")), msg
+    assert msg.startswith(("gdn_cpr_", "gdn_cpr2_", "gdn_linear_")), msg
 
 
 def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
@@ -267,3 +311,49 @@ def test_linear_accepts_every_contract_identity_and_empty_sizes(L):
         for d in DKS:
             assert linear(L, m=0, identity=api.contract_identity(c, d)) == api.GDN_OK
     assert linear(L, n=0, x=None, w=None, y=None) == api.GDN_OK
+
+
+@pytest.mark.parametrize("chunk", CHUNKS)
+@pytest.mark.parametrize("d_k", DKS[1:])
+def test_two_level_contract_text(chunk, d_k):
+    """The two-level text is the canonical text with its one-level "cpr=" line replaced by
+    the two-level lines, and its identity is the SHA-256 of that text."""
+    one = api.contract_string(chunk, d_k).splitlines(keepends=True)
+    two = api.cpr2_contract_string(chunk, d_k)
+    at = [i for i, line in enumerate(one) if line.startswith("cpr=")]
+    assert len(at) == 1 and one[at[0]].startswith("cpr=one_level;")
+    lines = two.splitlines(keepends=True)
+    assert lines[:at[0]] == one[:at[0]] and lines[at[0]] == "cpr=two_level\n"
+    extra = lines[at[0] + 1:len(lines) - (len(one) - at[0] - 1)]
+    assert [x.split("=")[0] for x in extra] == [
+        "two_level_transition", "two_level_boundary", "two_level_outputs", "two_level_final",
+        "two_level_decode"]
+    assert lines[len(lines) - (len(one) - at[0] - 1):] == one[at[0] + 1:]
+    assert api.cpr2_contract_identity(chunk, d_k) == hashlib.sha256(two.encode()).digest()
+    assert api.cpr2_contract_identity(chunk, d_k) != api.contract_identity(chunk, d_k)
+
+
+def test_two_level_d_k_16_not_admitted(L):
+    buf = ctypes.create_string_buffer(32)
+    assert L.gdn_cpr2_contract_identity(64, 16, buf) == api.GDN_E_UNSUPPORTED
+
+
+def test_cpr2_workspace_size(L):
+    """Batch: the plan, chunk bases, one A_c [d_k, d_k] and B_c [d_v, d_k] per full chunk and
+    head, and the prefill's boundary states; decode: one A_c and B_c per sequence and head."""
+    sh = shape(num_seqs=3, num_v_heads=4, d_k=64, d_v=40, chunk=32)
+    batch = api.cpr2_workspace_bytes(sh, 1000, 30, False)
+    dec = api.cpr2_workspace_bytes(sh, 0, 0, True)
+    assert batch >= 30 * 4 * (64 * 64 + 40 * 64) * 4 + 30 * 4 * 40 * 64 * 4
+    assert dec >= 3 * 4 * (64 * 64 + 40 * 64) * 4
+    assert batch % 256 == 0 and dec % 256 == 0
+    n = ctypes.c_size_t(0)
+    assert L.gdn_cpr2_workspace(ctypes.byref(sh), 100, 4, 0, ctypes.byref(n)) == api.GDN_E_SHAPE
+    assert L.gdn_cpr2_workspace(ctypes.byref(sh), 100, 2, 0, None) == api.GDN_E_NULL
+    assert L.gdn_cpr2_workspace(ctypes.byref(shape(d_k=16)), 0, 0, 1,
+                                ctypes.byref(n)) == api.GDN_E_SHAPE
+
+
+def test_linear_accepts_two_level_identities(L):
+    for d in DKS[1:]:
+        assert linear(L, m=0, identity=api.cpr2_contract_identity(64, d)) == api.GDN_OK

@@ -4,7 +4,7 @@
 * no packed fp32 instructions and no unfused multiply-add (v_mad/v_mac) forms;
 * every fused multiply-add is a v_fma/v_fmac, every DPP reduction step an add;
 * no register spills in any kernel.
-Forward, decode, backward and linear-region kernels alike.
+Forward, decode, backward, two-level and linear-region kernels alike.
 """
 
 import re
@@ -33,10 +33,15 @@ def test_all_kernels_present(asm):
     assert sum("cpr_bwd_chunk_kernel" in n for n in names) == 4 * 2 * 2  # d_k, dtype, schedule
     assert sum("cpr_bwd_combine_kernel" in n for n in names) == 6
     assert sum("linear_leaf_kernel" in n for n in names) == 4
+    assert sum("cpr2_plan_kernel" in n for n in names) == 1
+    assert sum("cpr2_rows_kernel" in n for n in names) == 3 * 2 * 2  # d_k, dtype, mode
+    assert sum("cpr2_boundary_kernel" in n for n in names) == 3
+    assert sum("cpr2_cache_kernel" in n for n in names) == 2
 
 
-def test_linear_uses_the_binary32_matrix_instruction(asm):
-    """Every matrix instruction is the binary32 form whose steps are fused multiply-adds in
+def test_matrix_code_uses_the_binary32_instruction(asm):
+    """The linear region and the two-level boundary sweep are the only matrix code. Every
+    matrix instruction is the binary32 form whose steps are fused multiply-adds in
     ascending k; no reduced-precision or packed form appears."""
     mfma = set(re.findall(r"^\s+(v_mfma_\w+)", asm, flags=re.M))
     assert mfma == {"v_mfma_f32_32x32x2_f32"}, mfma
