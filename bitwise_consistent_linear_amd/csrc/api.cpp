@@ -579,6 +579,7 @@ GDN_EXPORT gdn_status_t gdn_cpr2_decode_step(
   args.cache_a = cache_a;
   args.cache_b = cache_b;
   char *w = static_cast<char *>(workspace);
+  args.plan = reinterpret_cast<int32_t *>(w + ws.plan_off);
   args.trans_a = reinterpret_cast<float *>(w + ws.ta_off);
   args.trans_b = reinterpret_cast<float *>(w + ws.tb_off);
   if (gdn::decode_grid(d, L) > gdn::kMaxInt32 || gdn::cpr2_max_grid(args) > gdn::kMaxInt32)

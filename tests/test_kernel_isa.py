@@ -34,17 +34,17 @@ def test_all_kernels_present(asm):
     assert sum("cpr_bwd_combine_kernel" in n for n in names) == 6
     assert sum("linear_leaf_kernel" in n for n in names) == 4
     assert sum("cpr2_plan_kernel" in n for n in names) == 1
-    assert sum("cpr2_rows_kernel" in n for n in names) == 3 * 2 * 2  # d_k, dtype, mode
-    assert sum("cpr2_boundary_kernel" in n for n in names) == 3
+    assert sum("cpr2_rows_kernel" in n for n in names) == 3 * 2 * 3  # d_k, dtype, variant
+    assert sum("cpr2_boundary_kernel" in n for n in names) == 3 * 2  # d_k, prefetch
     assert sum("cpr2_cache_kernel" in n for n in names) == 2
 
 
-def test_matrix_code_uses_the_binary32_instruction(asm):
-    """The linear region and the two-level boundary sweep are the only matrix code. Every
-    matrix instruction is the binary32 form whose steps are fused multiply-adds in
-    ascending k; no reduced-precision or packed form appears."""
+def test_matrix_code_uses_the_binary32_instructions(asm):
+    """The linear region (32 x 32 x 2) and the two-level boundary sweep (16 x 16 x 4) are
+    the only matrix code: binary32 forms whose steps were measured to be fused
+    multiply-adds in ascending k; no reduced-precision or packed form appears."""
     mfma = set(re.findall(r"^\s+(v_mfma_\w+)", asm, flags=re.M))
-    assert mfma == {"v_mfma_f32_32x32x2_f32"}, mfma
+    assert mfma == {"v_mfma_f32_32x32x2_f32", "v_mfma_f32_16x16x4_f32"}, mfma
 
 
 def test_denormals_kept(asm):
