@@ -13,7 +13,7 @@ batch-invariant matrix product on the matrix cores) and the two-level reading of
 fraction of the relevant peak, plus the CPU oracle timed on the host as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--cases all|main|bwd|linear|cpr2]
+                       [--cases all|main|bwd|linear|cpr2|traffic]
                        [--no-cpu-baseline]
 """
 
@@ -37,9 +37,10 @@ METRIC = "GDN-CPR tokens/s (trainer_fwd, prefill), decode-step us, % of HBM peak
 KERNEL_SOURCES = {  # sources whose hash a traffic summary must match to be used
     "cpr_scan_trainer_fwd": ["cpr_kernels.hip", "cpr_row.hpp", "cpr_io.hpp"],
     "cpr_bwd_trainer": ["cpr_backward.hip", "cpr_row.hpp", "cpr_io.hpp"],
+    "cpr2_two_level_trainer": ["cpr2.hip", "cpr_row.hpp", "cpr_io.hpp"],
 }
 PMC_COMMAND = ("rocprofv3 --pmc {counter} --output-format csv -d <dir> -o {name} -- python3 "
-               "bench.py --cases bwd --no-cpu-baseline --steps 3 --warmup 1 --copy-probe")
+               "bench.py --cases traffic --no-cpu-baseline --steps 3 --warmup 1 --copy-probe")
 COPY_PROBE_BYTES = 256 << 20  # read once and written once by the calibration copy
 
 
@@ -91,6 +92,15 @@ def scan_bytes(w, with_o=True, chunk_states=0, final_states=0, initial_states=0)
         b += T * Hv * dv * 4
     b += (chunk_states + final_states + initial_states) * Hv * dv * dk * 4
     return b
+
+
+def cpr2_bytes(w):
+    """Algorithmic HBM bytes of one two-level trainer call: the inputs once, o once, the
+    chunk states written once and read once (the outputs restart from them), and the
+    transitions A_c, B_c written once and read once."""
+    trans = w.total_chunks * w.num_v_heads * (w.d_k + w.d_v) * w.d_k * 4
+    states = w.total_chunks * w.num_v_heads * w.d_v * w.d_k * 4
+    return scan_bytes(w, chunk_states=w.total_chunks) + states + 2 * trans
 
 
 def decode_step_bytes(N, Hk, Hv, dk, dv, el, C):
@@ -153,9 +163,10 @@ def traffic_for(name, launches_bytes_fn=None):
 
 
 def write_traffic(fetch_csv, write_csv):
-    """From two rocprofv3 --pmc runs of `bench.py --cases bwd --copy-probe` (FETCH_SIZE, then
-    WRITE_SIZE; KiB per dispatch), write profiles/cpr_scan_trainer_fwd_traffic.json and
-    profiles/cpr_bwd_trainer_traffic.json: HBM bytes per launch, each counter scaled by what
+    """From two rocprofv3 --pmc runs of `bench.py --cases traffic --copy-probe` (FETCH_SIZE,
+    then WRITE_SIZE; KiB per dispatch), write profiles/cpr_scan_trainer_fwd_traffic.json,
+    profiles/cpr_bwd_trainer_traffic.json and profiles/cpr2_two_level_trainer_traffic.json:
+    HBM bytes per launch (per call for the multi-kernel ones), each counter scaled by what
     it reads for the 256 MiB calibration copy (read once, written once)."""
     import csv
     import statistics
@@ -190,6 +201,9 @@ def write_traffic(fetch_csv, write_csv):
         ("cpr_bwd_trainer", "cpr_bwd_",
          "trainer_bwd on the trainer_fwd workload (every backward kernel of one call)",
          bwd_bytes(w)),
+        ("cpr2_two_level_trainer", "cpr2_",
+         "two-level trainer_fwd on the trainer_fwd workload (every kernel of one call)",
+         cpr2_bytes(w)),
     ]
     for name, substr, workload, alg in targets:
         kf, kw = per_kernel(fr, substr), per_kernel(wr, substr)
@@ -350,9 +364,10 @@ def cpr2_flops(w):
     return trans, boundary, outputs
 
 
-def bench_cpr2(steps, warmup):
+def bench_cpr2(steps, warmup, trainer_only=False):
     """The two-level reading of CPR (gdn_cpr2_*): trainer_fwd and prefill on the trainer
-    workload, decode steps on the engine-decode workload from a chunk-aligned prefix."""
+    workload, decode steps on the engine-decode workload from a chunk-aligned prefix
+    (trainer_only: the trainer calls alone, for the counter runs)."""
     import torch
     from bitwise_consistent_linear_amd import api
     from bitwise_consistent_linear_amd import workloads as W
@@ -370,17 +385,21 @@ def bench_cpr2(steps, warmup):
     wall_t, per_t = timed(lambda: api.cpr2_trainer_fwd(cu, q, k, v, a, b, chunk=w.chunk, o=o,
                                                        chunk_states=cs, total_chunks=tc,
                                                        workspace=ws), steps, warmup)
-    wall_p, per_p = timed(lambda: api.cpr2_prefill(cu, q, k, v, a, b, chunk=w.chunk, o=o,
-                                                   final_state=fs, total_chunks=tc,
-                                                   workspace=ws), steps, warmup)
-    mt, mp = sum(per_t) / len(per_t), sum(per_p) / len(per_p)
+    mt = sum(per_t) / len(per_t)
     trans, boundary, outputs = cpr2_flops(w)
-    del q, k, v, o, cs, fs, ws
-    torch.cuda.empty_cache()
-    dec = bench_cpr2_decode()
     roof = roofline_alu(trans + boundary + outputs, mt)
     roof["scope"] = ("whole call (plan, transitions, boundary sweep, outputs); the boundary "
                      "sweep's flops run on the matrix units")
+    roof["traffic"] = traffic_for("cpr2_two_level_trainer")
+    if trainer_only:
+        return {"trainer_fwd_kernel_ms": round(mt, 4), "steps": steps, "roofline": roof}
+    wall_p, per_p = timed(lambda: api.cpr2_prefill(cu, q, k, v, a, b, chunk=w.chunk, o=o,
+                                                   final_state=fs, total_chunks=tc,
+                                                   workspace=ws), steps, warmup)
+    mp = sum(per_p) / len(per_p)
+    del q, k, v, o, cs, fs, ws
+    torch.cuda.empty_cache()
+    dec = bench_cpr2_decode()
     return {"workload": "two-level CPR on the trainer_fwd workload (4 x 4096 tokens, 16 heads, "
                         "d=128, C=64, bf16 q/k/v): o, the 256 chunk states (trainer) or the "
                         "final states (prefill)",
@@ -390,7 +409,7 @@ def bench_cpr2(steps, warmup):
             "prefill_kernel_ms": round(mp, 4),
             "flops": {"transitions": trans, "boundary_sweep": boundary, "outputs": outputs},
             "workspace_bytes": int(need), "steps": steps, "roofline": roof,
-            "decode": dec}
+            "hbm": hbm(cpr2_bytes(w), mt), "decode": dec}
 
 
 def bench_cpr2_decode(prefix=960, nsteps=504, warmup_steps=8):
@@ -504,11 +523,24 @@ def bench_decode_after_prefill(w, prefix, nsteps, warmup_steps, label):
             "algorithmic_bytes_per_step": int(nbytes)}
 
 
+def copy_probe_gbs(nbytes=1 << 30, reps=5):
+    """A plain device copy of nbytes (read once, written once), timed with HIP events: the
+    HBM rate a streaming kernel can reach on this GPU, beside the 8 TB/s peak."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    _, per = timed(lambda: y.copy_(x), reps, 2)
+    del x, y
+    ms = sorted(per)[len(per) // 2]
+    return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+
+
 def bench_decode():
     from bitwise_consistent_linear_amd import workloads as W
     w = W.engine_decode()
     log("engine_decode: N=256, 1000-token prefill, 512 decode steps, 16/32 heads, d=128")
     r = bench_decode_after_prefill(w, 1000, 504, 8, "engine_decode")
+    r["copy_probe_GBs"] = copy_probe_gbs()
     r["workload"] = ("engine_decode: 256 sequences, 16 q/k / 32 v heads, d=128, C=64, fp32 "
                      "state in HBM, prefill 1000 tokens then 512 steps (8 untimed)")
     return r
@@ -558,8 +590,15 @@ def cpu_baseline(w):
     O.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=w.chunk, want_chunk_states=True,
            nthreads=threads)
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         "")
+    except OSError:
+        pass
     return {"value": round(w.total_tokens / dt, 1), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "affinity_cores": O.default_threads(), "cpu_model": model,
             "sample": f"the whole trainer_fwd workload (4 x 4096 tokens, 16 heads, o and "
                       f"chunk states), {dt:.2f} s on {threads} threads"}
 
@@ -569,10 +608,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cases", choices=["all", "main", "bwd", "linear", "cpr2"], default="all",
+    ap.add_argument("--cases", choices=["all", "main", "bwd", "linear", "cpr2", "traffic"],
+                    default="all",
                     help="all: every case; main: trainer_fwd only; bwd / linear / cpr2: "
                          "trainer_fwd and the backward / the linear region / the two-level "
-                         "reading (for profiling)")
+                         "reading (for profiling); traffic: trainer_fwd, the backward and the "
+                         "two-level trainer calls (for the counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (untimed), the known-size "
@@ -654,6 +695,9 @@ def main():
         out["cases"] = {"linear": bench_linear(max(3, args.steps // 4), 1)}
     elif args.cases == "cpr2":
         out["cases"] = {"two_level": bench_cpr2(max(3, args.steps // 4), 1)}
+    elif args.cases == "traffic":
+        out["cases"] = {"trainer_bwd": bench_trainer_bwd(max(3, args.steps // 4), 1, kernel_ms),
+                        "two_level": bench_cpr2(max(3, args.steps // 4), 1, trainer_only=True)}
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the trainer_fwd workload")
         out["cpu_baseline"] = cpu_baseline(w)
