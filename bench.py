@@ -400,6 +400,31 @@ def bench_cpr2(steps, warmup, trainer_only=False):
     del q, k, v, o, cs, fs, ws
     torch.cuda.empty_cache()
     dec = bench_cpr2_decode()
+    torch.cuda.empty_cache()
+    big = {}
+    for label, make, trainer in (("long_context_trainer", W.long_context, True),
+                                 ("engine_prefill_prefill", W.engine_prefill, False)):
+        wb = make()
+        log(f"cpr2: {label}")
+        d = [up(x) for x in (wb.cu_seqlens, wb.q, wb.k, wb.v, wb.a, wb.b)]
+        shape_b = api.GdnShape(wb.num_seqs, wb.num_qk_heads, wb.num_v_heads, wb.d_k, wb.d_v,
+                               wb.chunk, api.GDN_DTYPE_BF16)
+        wsb = torch.empty(api.cpr2_workspace_bytes(shape_b, wb.total_tokens, wb.total_chunks,
+                                                   False), dtype=torch.uint8, device="cuda")
+        if trainer:
+            call = lambda: api.cpr2_trainer_fwd(*d, chunk=wb.chunk, total_chunks=wb.total_chunks,
+                                                workspace=wsb)
+        else:
+            call = lambda: api.cpr2_prefill(*d, chunk=wb.chunk, total_chunks=wb.total_chunks,
+                                            workspace=wsb)
+        wall_b, per_b = timed(call, 2, 1)
+        mb = sum(per_b) / len(per_b)
+        tb, bb, ob = cpr2_flops(wb)
+        big[label] = {"kernel_ms": round(mb, 3),
+                      "tokens_per_s": round(wb.total_tokens / (wall_b / 2), 1),
+                      "roofline": roofline_alu(tb + bb + ob, mb)}
+        del d, wsb, call
+        torch.cuda.empty_cache()
     return {"workload": "two-level CPR on the trainer_fwd workload (4 x 4096 tokens, 16 heads, "
                         "d=128, C=64, bf16 q/k/v): o, the 256 chunk states (trainer) or the "
                         "final states (prefill)",
@@ -409,7 +434,7 @@ def bench_cpr2(steps, warmup, trainer_only=False):
             "prefill_kernel_ms": round(mp, 4),
             "flops": {"transitions": trans, "boundary_sweep": boundary, "outputs": outputs},
             "workspace_bytes": int(need), "steps": steps, "roofline": roof,
-            "hbm": hbm(cpr2_bytes(w), mt), "decode": dec}
+            "hbm": hbm(cpr2_bytes(w), mt), "decode": dec, "larger_workloads": big}
 
 
 def bench_cpr2_decode(prefix=960, nsteps=504, warmup_steps=8):

@@ -6,8 +6,9 @@ below, at and above multiples of C), GQA, ragged d_v, f32 and bf16 storage, init
 and every admitted C. Decode runs staggered sequences with idle slots through chunk
 boundaries, against the oracle's outputs, chunk states and final states. The trainer
 workload (4 x 4096 tokens, 16 heads, d 128, C 64) runs at full size in the launch
-configuration that bench.py times: trainer and prefill agree on the device, and the oracle
-checks sampled (sequence, head) pairs that it computes alone. Decode resumes the
+configuration that bench.py times, as do the engine-prefill and long-context workloads:
+trainer and prefill agree on the device, and the oracle checks sampled (sequence, head)
+pairs that it computes alone (for the long context, the first 8192 tokens of two heads). Decode resumes the
 engine-decode workload after a 1000-token prefix (mid-chunk, from a boundary state and a
 token cache) and must reproduce the trainer's outputs and chunk states step by step, and end
 on the prefill's final state.
@@ -218,6 +219,44 @@ def test_config_trainer_fwd():
     assert_dev_equal(po, o, "trainer vs prefill o")
     assert_dev_equal(fs, cs.view(4, 64, 16, 128, 128)[:, -1], "prefill final vs last state")
     sampled_oracle(w, [(0, 0), (3, 15), (1, 6)], o, cs, fs)
+
+
+def test_config_engine_prefill():
+    w = W.engine_prefill()
+    L = w.lengths
+    log(f"cpr2 engine_prefill: N=64 varlen {L.min()}..{L.max()} sum {L.sum()} Hk=16 Hv=32 d=128")
+    d = up_workload(w)
+    po, fs = run_prefill(w, d)
+    o, cs = run_trainer(w, d)
+    torch.cuda.synchronize()
+    assert_dev_equal(o, po, "trainer vs prefill o")
+    # sequences whose length is a multiple of C end on their last chunk state
+    coff = np.concatenate([[0], np.cumsum(L // w.chunk)])
+    for n in np.flatnonzero(L % w.chunk == 0):
+        assert_dev_equal(fs[n], cs[coff[n + 1] - 1], f"final of sequence {n} vs its last state")
+    longest, shortest = int(np.argmax(L)), int(np.argmin(L))
+    sampled_oracle(w, [(longest, 31), (shortest, 0), (7, 13)], po, cs, fs)
+
+
+def test_config_long_context():
+    w = W.long_context()
+    log("cpr2 long_context: T=131072 Hk=16 Hv=32 d=128 C=64")
+    d = up_workload(w)
+    o, cs = run_trainer(w, d)
+    po, fs = run_prefill(w, d)
+    torch.cuda.synchronize()
+    assert_dev_equal(po, o, "trainer vs prefill o")
+    assert_dev_equal(fs, cs[-1:], "prefill final vs last chunk state")
+    # the oracle on the first 8192 tokens of two heads: outputs and states there depend on
+    # those tokens only
+    head = W.Workload("long_head", np.array([0, 8192], np.int32), w.q[:8192], w.k[:8192],
+                      w.v[:8192], w.a[:8192], w.b[:8192], 64, True)
+    for h in (0, 31):
+        part, _ = pair_slice(head, 0, h)
+        ro, rcs, _ = O.cpr2_scan(part.cu_seqlens, part.q, part.k, part.v, part.a, part.b,
+                                 chunk=64)
+        assert_bits(o[:8192, h], ro[:, 0], f"long oracle o (h={h}, first 8192 tokens)")
+        assert_bits(cs[:128, h], rcs[:, 0], f"long oracle chunk states (h={h}, first 128)")
 
 
 def test_config_engine_decode_resumes_mid_chunk():
