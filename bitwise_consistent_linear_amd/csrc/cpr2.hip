@@ -464,14 +464,15 @@ __global__ __launch_bounds__(D * 2) void cpr2_boundary_kernel(const Cpr2Args p) 
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      // S_{c+1} to HBM by buffer stores (rows past d_v are dropped)
-      if (p.decode) {
+      // S_{c+1} to HBM by buffer stores (rows past d_v are dropped), a fixed number per
+      // variant with no branch, so the compiler's waits can count them exactly
+      if constexpr (PREFETCH) {  // batch: chunk_states is set whenever a chunk exists
+        store_rows(p.chunk_states + (cidx * Hv + h) * st, (int)(st * 4), off, out);
+      } else {  // decode: boundary, state, resync (the boundary again when there is none)
         const int64_t base = ((int64_t)n * Hv + h) * st;
         store_rows(p.boundary + base, (int)(st * 4), off, out);
         store_rows(p.state + base, (int)(st * 4), off, out);
-        if (p.resync) store_rows(p.resync + base, (int)(st * 4), off, out);
-      } else if (p.chunk_states) {
-        store_rows(p.chunk_states + (cidx * Hv + h) * st, (int)(st * 4), off, out);
+        store_rows((p.resync ? p.resync : p.boundary) + base, (int)(st * 4), off, out);
       }
       cur = nxt;
     }
