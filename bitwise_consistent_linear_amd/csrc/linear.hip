@@ -11,10 +11,12 @@
 // combined by the same pairwise tree as the gated delta rule's dots. The bits of Y[m, n]
 // therefore depend on neither the tile, nor the number of rows M, nor the schedule.
 //
-// Workgroup: 8 waves, a 128 x 128 tile of Y; wave (wm, wn) owns rows 32 wm .. 32 wm + 31 and
-// columns 64 wn .. 64 wn + 63 as two 32 x 32 blocks that share the A operand; two waves per
-// SIMD. K is staged 32 at a time into LDS as binary32 (k-major, double-buffered, the next
-// stage's global loads in registers while the current one computes).
+// Workgroup: 8 waves, a 128 x 128 tile of Y; wave (wm, wn) owns rows 64 wm .. 64 wm + 63 and
+// columns 32 wn .. 32 wn + 31 as two 32 x 32 blocks that share the B operand (two
+// independent accumulator chains); two waves per SIMD. K is staged 32 at a time into LDS as
+// binary32, double-buffered, the next stage's global loads in registers while the current
+// one computes: W k-major; X row-major with each row's even and odd k apart, so one 16-byte
+// read gives a lane its A operands for four steps.
 
 #include "internal.h"
 
@@ -25,7 +27,7 @@ using f32x16 = float __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = 8, kThreads = 64 * kWaves;
 constexpr int TM = 128, TN = 128, KS = 32;     // workgroup tile, k per stage
-constexpr int XS = TM + 1, WS = TN + 4;        // LDS row strides (conflict-free deposits)
+constexpr int QS = KS / 2 + 4, WS = TN + 4;    // LDS row strides (conflict-free reads)
 constexpr int kLeaves = 16;
 constexpr int XPT = TM * KS / kThreads;        // staged X values per thread (8)
 constexpr int WPT = KS * TN / kThreads;        // staged W values per thread (8)
@@ -36,11 +38,11 @@ __device__ __forceinline__ float widen_bf16(uint32_t bits16) { return __uint_as_
 template <bool XBF16, bool WBF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void linear_leaf_kernel(const LinearArgs p) {
-  __shared__ __align__(16) float sx[2][KS][XS];  // sx[buf][k][row]
-  __shared__ __align__(16) float sw[2][KS][WS];  // sw[buf][k][col]
+  __shared__ __align__(16) float sx[2][2][TM][QS];  // sx[buf][k % 2][row][k / 2]
+  __shared__ __align__(16) float sw[2][KS][WS];      // sw[buf][k][col]
 
   const int tid = threadIdx.x, wave = tid / 64, l = tid % 64;
-  const int wm = wave / 2, wn = wave % 2;  // 4 x 2 waves of 32 x 64
+  const int wm = wave / 4, wn = wave % 4;  // 2 x 4 waves of 64 x 32
   const int64_t M = p.m, N = p.n;
   const int K = p.k;
   const int64_t tiles_n = (N + TN - 1) / TN;
@@ -102,16 +104,18 @@ void linear_leaf_kernel(const LinearArgs p) {
     }
   };
   auto deposit = [&](int buf) {
-#pragma unroll
-    for (int e = 0; e < XPT; ++e) sx[buf][xk + e][xr] = xv[e];
+    // k = xk + e: even k to half 0, odd k to half 1, at position k / 2
+    *reinterpret_cast<float4 *>(&sx[buf][0][xr][xk / 2]) = make_float4(xv[0], xv[2], xv[4], xv[6]);
+    *reinterpret_cast<float4 *>(&sx[buf][1][xr][xk / 2]) = make_float4(xv[1], xv[3], xv[5], xv[7]);
 #pragma unroll
     for (int e = 0; e < WPT; e += 4)
       *reinterpret_cast<float4 *>(&sw[buf][wk][wc + e]) =
           make_float4(wv[e], wv[e + 1], wv[e + 2], wv[e + 3]);
   };
 
-  // per lane: A operand (row 32 wm + l%32, k = 2p + l/32), B operands for both blocks
-  const int arow = 32 * wm + l % 32, bcol = 64 * wn + l % 32, kl = l / 32;
+  // per lane: A operands for both blocks (rows 64 wm + l%32 and 32 more, k = 2q + l/32), the
+  // shared B operand (column 32 wn + l%32)
+  const int arow = 64 * wm + l % 32, bcol = 32 * wn + l % 32, kl = l / 32;
   const int stages_per_leaf = K / (KS * kLeaves);  // K % 512 == 0: a leaf is whole stages
   f32x16 acc0, acc1;              // the current leaf, blocks 0 and 1
   f32x16 t0[4], t1[4];            // pending subtrees: slot j holds a sum of 2^j leaves
@@ -147,12 +151,16 @@ void linear_leaf_kernel(const LinearArgs p) {
       for (int r = 0; r < 16; ++r) { acc0[r] = -0.0f; acc1[r] = -0.0f; }
     }
 #pragma unroll
-    for (int q = 0; q < KS / 2; ++q) {
-      const float a = sx[buf][2 * q + kl][arow];
-      const float b0 = sw[buf][2 * q + kl][bcol];
-      const float b1 = sw[buf][2 * q + kl][bcol + 32];
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b0, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b1, acc1, 0, 0, 0);
+    for (int g = 0; g < KS / 8; ++g) {  // steps q = 4 g .. 4 g + 3, k = 2 q + kl
+      const float4 x0 = *reinterpret_cast<const float4 *>(&sx[buf][kl][arow][4 * g]);
+      const float4 x1 = *reinterpret_cast<const float4 *>(&sx[buf][kl][arow + 32][4 * g]);
+      const float a0[4] = {x0.x, x0.y, x0.z, x0.w}, a1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float b = sw[buf][2 * (4 * g + u) + kl][bcol];
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0[u], b, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[u], b, acc1, 0, 0, 0);
+      }
     }
     if (++in_leaf == stages_per_leaf) {
       in_leaf = 0;
@@ -163,14 +171,14 @@ void linear_leaf_kernel(const LinearArgs p) {
   }
 
   // the root is in t0[3], t1[3]; lane l, register r holds row 8 (r/4) + 4 (l/32) + r%4,
-  // column l%32 of its block
+  // column l%32 of its block (block 1 is 32 rows below block 0)
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int64_t row = m0 + 32 * wm + 8 * (r / 4) + 4 * kl + r % 4;
-    const int64_t c0 = n0 + 64 * wn + l % 32;
-    if (row < M) {
-      if (c0 < N) p.y[row * N + c0] = t0[3][r];
-      if (c0 + 32 < N) p.y[row * N + c0 + 32] = t1[3][r];
+    const int64_t row = m0 + 64 * wm + 8 * (r / 4) + 4 * kl + r % 4;
+    const int64_t col = n0 + 32 * wn + l % 32;
+    if (col < N) {
+      if (row < M) p.y[row * N + col] = t0[3][r];
+      if (row + 32 < M) p.y[(row + 32) * N + col] = t1[3][r];
     }
   }
 }
