@@ -107,9 +107,11 @@ def decode_schedule(lengths, starts):
 
 
 @pytest.mark.parametrize("dk,dv,chunk,bf16", [(32, 32, 16, False), (64, 40, 16, True),
-                                               (128, 128, 32, True)])
+                                               (128, 128, 32, True), (128, 72, 64, False)])
 def test_decode_staggered_matches_oracle(dk, dv, chunk, bf16):
     lengths, starts = [70, 33, 16, 48], [0, 5, 40, 2]
+    if chunk == 64:  # several boundaries per sequence at the larger chunk
+        lengths, starts = [200, 130, 64, 5], [0, 17, 3, 60]
     w, s0 = small_workload(f"dec{dk}", lengths, 2, 4, dk, dv, chunk, bf16, True)
     log(f"cpr2 decode: d_k={dk} d_v={dv} C={chunk} bf16={bf16} staggered {lengths}")
     ro, rcs, rfs = O.cpr2_scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=chunk,
