@@ -301,3 +301,55 @@ def test_config_engine_decode_resumes_mid_chunk():
     ro, rcs, _ = O.cpr2_scan(part.cu_seqlens, part.q, part.k, part.v, part.a, part.b, chunk=C)
     assert_bits(o_seq[200, :, 31], ro[:, 0], "oracle o (n=200, h=31)")
     assert_bits(cs_seq[200, :, 31], rcs[:, 0], "oracle chunk states (n=200, h=31)")
+
+
+def test_decode_steps_in_hip_graph_match_eager():
+    """Two-level decode steps (running rows, token cache, listed transitions, boundary
+    sweep) captured once into a HIP graph and replayed: every replay, after eager work and
+    a sync, gives the bits of the same steps run eagerly (the launches read pos and the
+    list from device memory, so one graph serves steps that do and do not end a chunk)."""
+    N, Hk, Hv, d, C = 4, 2, 4, 64, 16
+    w, s0 = small_workload("graph2", [48] * N, Hk, Hv, d, d, C, True, True)
+    _, steps = W.split_for_decode(w, 0)
+    dst = {key: up(x) for key, x in steps.items()}
+    S = dst["q"].shape[0]
+
+    def make():
+        return api.Cpr2Decoder(N, Hk, Hv, d, d, C, torch.bfloat16, DEV, initial_state=up(s0))
+
+    eager = make()
+    ref_o, ref_rs = [], []
+    for s in range(S):
+        rs = torch.zeros((N, Hv, d, d), device=DEV)
+        ref_o.append(eager.step(dst["pos"][s], dst["q"][s], dst["k"][s], dst["v"][s],
+                                dst["a"][s], dst["b"][s], resync_states=rs).clone())
+        ref_rs.append(rs)
+    dec = make()
+    saved = [t.clone() for t in (dec.state, dec.boundary, dec.cache_k, dec.cache_v,
+                                 dec.cache_a, dec.cache_b)]
+    outs = [torch.empty((N, Hv, d), device=DEV) for _ in range(S)]
+    rss = [torch.zeros((N, Hv, d, d), device=DEV) for _ in range(S)]
+    api.cpr2_contract_identity(C, d)  # host work outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in range(S):
+            dec.step(dst["pos"][s], dst["q"][s], dst["k"][s], dst["v"][s], dst["a"][s],
+                     dst["b"][s], o=outs[s], resync_states=rss[s])
+    for replay in range(3):
+        junk = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        for t, src in zip((dec.state, dec.boundary, dec.cache_k, dec.cache_v, dec.cache_a,
+                           dec.cache_b), saved):
+            t.copy_(src)
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        del junk
+        for s in range(S):
+            assert_dev_equal(outs[s], ref_o[s], f"replay {replay} step {s} o")
+            if (s + 1) % C == 0:
+                assert_dev_equal(rss[s], ref_rs[s], f"replay {replay} step {s} resync")
+        assert_dev_equal(dec.state, eager.state, f"replay {replay} final state")
+        assert_dev_equal(dec.boundary, eager.boundary, f"replay {replay} boundary")
