@@ -430,7 +430,7 @@ GDN_EXPORT gdn_status_t gdn_cpr2_workspace(const gdn_shape_t *shape, int64_t tot
   return gdn::ok();
 }
 
-static gdn_status_t cpr2_scan(const char *fn, const gdn_shape_t *shape,
+static gdn_status_t cpr2_scan(const char *fn, bool prefill, const gdn_shape_t *shape,
                               const uint8_t *expected_identity, const int32_t *cu_seqlens,
                               int64_t total_tokens, const void *q, const void *k, const void *v,
                               const float *a, const float *b, const float *initial_state, float *o,
@@ -443,7 +443,9 @@ static gdn_status_t cpr2_scan(const char *fn, const gdn_shape_t *shape,
   if ((st = cpr2_claims(fn, shape, total_tokens, total_chunks)) != GDN_OK) return st;
   if ((st = gdn::check_state(fn, "chunk_states", chunk_states)) != GDN_OK) return st;
   if ((st = gdn::check_state(fn, "final_state", final_state)) != GDN_OK) return st;
-  const bool trainer = final_state == nullptr;
+  const bool trainer = !prefill;
+  if (prefill && shape->num_seqs > 0 && !final_state)
+    return gdn::fail(GDN_E_NULL, std::string(fn) + ": final_state is required");
   if (final_state && final_state == initial_state)
     return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": final_state must not alias initial_state");
   if (trainer && total_chunks > 0 && !chunk_states)
@@ -497,9 +499,9 @@ GDN_EXPORT gdn_status_t gdn_cpr2_trainer_fwd(
     int64_t total_tokens, const void *q, const void *k, const void *v, const float *a,
     const float *b, const float *initial_state, float *o, float *chunk_states,
     int64_t total_chunks, void *workspace, size_t workspace_bytes, void *stream) {
-  return cpr2_scan("gdn_cpr2_trainer_fwd", shape, expected_identity, cu_seqlens, total_tokens, q,
-                   k, v, a, b, initial_state, o, chunk_states, nullptr, total_chunks, workspace,
-                   workspace_bytes, stream);
+  return cpr2_scan("gdn_cpr2_trainer_fwd", false, shape, expected_identity, cu_seqlens,
+                   total_tokens, q, k, v, a, b, initial_state, o, chunk_states, nullptr,
+                   total_chunks, workspace, workspace_bytes, stream);
 }
 
 GDN_EXPORT gdn_status_t gdn_cpr2_prefill(
@@ -507,11 +509,9 @@ GDN_EXPORT gdn_status_t gdn_cpr2_prefill(
     int64_t total_tokens, const void *q, const void *k, const void *v, const float *a,
     const float *b, const float *initial_state, float *o, float *final_state,
     int64_t total_chunks, void *workspace, size_t workspace_bytes, void *stream) {
-  const char *fn = "gdn_cpr2_prefill";
-  if (!final_state) return gdn::fail(GDN_E_NULL, std::string(fn) + ": final_state is required");
-  return cpr2_scan(fn, shape, expected_identity, cu_seqlens, total_tokens, q, k, v, a, b,
-                   initial_state, o, nullptr, final_state, total_chunks, workspace,
-                   workspace_bytes, stream);
+  return cpr2_scan("gdn_cpr2_prefill", true, shape, expected_identity, cu_seqlens,
+                   total_tokens, q, k, v, a, b, initial_state, o, nullptr, final_state,
+                   total_chunks, workspace, workspace_bytes, stream);
 }
 
 GDN_EXPORT gdn_status_t gdn_cpr2_decode_step(

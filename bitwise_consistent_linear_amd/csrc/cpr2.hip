@@ -468,11 +468,13 @@ __global__ __launch_bounds__(D * 2) void cpr2_boundary_kernel(const Cpr2Args p) 
       // variant with no branch, so the compiler's waits can count them exactly
       if constexpr (PREFETCH) {  // batch: chunk_states is set whenever a chunk exists
         store_rows(p.chunk_states + (cidx * Hv + h) * st, (int)(st * 4), off, out);
-      } else {  // decode: boundary, state, resync (the boundary again when there is none)
+      } else {  // decode: boundary, state, resync (a range of 0 bytes when there is none:
+                // every store then falls outside it and is dropped)
         const int64_t base = ((int64_t)n * Hv + h) * st;
         store_rows(p.boundary + base, (int)(st * 4), off, out);
         store_rows(p.state + base, (int)(st * 4), off, out);
-        store_rows((p.resync ? p.resync : p.boundary) + base, (int)(st * 4), off, out);
+        store_rows((p.resync ? p.resync : p.boundary) + base, p.resync ? (int)(st * 4) : 0, off,
+                   out);
       }
       cur = nxt;
     }

@@ -309,9 +309,9 @@ gdn_status_t gdn_cpr2_trainer_fwd(const gdn_shape_t *shape, const uint8_t *expec
                                   size_t workspace_bytes, void *stream);
 
 /* engine_prefill, two-level: o for every token and final_state [N, Hv, d_v, d_k]
- * (required; must not alias initial_state). total_chunks = sum_n floor(T_n / C) sizes the
- * boundary states, which live in the workspace. Other arguments as for
- * gdn_cpr2_trainer_fwd. */
+ * (required unless N == 0; must not alias initial_state). total_chunks =
+ * sum_n floor(T_n / C) sizes the boundary states, which live in the workspace. Other
+ * arguments as for gdn_cpr2_trainer_fwd. */
 gdn_status_t gdn_cpr2_prefill(const gdn_shape_t *shape, const uint8_t *expected_identity,
                               const int32_t *cu_seqlens, int64_t total_tokens, const void *q,
                               const void *k, const void *v, const float *a, const float *b,

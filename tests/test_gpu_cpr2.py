@@ -353,3 +353,40 @@ def test_decode_steps_in_hip_graph_match_eager():
                 assert_dev_equal(rss[s], ref_rs[s], f"replay {replay} step {s} resync")
         assert_dev_equal(dec.state, eager.state, f"replay {replay} final state")
         assert_dev_equal(dec.boundary, eager.boundary, f"replay {replay} boundary")
+
+
+def test_decode_without_resync_buffer():
+    """resync_states may be NULL: the steps then give the same outputs, running state and
+    boundary state as with a buffer, and write nothing else."""
+    N, Hk, Hv, d, C = 3, 1, 2, 32, 16
+    w, s0 = small_workload("noresync", [40] * N, Hk, Hv, d, d, C, False, True)
+    _, steps = W.split_for_decode(w, 0)
+    dst = {key: up(x) for key, x in steps.items()}
+    decs = [api.Cpr2Decoder(N, Hk, Hv, d, d, C, torch.float32, DEV, initial_state=up(s0))
+            for _ in range(2)]
+    for s in range(dst["q"].shape[0]):
+        args = (dst["pos"][s], dst["q"][s], dst["k"][s], dst["v"][s], dst["a"][s], dst["b"][s])
+        o1 = decs[0].step(*args, resync_states=torch.zeros((N, Hv, d, d), device=DEV))
+        o2 = decs[1].step(*args)
+        assert_dev_equal(o2, o1, f"step {s} o")
+    assert_dev_equal(decs[1].state, decs[0].state, "running state")
+    assert_dev_equal(decs[1].boundary, decs[0].boundary, "boundary state")
+
+
+def test_empty_batch():
+    """No sequences at all: every call, one- and two-level, succeeds and launches nothing."""
+    cu = torch.zeros(1, dtype=torch.int32, device=DEV)
+    q = torch.zeros((0, 1, 64), dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros((0, 2, 64), dtype=torch.bfloat16, device=DEV)
+    a = torch.zeros((0, 2), device=DEV)
+    outs = [*api.cpr2_trainer_fwd(cu, q, q, v, a, a, chunk=16),
+            *api.cpr2_prefill(cu, q, q, v, a, a, chunk=16),
+            *api.trainer_fwd(cu, q, q, v, a, a, chunk=16),
+            *api.prefill(cu, q, q, v, a, a, chunk=16)]
+    pos = torch.zeros(0, dtype=torch.int32, device=DEV)
+    outs.append(api.decode_step(pos, q, q, v, a, a, torch.zeros((0, 2, 64, 64), device=DEV),
+                                chunk=16))
+    dec = api.Cpr2Decoder(0, 1, 2, 64, 64, 16, torch.bfloat16, DEV)
+    outs.append(dec.step(pos, q, q, v, a, a))
+    torch.cuda.synchronize()
+    assert all(t.numel() == 0 for t in outs)
