@@ -36,7 +36,9 @@ constexpr int kThreads = 256;
 // keeps the cross-lane part of each dot at two DPP levels.
 constexpr int kLanes = 4;
 constexpr int kRows = kThreads / kLanes;   // rows per workgroup
-constexpr int kSub = 16;                   // tokens staged at a time
+// Tokens staged at a time: 16 for the transitions, whose next block is loaded into
+// registers meanwhile; 32 for the outputs, which load between blocks (fewer waits per chunk)
+constexpr int kSubTransition = 16, kSubOutput = 32;
 enum Cpr2Mode : int { kTransition = 0, kOutput = 1 };
 // Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format, no swizzle).
 constexpr int kBufferWord3 = 0x00020000;
@@ -120,8 +122,9 @@ __device__ void list_chunk_ends(const Cpr2Args &p) {
 // sequences in a grid-stride loop.
 template <int D, bool BF16, int MODE, bool LISTED>
 __global__ __launch_bounds__(kThreads) void cpr2_rows_kernel(const Cpr2Args p) {
-  constexpr int L = kLanes, M = D / L, ROWS = kRows, SB = kSub, GROUPS = D / 4;
   constexpr bool OUT = MODE == kOutput;
+  constexpr int L = kLanes, M = D / L, ROWS = kRows, GROUPS = D / 4;
+  constexpr int SB = OUT ? kSubOutput : kSubTransition;
   constexpr int KQ_ITEMS = SB * GROUPS, V_ITEMS = SB * ROWS;
   constexpr int KQ_PER = (KQ_ITEMS + kThreads - 1) / kThreads;
   constexpr int V_PER = (V_ITEMS + kThreads - 1) / kThreads;
