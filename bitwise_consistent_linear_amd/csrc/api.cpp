@@ -300,8 +300,8 @@ GDN_EXPORT gdn_status_t gdn_cpr_decode_step(const gdn_shape_t *shape,
 static gdn_status_t bwd_claims(const char *fn, const gdn_shape_t *shape, int64_t total_tokens,
                                int64_t total_chunks) {
   if (!shape) return gdn::fail(GDN_E_NULL, std::string(fn) + ": shape is NULL");
-  if (shape->chunk != 16 && shape->chunk != 32 && shape->chunk != 64)
-    return gdn::fail(GDN_E_UNSUPPORTED, std::string(fn) + ": the backward admits chunk 16, 32 or 64");
+  if (!gdn::admitted_chunk(shape->chunk))
+    return gdn::fail(GDN_E_UNSUPPORTED, std::string(fn) + ": chunk must be 16, 32, 64, 128 or 256");
   if (total_tokens < 0 || total_tokens > gdn::kMaxInt32)
     return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": total_tokens must be in [0, 2^31)");
   if (total_chunks < 0 || total_chunks > total_tokens / (shape->chunk > 0 ? shape->chunk : 1))

@@ -36,7 +36,9 @@ using namespace io;
 constexpr int kThreads = 256;
 constexpr int kStateStage = 16;                   // tokens staged at a time by the state pass
 constexpr int kSub = 8;                           // tokens per recomputed sub-block
-constexpr int kMaxSub = 8;                        // sub-blocks per chunk: C <= 64
+constexpr int kMaxSub = 8;                        // sub-blocks per segment
+constexpr int kSeg = kSub * kMaxSub;              // tokens per segment: a chunk of C > 64 is
+                                                  // processed as segments of 64, last first
 constexpr int kChunkLanes = 16;                   // lanes per row in the chunk kernel
 constexpr int kChunkWaves = 8;                    // waves per chunk-kernel workgroup
 constexpr int kChunkThreads = 64 * kChunkWaves;
@@ -269,7 +271,7 @@ __device__ __forceinline__ void rows4_sum(const float (&pq)[M], const float (&pk
 //                writes dv and dS0 itself, so the state pass does not run.
 // Checkpoints and a sub-block of recomputed states live in registers: allow up to 256
 // VGPRs (two waves per SIMD) rather than spill.
-template <int D, bool BF16, bool SEQ>
+template <int D, bool BF16, bool SEQ, bool LONG>
 __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void cpr_bwd_chunk_kernel(const BwdArgs p) {
   constexpr int kThreads = kChunkThreads;
@@ -339,8 +341,12 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
   uint32_t rv = 0;
   float rg = 0.0f, ra = 0.0f, rb = 0.0f;
   for (int c = c_hi; c >= c_lo; --c) {
-    // Thread-derived values come from an opaque copy of the thread index, once per chunk,
-    // so that the addresses of the unrolled body are not held live across chunks.
+   const int64_t cstart = (int64_t)c * p.chunk;
+   const int clen = (int)(Tn - cstart < p.chunk ? Tn - cstart : p.chunk);
+   const int nseg = LONG ? (clen + kSeg - 1) / kSeg : 1;  // LONG: chunks longer than kSeg
+   for (int seg = nseg - 1; seg >= 0; --seg) {
+    // Thread-derived values come from an opaque copy of the thread index, once per segment,
+    // so that the addresses of the unrolled body are not held live across segments.
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int row = tid / L, lane = tid % L;
@@ -414,8 +420,29 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
       }
     };
 
-    const int64_t c0 = (int64_t)c * p.chunk;
-    const int len = (int)(Tn - c0 < p.chunk ? Tn - c0 : p.chunk);
+    // The state at this segment's start: the chunk's start state carried forward over the
+    // segments before it, token by token in the forward order (the row update of the trainer,
+    // so the same bits). One staged sub-block at a time, buffer 0, no overlap: this runs only
+    // for chunks longer than a segment.
+    if constexpr (LONG) {
+     for (int j0 = 0; j0 < seg * kSeg; j0 += SB) {
+      fetch(cstart, j0, SB);
+      __syncthreads();  // buffer 0's previous readers are done
+      deposit(0);
+      __syncthreads();
+      for (int j = 0; j < SB; ++j) {
+        float kr[M], x[M];
+        lds_slice<D, L>(&sk[0][j * D], lane, kr);
+        row_decay<D, L>(s, sa[0][j], x);
+        const float u = contract_dot<D, L>(x, kr);
+        row_update<D, L>(s, row_delta(sb[0][j], sv[0][j * ROWS + row], u), kr, x);
+      }
+     }
+     if (seg > 0) __syncthreads();  // the advance's readers of buffer 0 are done
+    }
+
+    const int64_t c0 = cstart + (int64_t)seg * kSeg;
+    const int len = clen - seg * kSeg < kSeg ? clen - seg * kSeg : kSeg;
     const int nsb = (len + SB - 1) / SB;
     auto sub_len = [&](int sbi) { return len - sbi * SB < SB ? len - sbi * SB : SB; };
     fetch(c0, 0, sub_len(0));
@@ -534,6 +561,7 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
         __syncthreads();
       }
     });
+   }  // segments
   }
   if constexpr (SEQ) {
     int t = threadIdx.x;
@@ -614,13 +642,19 @@ const void *state_fn(int L, bool bf16) {
   }
 }
 
-template <int D>
-const void *chunk_fn(bool bf16, bool seq) {
+template <int D, bool LONG>
+const void *chunk_fn_len(bool bf16, bool seq) {
   if (seq)
-    return bf16 ? (const void *)cpr_bwd_chunk_kernel<D, true, true>
-                : (const void *)cpr_bwd_chunk_kernel<D, false, true>;
-  return bf16 ? (const void *)cpr_bwd_chunk_kernel<D, true, false>
-              : (const void *)cpr_bwd_chunk_kernel<D, false, false>;
+    return bf16 ? (const void *)cpr_bwd_chunk_kernel<D, true, true, LONG>
+                : (const void *)cpr_bwd_chunk_kernel<D, false, true, LONG>;
+  return bf16 ? (const void *)cpr_bwd_chunk_kernel<D, true, false, LONG>
+              : (const void *)cpr_bwd_chunk_kernel<D, false, false, LONG>;
+}
+
+// Chunks of at most kSeg tokens take the kernels without the segment advance.
+template <int D>
+const void *chunk_fn(bool bf16, bool seq, int chunk) {
+  return chunk > kSeg ? chunk_fn_len<D, true>(bf16, seq) : chunk_fn_len<D, false>(bf16, seq);
 }
 
 }  // namespace
@@ -661,10 +695,10 @@ hipError_t launch_backward(const BwdArgs &a, int L, bool seq, hipStream_t st) {
   if (e != hipSuccess) return e;
   const void *sf, *cf;
   switch (a.d_k) {
-    case 16: sf = state_fn<16>(L, a.bf16); cf = chunk_fn<16>(a.bf16, seq); break;
-    case 32: sf = state_fn<32>(L, a.bf16); cf = chunk_fn<32>(a.bf16, seq); break;
-    case 64: sf = state_fn<64>(L, a.bf16); cf = chunk_fn<64>(a.bf16, seq); break;
-    case 128: sf = state_fn<128>(L, a.bf16); cf = chunk_fn<128>(a.bf16, seq); break;
+    case 16: sf = state_fn<16>(L, a.bf16); cf = chunk_fn<16>(a.bf16, seq, a.chunk); break;
+    case 32: sf = state_fn<32>(L, a.bf16); cf = chunk_fn<32>(a.bf16, seq, a.chunk); break;
+    case 64: sf = state_fn<64>(L, a.bf16); cf = chunk_fn<64>(a.bf16, seq, a.chunk); break;
+    case 128: sf = state_fn<128>(L, a.bf16); cf = chunk_fn<128>(a.bf16, seq, a.chunk); break;
     default: return hipErrorInvalidValue;
   }
   if (!seq && (e = launch1(sf, backward_state_grid(a, L), a, st)) != hipSuccess) return e;

@@ -174,7 +174,7 @@ gdn_status_t gdn_cpr_decode_step(const gdn_shape_t *shape, const uint8_t *expect
 
 /* Bytes of device workspace that gdn_cpr_trainer_bwd needs for this shape, total_tokens
  * and total_chunks, into *bytes (host). Host only. Errors: GDN_E_NULL, GDN_E_UNSUPPORTED
- * (chunk not 16, 32 or 64), GDN_E_SHAPE (sizes outside the claims of gdn_cpr_trainer_bwd). */
+ * (chunk not 16, 32, 64, 128 or 256), GDN_E_SHAPE (sizes outside the claims of gdn_cpr_trainer_bwd). */
 gdn_status_t gdn_cpr_trainer_bwd_workspace(const gdn_shape_t *shape, int64_t total_tokens,
                                            int64_t total_chunks, size_t *bytes);
 
@@ -199,7 +199,7 @@ gdn_status_t gdn_cpr_trainer_bwd_workspace(const gdn_shape_t *shape, int64_t tot
  * Arguments:
  *   shape, expected_identity, cu_seqlens, total_tokens, q, k, v, a, b, initial_state:
  *                    as passed to the gdn_cpr_trainer_fwd call being differentiated;
- *                    shape->chunk must be 16, 32 or 64
+ *                    (every admitted chunk; C changes no bit of the gradients)
  *   chunk_states     [total_chunks, Hv, d_v, d_k]: that call's output (read only); NULL
  *                    only when total_chunks == 0
  *   total_chunks     sum_n floor(T_n / C), as for gdn_cpr_trainer_fwd

@@ -218,8 +218,8 @@ REFUSALS = [
     ("decode wrong identity", lambda L: decode(L, shape(), identity=b"\x01" * 32), api.GDN_E_IDENTITY),
     ("decode chunk not admitted", lambda L: decode(L, shape(chunk=100)), api.GDN_E_UNSUPPORTED),
     ("bwd wrong identity", lambda L: bwd(L, shape(), identity=bytes(32)), api.GDN_E_IDENTITY),
-    ("bwd chunk 128", lambda L: bwd(L, shape(chunk=128), total_chunks=1), api.GDN_E_UNSUPPORTED),
-    ("bwd chunk 256", lambda L: bwd(L, shape(chunk=256), total_chunks=0), api.GDN_E_UNSUPPORTED),
+    ("bwd chunk not admitted", lambda L: bwd(L, shape(chunk=100), total_chunks=1), api.GDN_E_UNSUPPORTED),
+    ("bwd chunk 8", lambda L: bwd(L, shape(chunk=8), total_chunks=0), api.GDN_E_UNSUPPORTED),
     ("bwd more chunks than T/C", lambda L: bwd(L, shape(), total_chunks=3), api.GDN_E_SHAPE),
     ("bwd null chunk_states", lambda L: bwd(L, shape(), cs=None), api.GDN_E_NULL),
     ("bwd null d_o", lambda L: bwd(L, shape(), do=None), api.GDN_E_NULL),
@@ -297,8 +297,11 @@ def test_bwd_workspace_size(L):
     assert small >= 100 * 4 * rb * (2 * 64 + 2) * 4 + 2 * 4 * 40 * 64 * 4
     assert big > small and small % 256 == 0 and big % 256 == 0
     n = ctypes.c_size_t(0)
-    assert L.gdn_cpr_trainer_bwd_workspace(ctypes.byref(shape(chunk=128)), 128, 1,
+    assert L.gdn_cpr_trainer_bwd_workspace(ctypes.byref(shape(chunk=100)), 128, 1,
                                            ctypes.byref(n)) == api.GDN_E_UNSUPPORTED
+    for c in (128, 256):  # long chunks are admitted
+        assert L.gdn_cpr_trainer_bwd_workspace(ctypes.byref(shape(chunk=c)), 300, 1,
+                                               ctypes.byref(n)) == api.GDN_OK
     assert L.gdn_cpr_trainer_bwd_workspace(ctypes.byref(sh), 100, 4,
                                            ctypes.byref(n)) == api.GDN_E_SHAPE
     assert L.gdn_cpr_trainer_bwd_workspace(ctypes.byref(sh), 100, 2, None) == api.GDN_E_NULL

@@ -4,7 +4,9 @@ bit for bit.
 Small cases cover ragged and empty sequences, lengths that are and are not multiples of C
 and of the 8-token recompute sub-block, GQA, every d_k, f32 and bf16 storage, ragged d_v
 (row blocks that end part-way, d_v below 16, up to 1024 rows), initial states, dL/dS_final
-present or absent, C = 16, 32 and 64, every lanes-per-row value of the state pass, and both
+present or absent, every admitted C (chunks of 128 and 256 are processed as 64-token
+segments, so lengths end part-way through a segment and in every segment), every
+lanes-per-row value of the state pass, and both
 schedules of the chunk pass (one workgroup per chunk after the state pass, or one per
 sequence sweeping its chunks in reverse). The
 trainer-size configuration (4 x 4096 tokens, 16 heads, d = 128, C = 64) is compared with
@@ -76,6 +78,11 @@ SMALL = [
     ("d16_dv300_c16", [40], 1, 1, 16, 300, 16, True, True, True),
     ("d16_dv1024_c64", [70], 1, 1, 16, 1024, 64, False, False, True),
     ("d128_empty_batch_c64", [0, 0, 0], 1, 2, 128, 128, 64, True, True, True),
+    ("d32_c128_segments", [300, 128, 65, 0, 129], 1, 2, 32, 32, 128, True, True, True),
+    ("d128_c128_f32", [200, 57], 1, 1, 128, 128, 128, False, False, True),
+    ("d64_dv40_c256", [520, 255, 64, 193], 2, 2, 64, 40, 256, True, True, True),
+    ("d128_bf16_c256_gqa", [256, 300], 1, 2, 128, 128, 256, True, True, False),
+    ("d16_dv300_c256", [270], 1, 1, 16, 300, 256, False, True, True),
 ]
 
 
@@ -139,14 +146,15 @@ def test_bwd_workspace_contents_do_not_matter():
 
 
 def test_bwd_refuses_unadmitted_chunk_and_leaves_outputs():
-    w, s0, do, dsf = case_workload("refuse", [130], 1, 1, 32, 32, 128, False, False, True)
+    w, s0, do, dsf = case_workload("refuse", [130], 1, 1, 32, 32, 64, False, False, True)
     d = up_workload(w)
-    o, cs = api.trainer_fwd(d["cu"], d["q"], d["k"], d["v"], d["a"], d["b"], chunk=128)
+    o, cs = api.trainer_fwd(d["cu"], d["q"], d["k"], d["v"], d["a"], d["b"], chunk=64)
     out = {g: None for g in GRADS}
     sentinel = torch.full((130, 1, 32), 7.0, device=DEV)
     with pytest.raises(api.GdnError) as e:
         api.trainer_bwd(d["cu"], d["q"], d["k"], d["v"], d["a"], d["b"], cs, up(do),
-                        chunk=128, d_final_state=up(dsf), out={"dq": sentinel})
+                        chunk=100, total_chunks=1, d_final_state=up(dsf),
+                        out={"dq": sentinel})
     assert e.value.status == api.GDN_E_UNSUPPORTED
     torch.cuda.synchronize()
     assert bool((sentinel == 7.0).all())
@@ -189,7 +197,7 @@ def test_bwd_config_trainer_matches_oracle(trainer_case):
         assert_dev_equal(again[g], got[g], f"repeat {g}")
 
 
-@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("chunk", [16, 32, 128, 256])
 def test_bwd_config_trainer_other_chunks_same_bits(trainer_case, chunk):
     """C only selects which states the forward stores: the gradients keep their bits."""
     w, do, dsf, ref = trainer_case
