@@ -39,16 +39,38 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source into bitwise_consistent_linear_amd/libgdn_cpr.so; return its path."""
+    """Compile every source into bitwise_consistent_linear_amd/libgdn_cpr.so; return its path.
+    Sources compile to objects side by side (one hipcc per source), then link."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+
+    def compile_one(src):
+        obj = os.path.join(objdir, src + ".o")
+        cmd = [HIPCC, *compile_flags, "-c", "-I", INCLUDE, "-I", CSRC, "-o", obj,
+               os.path.join(CSRC, src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        return obj, subprocess.run(cmd, capture_output=True, text=True)
+
+    jobs = max(1, min(len(SOURCES), os.cpu_count() or 1))
+    with ThreadPoolExecutor(jobs) as pool:
+        results = list(pool.map(compile_one, SOURCES))
+    for (obj, res), src in zip(results, SOURCES):
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc failed to compile {src}")
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp,
-           *[os.path.join(CSRC, s) for s in SOURCES]]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
+           *[obj for obj, _ in results]]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed to build libgdn_cpr.so")
+        raise RuntimeError("hipcc failed to link libgdn_cpr.so")
     os.replace(tmp, LIB)
     return LIB
 

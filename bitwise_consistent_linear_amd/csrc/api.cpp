@@ -21,6 +21,9 @@ namespace {
 thread_local std::string g_last_error;
 
 constexpr int64_t kMaxInt32 = 2147483647;
+// Elements of one token across all value heads (Hv * max(d_k, d_v)): bounded so that the
+// kernels' offsets inside a stage of tokens fit in 32 bits.
+constexpr int64_t kMaxHeadWidth = int64_t(1) << 20;
 
 bool aligned(const void *p, size_t bytes) {
   return (reinterpret_cast<uintptr_t>(p) % bytes) == 0;
@@ -57,12 +60,15 @@ int64_t device_simds() {
 // instructions but gives 4x the waves of 4 lanes per row; the recurrence is serial along
 // the tokens, so with at most one wave per SIMD latency dominates and more lanes win, while
 // with many waves per SIMD issue dominates and fewer lanes (fewer reduction steps) win.
+// At two waves per SIMD, 16 lanes per row beat one wave of 8 (measured on the 8192-row
+// trainer workload: the second wave issues its LDS and scalar work beside the first's
+// vector work, which a lone wave cannot).
 int scan_lanes(const ScanArgs &a) {
   if (const int o = lanes_override()) return o;
   const int64_t rows = (int64_t)a.num_seqs * a.num_v_heads * a.d_v;
   const int64_t simds = device_simds();
-  if (rows / 4 <= simds) return 16;  // <= 1 wave per SIMD with 16 lanes per row
-  if (rows / 8 <= simds) return 8;   // <= 1 wave per SIMD with 8 lanes per row
+  if (rows / 4 <= 2 * simds) return 16;  // <= 2 waves per SIMD with 16 lanes per row
+  if (rows / 8 <= simds) return 8;       // <= 1 wave per SIMD with 8 lanes per row
   return 4;
 }
 
@@ -110,6 +116,8 @@ gdn_status_t check_shape(const char *fn, const gdn_shape_t *sh, const uint8_t *i
     return fail(GDN_E_UNSUPPORTED, std::string(fn) + ": the two-level reading admits d_k 32, 64 or 128");
   if (sh->d_v < 1 || sh->d_v > 1024)
     return fail(GDN_E_UNSUPPORTED, std::string(fn) + ": d_v must be in [1, 1024]");
+  if ((int64_t)sh->num_v_heads * (sh->d_k > sh->d_v ? sh->d_k : sh->d_v) > kMaxHeadWidth)
+    return fail(GDN_E_SHAPE, std::string(fn) + ": num_v_heads * max(d_k, d_v) must be <= 2^20");
   if (!admitted_chunk(sh->chunk))
     return fail(GDN_E_UNSUPPORTED, std::string(fn) + ": chunk must be 16, 32, 64, 128 or 256");
   if (sh->qkv_dtype != GDN_DTYPE_F32 && sh->qkv_dtype != GDN_DTYPE_BF16)

@@ -51,16 +51,31 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
   using raw_t = typename Raw4<BF16>::type;
 
   // Two stage buffers: stage s is computed from buffer s&1 while stage s+1 is deposited
-  // into the other, so one barrier per stage suffices.
-  __shared__ __align__(16) float sk[2][TS * D];
-  __shared__ __align__(16) float sq[2][TS * D];
-  __shared__ float sv[2][V_ITEMS];
-  __shared__ float so[2][V_ITEMS];
-  __shared__ float sa[2][TS], sb[2][TS];
-  __shared__ int s_len[kMaxRankedSeqs];
-  __shared__ int s_pick, s_acc;
+  // into the other. A buffer holds the stage's k, then its q.
+  constexpr int KQ_FLOATS = TS * D;
+  constexpr int POOL = 2 * KQ_FLOATS;
+  // One block with the small arrays first, so that they sit below 64 KiB and every read of
+  // them takes an immediate offset from a fixed base.
+  struct alignas(16) Lds {
+    float sa[2][TS], sb[2][TS];
+    float sv[2][V_ITEMS];
+    float so[2][V_ITEMS];
+    int s_len[kMaxRankedSeqs];
+    int s_pick, s_acc;
+    alignas(16) float pool[2][POOL];
+  };
+  __shared__ Lds lds;
+  auto &sa = lds.sa;
+  auto &sb = lds.sb;
+  auto &sv = lds.sv;
+  auto &so = lds.so;
+  auto &pool = lds.pool;
+  int *const s_len = lds.s_len;
+  int &s_pick = lds.s_pick, &s_acc = lds.s_acc;
 
   const int tid = threadIdx.x, row = tid / L, lane = tid % L;
+  auto SK = [&](int buf) { return &pool[buf][0]; };
+  auto SQ = [&](int buf) { return &pool[buf][KQ_FLOATS]; };
   const int Hv = p.num_v_heads, Hk = p.num_qk_heads, dv = p.d_v;
   const int rblocks = (dv + ROWS - 1) / ROWS;
   int pair, rblock;
@@ -101,6 +116,8 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
   raw_t rk[KQ_PER], rq[KQ_PER];
   uint32_t rv[V_PER];
   float ra, rb;
+  // Generic fetch of the stage starting at in-sequence token t0 (any length, indices clamped
+  // to the sequence's last token): used for a sequence's last, partial stage.
   auto fetch = [&](int64_t t0) {
     const int64_t last = Tn - 1;
 #pragma unroll
@@ -122,14 +139,60 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
     ra = p.a[(bos + t) * Hv + h];
     rb = p.b[(bos + t) * Hv + h];
   };
+  // Byte offsets of this thread's staged loads and o stores inside one full stage, fixed for
+  // the whole scan. A full stage adds them to scalar stage bases, so its global accesses
+  // need no per-stage 64-bit address arithmetic. The host admits Hv * max(d_k, d_v) <= 2^20,
+  // so every offset inside a stage of at most 32 tokens fits in 32 bits.
+  constexpr uint32_t EL = BF16 ? 2 : 4;
+  const uint32_t kq_tok = (uint32_t)Hk * D;  // q/k elements per token
+  uint32_t kq_off[KQ_PER], v_off[V_PER], o_off[V_PER];
+  bool o_ok[V_PER];
+#pragma unroll
+  for (int j = 0; j < KQ_PER; ++j) {
+    const uint32_t g = (uint32_t)(tid + j * kThreads) % KQ_ITEMS;
+    kq_off[j] = ((g / GROUPS) * kq_tok + (uint32_t)hk * D + 4 * (g % GROUPS)) * EL;
+  }
+#pragma unroll
+  for (int j = 0; j < V_PER; ++j) {
+    const uint32_t e = (uint32_t)(tid + j * kThreads) % V_ITEMS;
+    const int r = r0 + (int)(e % ROWS) < dv ? r0 + (int)(e % ROWS) : dv - 1;
+    v_off[j] = ((e / ROWS) * (uint32_t)vstride + (uint32_t)(h * dv + r)) * EL;
+    const int eo = tid + j * kThreads;
+    o_off[j] = ((uint32_t)(eo / ROWS) * (uint32_t)vstride + (uint32_t)(h * dv + r0 + eo % ROWS)) * 4;
+    o_ok[j] = (V_ITEMS % kThreads == 0 || eo < V_ITEMS) && r0 + eo % ROWS < dv;
+  }
+  const uint32_t ab_off = (uint32_t)((tid % TS) * Hv + h) * 4;
+  // Fetch of a full stage (t0 + TS <= Tn): scalar bases plus the fixed offsets.
+  auto fetch_full = [&](int64_t t0) {
+    const int64_t tok = bos + t0;
+    const char *kb = static_cast<const char *>(p.k) + tok * kq_tok * EL;
+    const char *qb = static_cast<const char *>(p.q) + tok * kq_tok * EL;
+    const char *vb = static_cast<const char *>(p.v) + tok * vstride * EL;
+    const char *ab = reinterpret_cast<const char *>(p.a + tok * Hv);
+    const char *bb = reinterpret_cast<const char *>(p.b + tok * Hv);
+#pragma unroll
+    for (int j = 0; j < KQ_PER; ++j) {
+      rk[j] = *reinterpret_cast<const raw_t *>(kb + kq_off[j]);
+      rq[j] = *reinterpret_cast<const raw_t *>(qb + kq_off[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < V_PER; ++j) {
+      if constexpr (BF16)
+        rv[j] = *reinterpret_cast<const uint16_t *>(vb + v_off[j]);
+      else
+        rv[j] = *reinterpret_cast<const uint32_t *>(vb + v_off[j]);
+    }
+    ra = *reinterpret_cast<const float *>(ab + ab_off);
+    rb = *reinterpret_cast<const float *>(bb + ab_off);
+  };
   auto deposit = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < KQ_PER; ++j) {
       const int g = tid + j * kThreads;
       if (KQ_ITEMS % kThreads == 0 || g < KQ_ITEMS) {
         const int off = (g / GROUPS) * D + stage_slot<D, L>(g % GROUPS);
-        *reinterpret_cast<float4 *>(&sk[buf][off]) = widen4<BF16>(rk[j]);
-        *reinterpret_cast<float4 *>(&sq[buf][off]) = widen4<BF16>(rq[j]);
+        *reinterpret_cast<float4 *>(&SK(buf)[off]) = widen4<BF16>(rk[j]);
+        *reinterpret_cast<float4 *>(&SQ(buf)[off]) = widen4<BF16>(rq[j]);
       }
     }
 #pragma unroll
@@ -143,6 +206,13 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
     }
   };
   auto write_o = [&](int64_t t0, int nt, int buf) {
+    if (nt == TS) {  // full stage: scalar base plus the fixed offsets
+      char *ob = reinterpret_cast<char *>(p.o + (bos + t0) * vstride);
+#pragma unroll
+      for (int j = 0; j < V_PER; ++j)
+        if (o_ok[j]) *reinterpret_cast<float *>(ob + o_off[j]) = so[buf][tid + j * kThreads];
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < V_PER; ++j) {
       const int e = tid + j * kThreads;
@@ -155,8 +225,8 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
   // o_i and stores it (no branch), which keeps an unrolled stage in one basic block.
   auto run_token = [&](int buf, int tt) {
     float kr[M], qr[M];
-    lds_slice<D, L>(&sk[buf][tt * D], lane, kr);
-    lds_slice<D, L>(&sq[buf][tt * D], lane, qr);
+    lds_slice<D, L>(&SK(buf)[tt * D], lane, kr);
+    lds_slice<D, L>(&SQ(buf)[tt * D], lane, qr);
     so[buf][tt * ROWS + row] =
         row_token<D, L>(s, sa[buf][tt], sb[buf][tt], sv[buf][tt * ROWS + row], kr, qr);
   };
@@ -170,8 +240,8 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
   auto run_stage_pipelined = [&](int buf, float (&snap)[M]) {
     float rk_[3][M], rq_[3][M], ra_[3], rb_[3], rv_[3], x[M];
     auto load_token = [&](int tt, int slot) {
-      lds_slice<D, L>(&sk[buf][tt * D], lane, rk_[slot]);
-      lds_slice<D, L>(&sq[buf][tt * D], lane, rq_[slot]);
+      lds_slice<D, L>(&SK(buf)[tt * D], lane, rk_[slot]);
+      lds_slice<D, L>(&SQ(buf)[tt * D], lane, rq_[slot]);
       ra_[slot] = sa[buf][tt];
       rb_[slot] = sb[buf][tt];
       rv_[slot] = sv[buf][tt * ROWS + row];
@@ -189,7 +259,6 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
 #pragma unroll
         for (int e = 0; e < M; ++e) snap[e] = s[e];
       }
-      float o;
       if (tt + 1 < TS) {
         row_decay<D, L>(s, ra_[nxt], x);
         float xs[2][M], ys[2][M], r[2];
@@ -201,12 +270,11 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
           ys[1][e] = rk_[nxt][e];
         }
         contract_dots<D, L, 2>(xs, ys, r);
-        o = r[0];
+        so[buf][tt * ROWS + row] = r[0];
         u = r[1];
       } else {
-        o = contract_dot<D, L>(s, rq_[cur]);
+        so[buf][tt * ROWS + row] = contract_dot<D, L>(s, rq_[cur]);
       }
-      so[buf][tt * ROWS + row] = o;
     }
   };
 
@@ -225,7 +293,10 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
   const int64_t nstages = (Tn + TS - 1) / TS;
 
   if (Tn > 0) {
-    fetch(0);
+    if (Tn >= TS)
+      fetch_full(0);
+    else
+      fetch(0);
     deposit(0);
   }
   __syncthreads();
@@ -234,7 +305,12 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
     const int64_t t0 = st * TS;
     const int nt = (int)(Tn - t0 < TS ? Tn - t0 : TS);
     const bool more = st + 1 < nstages;
-    if (more) fetch(t0 + TS);  // global loads in flight while this stage computes
+    if (more) {  // global loads in flight while this stage computes
+      if (t0 + 2 * TS <= Tn)
+        fetch_full(t0 + TS);
+      else
+        fetch(t0 + TS);
+    }
     if (nt == TS) {
       if constexpr (L >= 8) {
         float snap[M];

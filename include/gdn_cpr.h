@@ -85,6 +85,7 @@ typedef enum gdn_dtype { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 } gdn_dtype_t;
 /* Host struct. Admitted values (claims checked on every call):
  *   num_seqs >= 0; num_qk_heads >= 1; num_v_heads a multiple of num_qk_heads;
  *   d_k in {16, 32, 64, 128}; 1 <= d_v <= 1024; chunk in {16, 32, 64, 128, 256};
+ *   num_v_heads * max(d_k, d_v) <= 2^20 (GDN_E_SHAPE otherwise);
  *   qkv_dtype GDN_DTYPE_F32 or GDN_DTYPE_BF16. */
 typedef struct gdn_shape {
   int32_t num_seqs;     /* N  */

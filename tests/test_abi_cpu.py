@@ -190,6 +190,7 @@ REFUSALS = [
     ("identity of other d_k", lambda L: prefill(L, shape(), identity=api.contract_identity(64, 128)), api.GDN_E_IDENTITY),
     ("heads not a multiple", lambda L: trainer(L, shape(num_qk_heads=3, num_v_heads=4)), api.GDN_E_SHAPE),
     ("zero qk heads", lambda L: trainer(L, shape(num_qk_heads=0)), api.GDN_E_SHAPE),
+    ("heads x width > 2^20", lambda L: trainer(L, shape(num_qk_heads=1, num_v_heads=16385)), api.GDN_E_SHAPE),
     ("negative seqs", lambda L: trainer(L, shape(num_seqs=-1)), api.GDN_E_SHAPE),
     ("d_k not admitted", lambda L: trainer(L, shape(d_k=48)), api.GDN_E_UNSUPPORTED),
     ("d_v zero", lambda L: trainer(L, shape(d_v=0)), api.GDN_E_UNSUPPORTED),
