@@ -633,12 +633,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cases", choices=["all", "main", "bwd", "linear", "cpr2", "traffic"],
+    ap.add_argument("--cases",
+                    choices=["all", "main", "bwd", "decode", "linear", "cpr2", "traffic"],
                     default="all",
-                    help="all: every case; main: trainer_fwd only; bwd / linear / cpr2: "
-                         "trainer_fwd and the backward / the linear region / the two-level "
-                         "reading (for profiling); traffic: trainer_fwd, the backward and the "
-                         "two-level trainer calls (for the counter runs)")
+                    help="all: every case; main: trainer_fwd only; bwd / decode / linear / "
+                         "cpr2: trainer_fwd and the backward / the engine_decode steps / the "
+                         "linear region / the two-level reading (for profiling); traffic: "
+                         "trainer_fwd, the backward and the two-level trainer calls (for the "
+                         "counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (untimed), the known-size "
@@ -651,8 +653,9 @@ def main():
         write_traffic(*args.traffic_from)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (every state "
-              "row is independent; see DESIGN.md for how the work would shard).",
+        print("bench.py measures one GPU only: there is no multi-GPU path. Every state row "
+              "evolves on its own, so sequences and value heads would split across GPUs with "
+              "no exchange and no change of bits.",
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -716,6 +719,8 @@ def main():
         out["cases"] = cases
     elif args.cases == "bwd":
         out["cases"] = {"trainer_bwd": bench_trainer_bwd(max(3, args.steps // 4), 1, kernel_ms)}
+    elif args.cases == "decode":
+        out["cases"] = {"engine_decode": bench_decode()}
     elif args.cases == "linear":
         out["cases"] = {"linear": bench_linear(max(3, args.steps // 4), 1)}
     elif args.cases == "cpr2":
