@@ -634,11 +634,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cases",
-                    choices=["all", "main", "bwd", "decode", "linear", "cpr2", "traffic"],
+                    choices=["all", "main", "bwd", "prefill", "decode", "linear", "cpr2",
+                             "traffic"],
                     default="all",
-                    help="all: every case; main: trainer_fwd only; bwd / decode / linear / "
-                         "cpr2: trainer_fwd and the backward / the engine_decode steps / the "
-                         "linear region / the two-level reading (for profiling); traffic: "
+                    help="all: every case; main: trainer_fwd only; bwd / prefill / decode / "
+                         "linear / cpr2: trainer_fwd and the backward / the engine_prefill call "
+                         "/ the engine_decode steps / the linear region / the two-level reading "
+                         "(for profiling); traffic: "
                          "trainer_fwd, the backward and the two-level trainer calls (for the "
                          "counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -719,6 +721,8 @@ def main():
         out["cases"] = cases
     elif args.cases == "bwd":
         out["cases"] = {"trainer_bwd": bench_trainer_bwd(max(3, args.steps // 4), 1, kernel_ms)}
+    elif args.cases == "prefill":
+        out["cases"] = {"engine_prefill": bench_prefill(max(3, args.steps // 4), 1)}
     elif args.cases == "decode":
         out["cases"] = {"engine_decode": bench_decode()}
     elif args.cases == "linear":
