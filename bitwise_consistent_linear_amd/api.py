@@ -127,6 +127,7 @@ def sha256(data: bytes) -> bytes:
 
 
 @lru_cache(maxsize=None)
+@lru_cache(maxsize=None)
 def contract_identity(chunk: int, d_k: int) -> bytes:
     out = ctypes.create_string_buffer(32)
     _check(lib().gdn_contract_identity(chunk, d_k, out))
@@ -155,7 +156,7 @@ def _need(t, name, dtypes, ndim=None):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU device")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
@@ -388,6 +389,7 @@ def cpr2_contract_string(chunk: int, d_k: int) -> str:
     return buf.value.decode()
 
 
+@lru_cache(maxsize=None)
 @lru_cache(maxsize=None)
 def cpr2_contract_identity(chunk: int, d_k: int) -> bytes:
     out = ctypes.create_string_buffer(32)

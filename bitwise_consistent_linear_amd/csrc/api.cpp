@@ -10,6 +10,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -102,6 +103,20 @@ int decode_lanes() {
   return 16;
 }
 
+// SHA-256 of the contract text for an admitted (chunk, d_k), computed once per process and
+// entry: the text is fixed for the library, and hashing it on every call would cost each
+// decode step microseconds of host time.
+const uint8_t *contract_digest(bool two_level, int32_t chunk, int32_t d_k) {
+  static std::once_flag once[2][5][4];
+  static uint8_t digest[2][5][4][32];
+  const int c = __builtin_ctz((unsigned)chunk) - 4, d = __builtin_ctz((unsigned)d_k) - 4;
+  std::call_once(once[two_level][c][d], [&] {
+    const std::string text = two_level ? cpr2_contract_text(chunk, d_k) : contract_text(chunk, d_k);
+    sha256(reinterpret_cast<const uint8_t *>(text.data()), text.size(), digest[two_level][c][d]);
+  });
+  return digest[two_level][c][d];
+}
+
 gdn_status_t check_shape(const char *fn, const gdn_shape_t *sh, const uint8_t *identity,
                          bool two_level = false) {
   if (!sh) return fail(GDN_E_NULL, std::string(fn) + ": shape is NULL");
@@ -122,11 +137,7 @@ gdn_status_t check_shape(const char *fn, const gdn_shape_t *sh, const uint8_t *i
     return fail(GDN_E_UNSUPPORTED, std::string(fn) + ": chunk must be 16, 32, 64, 128 or 256");
   if (sh->qkv_dtype != GDN_DTYPE_F32 && sh->qkv_dtype != GDN_DTYPE_BF16)
     return fail(GDN_E_UNSUPPORTED, std::string(fn) + ": qkv_dtype must be F32 or BF16");
-  uint8_t mine[32];
-  const std::string text = two_level ? cpr2_contract_text(sh->chunk, sh->d_k)
-                                     : contract_text(sh->chunk, sh->d_k);
-  sha256(reinterpret_cast<const uint8_t *>(text.data()), text.size(), mine);
-  if (std::memcmp(mine, identity, 32) != 0)
+  if (std::memcmp(contract_digest(two_level, sh->chunk, sh->d_k), identity, 32) != 0)
     return fail(GDN_E_IDENTITY, std::string(fn) + ": expected_identity differs from this "
                                 "library's contract for (chunk, d_k)");
   return GDN_OK;
