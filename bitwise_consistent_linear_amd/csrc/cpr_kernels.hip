@@ -29,21 +29,21 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-// Tokens staged in LDS at a time: 32 where few waves share a SIMD (lanes per row >= 8),
-// which halves the per-stage barrier and pipeline restart; 16 where occupancy matters.
-// Both divide every admitted chunk size's multiples of 16: a chunk boundary falls on
-// token 15 or 31 of a stage.
-template <int L>
-constexpr int stage_tokens() { return L >= 8 ? 32 : 16; }
+// TS, the tokens staged in LDS at a time, is chosen by the launcher: 64 for a prefill with a
+// lone wave per SIMD at 16 lanes per row, 32 for 8 or 16 lanes per row otherwise, 16 for 4
+// (where occupancy matters). Longer stages halve the per-stage barrier and pipeline restart but
+// take more LDS. Stages start at in-sequence index 0 and every admitted C is a multiple of
+// 16, so a chunk boundary falls on a token 16 m - 1 of a stage.
 // ----------------------------------------------------------------------------- kernels
 
 using namespace io;
 
-template <int D, int L, bool BF16, int MODE>
+template <int D, int L, int TS, bool BF16, int MODE>
 __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
+  static_assert(TS % 16 == 0, "a stage holds whole 16-token groups");
   constexpr int ROWS = kThreads / L;
   constexpr int M = D / L;
-  constexpr int TS = stage_tokens<L>();
+  constexpr int SNAPS = TS / 16 > 1 ? TS / 16 - 1 : 1;  // chunk boundaries inside a stage
   constexpr int GROUPS = D / 4;  // float4 groups per staged k or q vector
   constexpr int KQ_ITEMS = TS * GROUPS, V_ITEMS = TS * ROWS;
   constexpr int KQ_PER = (KQ_ITEMS + kThreads - 1) / kThreads;
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
   // one that row_token performs, on the same operands; only independent operations are
   // interleaved, so the bits are the same. Used where few waves share a SIMD and latency,
   // not issue, bounds the stage.
-  auto run_stage_pipelined = [&](int buf, float (&snap)[M]) {
+  auto run_stage_pipelined = [&](int buf, float (&snap)[SNAPS][M]) {
     float rk_[3][M], rq_[3][M], ra_[3], rb_[3], rv_[3], x[M];
     auto load_token = [&](int tt, int slot) {
       lds_slice<D, L>(&SK(buf)[tt * D], lane, rk_[slot]);
@@ -255,9 +255,9 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
       const int cur = tt % 3, nxt = (tt + 1) % 3;
       if (tt + 2 < TS) load_token(tt + 2, (tt + 2) % 3);
       row_update<D, L>(s, row_delta(rb_[cur], rv_[cur], u), rk_[cur], x);
-      if (tt == 15 && TS == 32) {  // state after the stage's 16th token (a C = 16 boundary)
+      if (tt % 16 == 15 && tt + 1 < TS) {  // the state at a possible chunk boundary
 #pragma unroll
-        for (int e = 0; e < M; ++e) snap[e] = s[e];
+        for (int e = 0; e < M; ++e) snap[tt / 16][e] = s[e];
       }
       if (tt + 1 < TS) {
         row_decay<D, L>(s, ra_[nxt], x);
@@ -278,8 +278,8 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
     }
   };
 
-  // Stages start at in-sequence index 0 and every admitted C is a multiple of 16, so a chunk
-  // boundary (j + 1) % C == 0 falls on token 15 or 31 of a stage. `done` = tokens absorbed.
+  // A chunk boundary (j + 1) % C == 0 falls on a token 16 m - 1 of a stage (see TS above).
+  // `done` = tokens absorbed.
   const int chunk_shift = __builtin_ctz((unsigned)p.chunk);
   auto store_chunk_state = [&](int64_t done, const float (&st)[M]) {
     if constexpr (MODE == kTrainer) {
@@ -313,9 +313,10 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
     }
     if (nt == TS) {
       if constexpr (L >= 8) {
-        float snap[M];
+        float snap[SNAPS][M];
         run_stage_pipelined(buf, snap);
-        if constexpr (TS == 32) store_chunk_state(t0 + 16, snap);
+#pragma unroll
+        for (int m = 0; m + 1 < TS / 16; ++m) store_chunk_state(t0 + 16 * (m + 1), snap[m]);
       } else {
 #pragma unroll
         for (int tt = 0; tt < TS; ++tt) run_token(buf, tt);
@@ -387,17 +388,21 @@ hipError_t launch(const void *fn, int64_t grid, Args args, hipStream_t stream) {
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
 }
 
-template <int D, int L>
+template <int D, int L, int TS>
 hipError_t scan_dl(const ScanArgs &a, hipStream_t st) {
   const int64_t grid = scan_grid(a, L);
-  const bool trainer = a.mode == kTrainer;
   const void *fn;
-  if (a.bf16)
-    fn = trainer ? (const void *)cpr_scan_kernel<D, L, true, kTrainer>
-                 : (const void *)cpr_scan_kernel<D, L, true, kPrefill>;
-  else
-    fn = trainer ? (const void *)cpr_scan_kernel<D, L, false, kTrainer>
-                 : (const void *)cpr_scan_kernel<D, L, false, kPrefill>;
+  if (a.mode == kTrainer) {
+    if constexpr (TS == 64) {  // 64-token stages serve the prefill case only
+      return hipErrorInvalidValue;
+    } else {
+      fn = a.bf16 ? (const void *)cpr_scan_kernel<D, L, TS, true, kTrainer>
+                  : (const void *)cpr_scan_kernel<D, L, TS, false, kTrainer>;
+    }
+  } else {
+    fn = a.bf16 ? (const void *)cpr_scan_kernel<D, L, TS, true, kPrefill>
+                : (const void *)cpr_scan_kernel<D, L, TS, false, kPrefill>;
+  }
   return launch(fn, grid, a, st);
 }
 
@@ -409,13 +414,12 @@ hipError_t decode_dl(const DecodeArgs &a, hipStream_t st) {
 }
 
 template <int D>
-hipError_t scan_d(const ScanArgs &a, int L, hipStream_t st) {
-  switch (L) {
-    case 16: return scan_dl<D, 16>(a, st);
-    case 8: return scan_dl<D, 8>(a, st);
-    case 4: return scan_dl<D, 4>(a, st);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t scan_d(const ScanArgs &a, int L, int TS, hipStream_t st) {
+  if (L == 16 && TS == 64) return scan_dl<D, 16, 64>(a, st);
+  if (L == 16 && TS == 32) return scan_dl<D, 16, 32>(a, st);
+  if (L == 8 && TS == 32) return scan_dl<D, 8, 32>(a, st);
+  if (L == 4 && TS == 16) return scan_dl<D, 4, 16>(a, st);
+  return hipErrorInvalidValue;
 }
 
 template <int D>
@@ -440,12 +444,12 @@ int64_t decode_grid(const DecodeArgs &a, int L) {
   return (int64_t)a.num_seqs * a.num_v_heads * ((a.d_v + rows - 1) / rows);
 }
 
-hipError_t launch_scan(const ScanArgs &a, int L, hipStream_t st) {
+hipError_t launch_scan(const ScanArgs &a, int L, int TS, hipStream_t st) {
   switch (a.d_k) {
-    case 16: return scan_d<16>(a, L, st);
-    case 32: return scan_d<32>(a, L, st);
-    case 64: return scan_d<64>(a, L, st);
-    case 128: return scan_d<128>(a, L, st);
+    case 16: return scan_d<16>(a, L, TS, st);
+    case 32: return scan_d<32>(a, L, TS, st);
+    case 64: return scan_d<64>(a, L, TS, st);
+    case 128: return scan_d<128>(a, L, TS, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -126,7 +126,8 @@ int64_t linear_grid(const LinearArgs &args);
 hipError_t launch_linear(const LinearArgs &args, hipStream_t stream);
 
 // Enqueue the kernels. lanes_per_row is 16, 8 or 4. Return the HIP launch status.
-hipError_t launch_scan(const ScanArgs &args, int lanes_per_row, hipStream_t stream);
+hipError_t launch_scan(const ScanArgs &args, int lanes_per_row, int stage_tokens,
+                       hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &args, int lanes_per_row, hipStream_t stream);
 
 // Number of workgroups a scan or decode launch uses (for the host-side size claims).
