@@ -73,14 +73,15 @@ int scan_lanes(const ScanArgs &a) {
   return 4;
 }
 
-// Tokens per LDS stage of the scan: 64 for a prefill with a lone wave per SIMD at 16 lanes
-// per row (its 149 KiB of LDS at d_k = 128 then fits the one workgroup per CU it needs;
-// measured 3.7 % faster than 32 on the long-context prefill; the trainer case, which keeps
-// the state at every 16-token point of a stage for the chunk boundaries, then needs more
-// than 256 registers and ran 3.3 times slower), 32 for 8 or 16 lanes otherwise (two
+// Tokens per LDS stage of the scan: 64 for a lone wave per SIMD at 16 lanes per row with
+// bf16 inputs (its 149 KiB of LDS at d_k = 128 then fits the one workgroup per CU it needs;
+// measured 3.7 % faster than 32 on the long-context prefill), for the trainer case only
+// when C >= 64. Chunk boundaries inside a 64-token stage would have to be kept in
+// registers, and binary32 inputs double the staging registers: either takes the kernel
+// past 256 registers, which ran 3.3 times slower. 32 for 8 or 16 lanes otherwise (two
 // workgroups per CU), 16 for 4 lanes per row.
 int scan_stage_tokens(const ScanArgs &a, int L) {
-  if (L == 16 && a.mode == kPrefill) {
+  if (L == 16 && a.bf16 && (a.mode == kPrefill || a.chunk >= 64)) {
     const int64_t rows = (int64_t)a.num_seqs * a.num_v_heads * a.d_v;
     return rows / 4 <= device_simds() ? 64 : 32;
   }

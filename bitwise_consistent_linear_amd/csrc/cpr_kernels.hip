@@ -29,9 +29,9 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-// TS, the tokens staged in LDS at a time, is chosen by the launcher: 64 for a prefill with a
-// lone wave per SIMD at 16 lanes per row, 32 for 8 or 16 lanes per row otherwise, 16 for 4
-// (where occupancy matters). Longer stages halve the per-stage barrier and pipeline restart but
+// TS, the tokens staged in LDS at a time, is chosen by the launcher: 64 for a lone wave per
+// SIMD at 16 lanes per row with bf16 inputs (a trainer launch only when C >= 64), 32 for 8
+// or 16 lanes per row otherwise, 16 for 4 (where occupancy matters). Longer stages halve the per-stage barrier and pipeline restart but
 // take more LDS. Stages start at in-sequence index 0 and every admitted C is a multiple of
 // 16, so a chunk boundary falls on a token 16 m - 1 of a stage.
 // ----------------------------------------------------------------------------- kernels
@@ -43,7 +43,11 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
   static_assert(TS % 16 == 0, "a stage holds whole 16-token groups");
   constexpr int ROWS = kThreads / L;
   constexpr int M = D / L;
-  constexpr int SNAPS = TS / 16 > 1 ? TS / 16 - 1 : 1;  // chunk boundaries inside a stage
+  // Chunk boundaries inside a full stage (after its tokens 15, 31, ...) are kept from the
+  // registers and stored after the stage; a trainer launch with 64-token stages is made only
+  // for C >= 64, whose boundaries fall on stage ends.
+  constexpr bool INNER = MODE == kTrainer && TS <= 32;
+  constexpr int SNAPS = INNER && TS / 16 > 1 ? TS / 16 - 1 : 1;
   constexpr int GROUPS = D / 4;  // float4 groups per staged k or q vector
   constexpr int KQ_ITEMS = TS * GROUPS, V_ITEMS = TS * ROWS;
   constexpr int KQ_PER = (KQ_ITEMS + kThreads - 1) / kThreads;
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
       const int cur = tt % 3, nxt = (tt + 1) % 3;
       if (tt + 2 < TS) load_token(tt + 2, (tt + 2) % 3);
       row_update<D, L>(s, row_delta(rb_[cur], rv_[cur], u), rk_[cur], x);
-      if (tt % 16 == 15 && tt + 1 < TS) {  // the state at a possible chunk boundary
+      if (INNER && tt % 16 == 15 && tt + 1 < TS) {  // the state at a possible chunk boundary
 #pragma unroll
         for (int e = 0; e < M; ++e) snap[tt / 16][e] = s[e];
       }
@@ -315,8 +319,10 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
       if constexpr (L >= 8) {
         float snap[SNAPS][M];
         run_stage_pipelined(buf, snap);
+        if constexpr (INNER) {
 #pragma unroll
-        for (int m = 0; m + 1 < TS / 16; ++m) store_chunk_state(t0 + 16 * (m + 1), snap[m]);
+          for (int m = 0; m + 1 < TS / 16; ++m) store_chunk_state(t0 + 16 * (m + 1), snap[m]);
+        }
       } else {
 #pragma unroll
         for (int tt = 0; tt < TS; ++tt) run_token(buf, tt);
@@ -392,13 +398,13 @@ template <int D, int L, int TS>
 hipError_t scan_dl(const ScanArgs &a, hipStream_t st) {
   const int64_t grid = scan_grid(a, L);
   const void *fn;
-  if (a.mode == kTrainer) {
-    if constexpr (TS == 64) {  // 64-token stages serve the prefill case only
-      return hipErrorInvalidValue;
-    } else {
-      fn = a.bf16 ? (const void *)cpr_scan_kernel<D, L, TS, true, kTrainer>
-                  : (const void *)cpr_scan_kernel<D, L, TS, false, kTrainer>;
-    }
+  if constexpr (TS > 32) {  // bf16 inputs only; a trainer launch needs C >= TS
+    if (!a.bf16 || (a.mode == kTrainer && a.chunk < TS)) return hipErrorInvalidValue;
+    fn = a.mode == kTrainer ? (const void *)cpr_scan_kernel<D, L, TS, true, kTrainer>
+                            : (const void *)cpr_scan_kernel<D, L, TS, true, kPrefill>;
+  } else if (a.mode == kTrainer) {
+    fn = a.bf16 ? (const void *)cpr_scan_kernel<D, L, TS, true, kTrainer>
+                : (const void *)cpr_scan_kernel<D, L, TS, false, kTrainer>;
   } else {
     fn = a.bf16 ? (const void *)cpr_scan_kernel<D, L, TS, true, kPrefill>
                 : (const void *)cpr_scan_kernel<D, L, TS, false, kPrefill>;
@@ -415,7 +421,7 @@ hipError_t decode_dl(const DecodeArgs &a, hipStream_t st) {
 
 template <int D>
 hipError_t scan_d(const ScanArgs &a, int L, int TS, hipStream_t st) {
-  if (L == 16 && TS == 64) return scan_dl<D, 16, 64>(a, st);
+  if (L == 16 && TS == 64 && a.bf16) return scan_dl<D, 16, 64>(a, st);
   if (L == 16 && TS == 32) return scan_dl<D, 16, 32>(a, st);
   if (L == 8 && TS == 32) return scan_dl<D, 8, 32>(a, st);
   if (L == 4 && TS == 16) return scan_dl<D, 4, 16>(a, st);
