@@ -81,6 +81,10 @@ SMALL = [
     ("d128_dv72", [45, 19], 2, 4, 128, 72, 32, False, False),
     ("d16_dv256", [20], 1, 1, 16, 256, 16, True, True),
     ("d128_empty_batch_of_zero_lengths", [0, 0, 0], 1, 2, 128, 128, 64, True, True),
+    # few rows and bf16: at 16 lanes per row the scan stages 64 tokens at a time, and chunk
+    # boundaries fall on every second or fourth stage end
+    ("d128_bf16_c128_long_stages", [300, 129, 64], 1, 2, 128, 128, 128, True, True),
+    ("d128_bf16_c256_long_stages", [520, 255], 1, 1, 128, 128, 256, True, False),
 ]
 
 
