@@ -38,8 +38,11 @@ constexpr int kThreads = 256;
 
 using namespace io;
 
+// At 4 lanes per row the scan is issue-bound with many waves to run: it asks for three
+// waves per SIMD (at most 168 registers), which hides each wave's dependency chains.
 template <int D, int L, int TS, bool BF16, int MODE>
-__global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(L == 4 ? 3 : 1)))
+void cpr_scan_kernel(const ScanArgs p) {
   static_assert(TS % 16 == 0, "a stage holds whole 16-token groups");
   constexpr int ROWS = kThreads / L;
   constexpr int M = D / L;
@@ -146,7 +149,9 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
   // Byte offsets of this thread's staged loads and o stores inside one full stage, fixed for
   // the whole scan. A full stage adds them to scalar stage bases, so its global accesses
   // need no per-stage 64-bit address arithmetic. The host admits Hv * max(d_k, d_v) <= 2^20,
-  // so every offset inside a stage of at most 32 tokens fits in 32 bits.
+  // so every offset inside a stage of at most 64 tokens fits in 32 bits. Used where stages
+  // are pipelined (L >= 8); at 4 lanes per row the registers go to a third wave instead.
+  constexpr bool FIXED = L >= 8;
   constexpr uint32_t EL = BF16 ? 2 : 4;
   const uint32_t kq_tok = (uint32_t)Hk * D;  // q/k elements per token
   uint32_t kq_off[KQ_PER], v_off[V_PER], o_off[V_PER];
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
     }
   };
   auto write_o = [&](int64_t t0, int nt, int buf) {
-    if (nt == TS) {  // full stage: scalar base plus the fixed offsets
+    if (FIXED && nt == TS) {  // full stage: scalar base plus the fixed offsets
       char *ob = reinterpret_cast<char *>(p.o + (bos + t0) * vstride);
 #pragma unroll
       for (int j = 0; j < V_PER; ++j)
@@ -225,14 +230,18 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
         p.o[(bos + t0 + tt) * vstride + (int64_t)h * dv + r0 + r] = so[buf][e];
     }
   };
-  // One token of a stage, in row_token's plain order. Every lane of a row holds the same
-  // o_i and stores it (no branch), which keeps an unrolled stage in one basic block.
+  // One token of a stage, in row_token's order of operations (decay, key dot, delta,
+  // update, readout); q is read from LDS only once k is no longer needed, so the two are
+  // never held together. Every lane of a row holds the same o_i and stores it (no branch),
+  // which keeps an unrolled stage in one basic block.
   auto run_token = [&](int buf, int tt) {
-    float kr[M], qr[M];
+    float kr[M], qr[M], x[M];
     lds_slice<D, L>(&SK(buf)[tt * D], lane, kr);
+    row_decay<D, L>(s, sa[buf][tt], x);
+    const float u = contract_dot<D, L>(x, kr);
+    row_update<D, L>(s, row_delta(sb[buf][tt], sv[buf][tt * ROWS + row], u), kr, x);
     lds_slice<D, L>(&SQ(buf)[tt * D], lane, qr);
-    so[buf][tt * ROWS + row] =
-        row_token<D, L>(s, sa[buf][tt], sb[buf][tt], sv[buf][tt * ROWS + row], kr, qr);
+    so[buf][tt * ROWS + row] = contract_dot<D, L>(s, qr);
   };
 
   // A full stage, software-pipelined: the inputs of token t+2 are read from LDS while token
@@ -297,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
   const int64_t nstages = (Tn + TS - 1) / TS;
 
   if (Tn > 0) {
-    if (Tn >= TS)
+    if (FIXED && Tn >= TS)
       fetch_full(0);
     else
       fetch(0);
@@ -310,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void cpr_scan_kernel(const ScanArgs p) {
     const int nt = (int)(Tn - t0 < TS ? Tn - t0 : TS);
     const bool more = st + 1 < nstages;
     if (more) {  // global loads in flight while this stage computes
-      if (t0 + 2 * TS <= Tn)
+      if (FIXED && t0 + 2 * TS <= Tn)
         fetch_full(t0 + TS);
       else
         fetch(t0 + TS);
