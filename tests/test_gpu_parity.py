@@ -85,6 +85,10 @@ SMALL = [
     # boundaries fall on every second or fourth stage end
     ("d128_bf16_c128_long_stages", [300, 129, 64], 1, 2, 128, 128, 128, True, True),
     ("d128_bf16_c256_long_stages", [520, 255], 1, 1, 128, 128, 256, True, False),
+    # the largest admitted rows (d_v = 1024 at d_k = 128), and the largest admitted token
+    # width: Hv * max(d_k, d_v) = 2^20, the bound of the kernels' 32-bit in-stage offsets
+    ("d128_dv1024_max_rows", [40, 7], 1, 1, 128, 1024, 64, True, True),
+    ("max_head_width", [20, 3], 1024, 1024, 16, 1024, 16, True, False),
 ]
 
 
