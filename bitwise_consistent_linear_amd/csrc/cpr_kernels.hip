@@ -7,7 +7,7 @@
 // L lanes (cpr_row.hpp). No MFMA: each token is a matrix-vector step on a d_k x d_v state
 // whose every element is touched four times, not a dense contraction.
 //
-// Scan: tokens are staged 16 at a time - q and k of the (n, q/k head) in the order the
+// Scan: tokens are staged TS at a time - q and k of the (n, q/k head) in the order the
 // lanes read them, v of the workgroup's rows, a and b - into LDS as binary32 (bf16 widened
 // exactly) with coalesced loads; the token loop then runs from LDS and registers only. The
 // outputs o of a stage go back through LDS so that each token's ROWS values are stored
@@ -31,9 +31,10 @@ namespace {
 constexpr int kThreads = 256;
 // TS, the tokens staged in LDS at a time, is chosen by the launcher: 64 for a lone wave per
 // SIMD at 16 lanes per row with bf16 inputs (a trainer launch only when C >= 64), 32 for 8
-// or 16 lanes per row otherwise, 16 for 4 (where occupancy matters). Longer stages halve the per-stage barrier and pipeline restart but
-// take more LDS. Stages start at in-sequence index 0 and every admitted C is a multiple of
-// 16, so a chunk boundary falls on a token 16 m - 1 of a stage.
+// or 16 lanes per row otherwise, 16 for 4 (where occupancy matters). Longer stages halve
+// the per-stage barrier and pipeline restart but take more LDS. Stages start at in-sequence
+// index 0 and every admitted C is a multiple of 16, so a chunk boundary falls on a token
+// 16 m - 1 of a stage.
 // ----------------------------------------------------------------------------- kernels
 
 using namespace io;
