@@ -30,12 +30,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, spec sheet
-FP32_FMA_PEAK_TFLOPS = 78.6       # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (no packed fp32)
-FP32_PACKED_PEAK_TFLOPS = 157.3   # spec-sheet figure with packed fp32 (not used by these kernels)
+# fp32 vector peak: 256 CU x 4 SIMD x 2.4 GHz x 64 flop per SIMD-cycle. The kernels emit no
+# packed fp32; gfx950 still reaches this rate with plain instructions when two waves on a
+# SIMD issue one vector instruction each in the same four-cycle slot (measured by the probe
+# beside every run: valu_probe in the JSON line).
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 FP32_MFMA_PEAK_TFLOPS = 157.3     # dense binary32 matrix instructions (the linear region)
 METRIC = "GDN-CPR tokens/s (trainer_fwd, prefill), decode-step us, % of HBM peak"
 KERNEL_SOURCES = {  # sources whose hash a traffic summary must match to be used
     "cpr_scan_trainer_fwd": ["cpr_kernels.hip", "cpr_row.hpp", "cpr_io.hpp"],
+    "cpr_scan_engine_prefill": ["cpr_kernels.hip", "cpr_row.hpp", "cpr_io.hpp"],
+    "cpr_scan_long_context_trainer": ["cpr_kernels.hip", "cpr_row.hpp", "cpr_io.hpp"],
+    "cpr_scan_long_context_prefill": ["cpr_kernels.hip", "cpr_row.hpp", "cpr_io.hpp"],
+    "cpr_decode_engine_decode": ["cpr_kernels.hip", "cpr_row.hpp", "cpr_io.hpp"],
     "cpr_bwd_trainer": ["cpr_backward.hip", "cpr_row.hpp", "cpr_io.hpp"],
     "cpr2_two_level_trainer": ["cpr2.hip", "cpr_row.hpp", "cpr_io.hpp"],
 }
@@ -139,8 +146,67 @@ def timed(fn, steps, warmup):
 
 def roofline_alu(flops, ms):
     achieved = flops / (ms * 1e-3) / 1e12
-    return {"bound": "alu", "achieved": round(achieved, 3), "peak": FP32_FMA_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / FP32_FMA_PEAK_TFLOPS, 4)}
+    return {"bound": "alu", "achieved": round(achieved, 3), "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / FP32_VECTOR_PEAK_TFLOPS, 4)}
+
+
+def same_bits(x, y):
+    """Bitwise equality of two float32 device tensors (compared as int32 on the device)."""
+    import torch
+    return bool(torch.equal(x.contiguous().view(torch.int32), y.contiguous().view(torch.int32)))
+
+
+def verdict(checks):
+    """The parity verdict of one case: every check is a bitwise comparison on the device."""
+    return {"bitwise_exact": all(checks.values()), "checks": checks}
+
+
+def valu_probe():
+    """Vector-issue ceiling and shader clock of this GPU, from libgdn_probe.so: SIMD-cycles
+    per wave instruction for plain multiplies, fused multiply-adds and DPP adds with one, two
+    and four waves per SIMD, the fused multiply-add rate at two waves per SIMD, and the shader
+    clock (s_memtime against the 100 MHz s_memrealtime)."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "bitwise_consistent_linear_amd", "libgdn_probe.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    L.gdn_probe_valu.restype = ctypes.c_int
+    L.gdn_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    per_iter = L.gdn_probe_valu_insts_per_iter()
+    iters = 4000
+    out = {"unit": "SIMD-cycles per wave instruction at the measured clock"}
+    clocks = []
+    fma2 = None
+    for form, name in ((0, "v_mul_f32"), (1, "v_fmac_f32"), (2, "v_add_f32_dpp")):
+        row = {}
+        for wps in (1, 2, 4):
+            grid = 256 * wps
+            buf = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+            clk = torch.empty(grid * 2, dtype=torch.int64, device="cuda")
+            stream = torch.cuda.current_stream().cuda_stream
+            if L.gdn_probe_valu(form, wps, iters // 10, buf.data_ptr(), clk.data_ptr(), stream):
+                return None
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if L.gdn_probe_valu(form, wps, iters, buf.data_ptr(), clk.data_ptr(), stream):
+                return None
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            c = clk.view(grid, 2).double().sum(0)
+            ghz = float(c[0] / (c[1] / 100e6) / 1e9)
+            clocks.append(ghz)
+            insts_per_simd = wps * iters * per_iter
+            row[str(wps)] = round(ms * 1e-3 * ghz * 1e9 / insts_per_simd, 3)
+            if form == 1 and wps == 2:
+                fma2 = 2 * 64 * 1024 * insts_per_simd / (ms * 1e-3) / 1e12
+        out[name] = row
+    out["v_fmac_f32_TFLOPs_at_2_waves_per_simd"] = round(fma2, 1)
+    out["shader_clock_GHz"] = round(sum(clocks) / len(clocks), 3)
+    return out
 
 
 def hbm(bytes_, ms):
@@ -175,18 +241,25 @@ def write_traffic(fetch_csv, write_csv):
         return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
 
     def copy_kib(rs):
-        c = [float(r["Counter_Value"]) for r in rs
-             if "copyBuffer" in r["Kernel_Name"] and float(r["Counter_Value"]) > 1024]
-        if not c:
+        # the calibration copies are the first device-to-device copies of the run: --copy-probe
+        # makes them right after the library loads, before any upload
+        cp = sorted((int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in rs
+                    if "copyBuffer" in r["Kernel_Name"])
+        c = [v for _, v in cp[:3]]
+        if len(c) < 3 or min(c) < 1024:
             raise SystemExit("no calibration copy in the counter files")
         return statistics.median(c)
 
-    def per_kernel(rs, substr):
+    def per_kernel(rs, match):
         by = {}
         for r in rs:
-            if substr in r["Kernel_Name"]:
+            if match(r["Kernel_Name"], int(r["Grid_Size"])):
                 by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return {k: statistics.median(v) for k, v in by.items()}
+
+    def scan(mode, grid):  # one scan launch: the template's last argument is the case
+        return lambda name, g: ("cpr_scan_kernel<" in name and name.endswith(f", {mode}>(gdn::ScanArgs)")
+                                and g == grid)
 
     fr, wr = rows(fetch_csv, "FETCH_SIZE"), rows(write_csv, "WRITE_SIZE")
     cf, cw = copy_kib(fr), copy_kib(wr)
@@ -194,21 +267,44 @@ def write_traffic(fetch_csv, write_csv):
     write_scale = COPY_PROBE_BYTES / (cw * 1024)
     from bitwise_consistent_linear_amd import workloads as W
     w = W.trainer_fwd()
+    wp, wl, wd = W.engine_prefill(), W.long_context(), W.engine_decode()
+    threads = 256
+
+    def grid(wk, lanes):  # threads of a one-level launch at `lanes` lanes per row
+        rows = threads // lanes
+        return wk.num_seqs * wk.num_v_heads * -(-wk.d_v // rows) * threads
+
+    dec_state = wd.num_seqs * wd.num_v_heads * wd.d_v * wd.d_k * 4
     targets = [
-        ("cpr_scan_trainer_fwd", "cpr_scan_kernel",
+        ("cpr_scan_trainer_fwd", scan(0, grid(w, 16)),
          "trainer_fwd: 4 x 4096 tokens, 16 heads, d=128, C=64, bf16 q/k/v",
          scan_bytes(w, chunk_states=w.total_chunks)),
-        ("cpr_bwd_trainer", "cpr_bwd_",
+        ("cpr_scan_engine_prefill", scan(1, grid(wp, 4)),
+         "engine_prefill: 64 varlen sequences, 262144 tokens, 16 q/k / 32 v heads, d=128, "
+         "bf16 q/k/v; o and the final states", scan_bytes(wp, final_states=wp.num_seqs)),
+        ("cpr_scan_long_context_trainer", scan(0, grid(wl, 16)),
+         "long_context trainer_fwd: 1 x 131072 tokens, 16 q/k / 32 v heads, d=128, C=64",
+         scan_bytes(wl, chunk_states=wl.total_chunks)),
+        ("cpr_scan_long_context_prefill", scan(1, grid(wl, 16)),
+         "long_context prefill: 1 x 131072 tokens, 16 q/k / 32 v heads, d=128",
+         scan_bytes(wl, final_states=1)),
+        ("cpr_decode_engine_decode",
+         lambda name, g: "cpr_decode_kernel<" in name and g == grid(wd, 16),
+         "engine_decode: one decode step of 256 sequences, 16 q/k / 32 v heads, d=128, C=64 "
+         "(per step; a step that ends no chunk writes no resync checkpoint)",
+         decode_step_bytes(wd.num_seqs, wd.num_qk_heads, wd.num_v_heads, wd.d_k, wd.d_v, 2,
+                           wd.chunk) - dec_state / wd.chunk),
+        ("cpr_bwd_trainer", lambda name, g: "cpr_bwd_" in name,
          "trainer_bwd on the trainer_fwd workload (every backward kernel of one call)",
          bwd_bytes(w)),
-        ("cpr2_two_level_trainer", "cpr2_",
+        ("cpr2_two_level_trainer", lambda name, g: "cpr2_" in name,
          "two-level trainer_fwd on the trainer_fwd workload (every kernel of one call)",
          cpr2_bytes(w)),
     ]
-    for name, substr, workload, alg in targets:
-        kf, kw = per_kernel(fr, substr), per_kernel(wr, substr)
+    for name, match, workload, alg in targets:
+        kf, kw = per_kernel(fr, match), per_kernel(wr, match)
         if not kf or not kw:
-            raise SystemExit(f"no {substr} dispatch in the counter files")
+            raise SystemExit(f"no dispatch for {name} in the counter files")
         kernels = {k: {"fetch_kib": kf[k], "write_kib": kw.get(k, 0.0),
                        "hbm_bytes": int(kf[k] * 1024 * fetch_scale
                                         + kw.get(k, 0.0) * 1024 * write_scale)}
@@ -260,10 +356,22 @@ def bench_trainer(steps, warmup):
     kernel_ms = sum(per) / len(per)
     flops = flops_per_token_head(w.d_k, w.d_v) * w.total_tokens * w.num_v_heads
     nbytes = scan_bytes(w, chunk_states=tc)
-    return w, wall, kernel_ms, flops, nbytes
+    # parity, after the timed region: the prefill case on the same batch, and a repeat
+    po, fs = api.prefill(cu, q, k, v, a, b, chunk=w.chunk)
+    o2, cs2 = api.trainer_fwd(cu, q, k, v, a, b, chunk=w.chunk, total_chunks=tc)
+    torch.cuda.synchronize()
+    N, Tn = w.num_seqs, int(w.lengths[0])
+    last = cs.view(N, Tn // w.chunk, w.num_v_heads, w.d_v, w.d_k)[:, -1]
+    par = verdict({"prefill o == trainer o": same_bits(po, o),
+                   "prefill final state == trainer last chunk state": same_bits(fs, last),
+                   "repeat call: same o and chunk states": same_bits(o2, o) and same_bits(cs2, cs)})
+    outputs = (o.cpu().numpy(), cs.cpu().numpy())
+    del po, fs, o2, cs2, q, k, v, o, cs
+    return w, wall, kernel_ms, flops, nbytes, par, outputs
 
 
 def bench_prefill(steps, warmup):
+    import numpy as np
     import torch
     from bitwise_consistent_linear_amd import api
     from bitwise_consistent_linear_amd import workloads as W
@@ -282,15 +390,28 @@ def bench_prefill(steps, warmup):
     ms = sum(per) / len(per)
     flops = flops_per_token_head(w.d_k, w.d_v) * w.total_tokens * w.num_v_heads
     nbytes = scan_bytes(w, final_states=w.num_seqs)
-    del q, k, v, o
+    # parity, after the timed region: the trainer case's o on the same batch (no chunk states
+    # requested), and the final state of every sequence whose length is a multiple of C
+    # against its trainer's last chunk state
+    to, tcs = api.trainer_fwd(cu, q, k, v, a, b, chunk=w.chunk, total_chunks=w.total_chunks)
+    torch.cuda.synchronize()
+    coff = np.concatenate([[0], np.cumsum(L // w.chunk)])
+    whole = [n for n in range(w.num_seqs) if L[n] % w.chunk == 0 and L[n] > 0]
+    fin = all(same_bits(fs[n], tcs[int(coff[n + 1]) - 1]) for n in whole)
+    par = verdict({"trainer o == prefill o": same_bits(to, o),
+                   f"final state == last chunk state ({len(whole)} sequences of whole chunks)":
+                   fin})
+    del q, k, v, o, to, tcs
     return {"workload": f"engine_prefill: 64 varlen sequences (lognormal, {L.min()}..{L.max()} "
                         f"tokens), {L.sum()} tokens, 16 q/k / 32 v heads, d=128, C=64, bf16 q/k/v",
             "tokens_per_s": round(w.total_tokens / (wall / steps), 1),
             "ms_per_call": round(wall / steps * 1e3, 4), "kernel_ms": round(ms, 4),
-            "steps": steps, "roofline": roofline_alu(flops, ms), "hbm": hbm(nbytes, ms)}
+            "steps": steps,
+            "roofline": dict(roofline_alu(flops, ms), traffic=traffic_for("cpr_scan_engine_prefill")),
+            "hbm": hbm(nbytes, ms), "parity": par}
 
 
-def bench_trainer_bwd(steps, warmup, fwd_kernel_ms):
+def bench_trainer_bwd(steps, warmup, fwd_kernel_ms, verify=True):
     """gdn_cpr_trainer_bwd on the trainer workload, given seeded dL/do and dL/dS_final."""
     import torch
     from bitwise_consistent_linear_amd import api
@@ -316,7 +437,29 @@ def bench_trainer_bwd(steps, warmup, fwd_kernel_ms):
     wall, per = timed(step, steps, warmup)
     ms = sum(per) / len(per)
     flops = bwd_flops_per_token_head(w.d_k, w.d_v) * w.total_tokens * w.num_v_heads
-    del q, k, v, cs, ws, grads
+    if not verify:  # the counter runs: only the timed schedule's kernels
+        del q, k, v, cs, ws, grads
+        return {"kernel_ms": round(ms, 4)}
+    # parity, after the timed region: a repeat, and the other schedule (a reverse state pass,
+    # then every chunk in parallel), which must give the same bits
+    again = api.trainer_bwd(cu, q, k, v, a, b, cs, ddo, chunk=w.chunk, d_final_state=ddsf,
+                            total_chunks=tc, workspace=ws)
+    sched = os.environ.get("GDN_CPR_BWD_SCHEDULE")
+    os.environ["GDN_CPR_BWD_SCHEDULE"] = "chunks"
+    try:
+        other = api.trainer_bwd(cu, q, k, v, a, b, cs, ddo, chunk=w.chunk, d_final_state=ddsf,
+                                total_chunks=tc, workspace=ws)
+    finally:
+        if sched is None:
+            del os.environ["GDN_CPR_BWD_SCHEDULE"]
+        else:
+            os.environ["GDN_CPR_BWD_SCHEDULE"] = sched
+    torch.cuda.synchronize()
+    names = ("dq", "dk", "dv", "da", "db", "dS0")
+    par = verdict({"repeat call: same gradients": all(same_bits(again[g], grads[g]) for g in names),
+                   "chunk schedule == sequence schedule": all(same_bits(other[g], grads[g])
+                                                              for g in names)})
+    del q, k, v, cs, ws, grads, again, other
     return {"workload": "trainer_bwd: the trainer_fwd workload (4 x 4096 tokens, 16 heads, "
                         "d=128, C=64, bf16 q/k/v) given dL/do and dL/dS_final; writes dq, dk, "
                         "dv, da, db, dS0",
@@ -325,7 +468,7 @@ def bench_trainer_bwd(steps, warmup, fwd_kernel_ms):
             "fwd_plus_bwd_kernel_ms": round(fwd_kernel_ms + ms, 4),
             "workspace_bytes": int(need), "steps": steps,
             "roofline": dict(roofline_alu(flops, ms), traffic=traffic_for("cpr_bwd_trainer")),
-            "hbm": hbm(bwd_bytes(w), ms)}
+            "hbm": hbm(bwd_bytes(w), ms), "parity": par}
 
 
 def bench_linear(steps, warmup, M=16384, N=4096, K=4096):
@@ -341,7 +484,13 @@ def bench_linear(steps, warmup, M=16384, N=4096, K=4096):
     ms = sum(per) / len(per)
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
     nbytes = M * K * 2 + K * N * 2 + M * N * 4
-    del dx, dw, y
+    # parity, after the timed region: batch invariance - rows computed in a batch of 65
+    # equal the same rows of the full product
+    part = api.linear_fwd(dx[:65].contiguous(), dw)
+    torch.cuda.synchronize()
+    par = verdict({"rows of a 65-row batch == the same rows of the full batch":
+                   same_bits(part, y[:65])})
+    del dx, dw, y, part
     return {"workload": f"linear region: Y[{M}, {N}] = X[{M}, {K}] W[{K}, {N}], bf16 X and W "
                         "(widened exactly), binary32 Y, each output the 16-leaf contract dot",
             "ms_per_call": round(wall / steps * 1e3, 4), "kernel_ms": round(ms, 4),
@@ -349,7 +498,7 @@ def bench_linear(steps, warmup, M=16384, N=4096, K=4096):
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                          "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4)},
-            "hbm": hbm(nbytes, ms)}
+            "hbm": hbm(nbytes, ms), "parity": par}
 
 
 def cpr2_flops(w):
@@ -393,11 +542,17 @@ def bench_cpr2(steps, warmup, trainer_only=False):
     roof["traffic"] = traffic_for("cpr2_two_level_trainer")
     if trainer_only:
         return {"trainer_fwd_kernel_ms": round(mt, 4), "steps": steps, "roofline": roof}
-    wall_p, per_p = timed(lambda: api.cpr2_prefill(cu, q, k, v, a, b, chunk=w.chunk, o=o,
+    po = torch.empty_like(o)
+    wall_p, per_p = timed(lambda: api.cpr2_prefill(cu, q, k, v, a, b, chunk=w.chunk, o=po,
                                                    final_state=fs, total_chunks=tc,
                                                    workspace=ws), steps, warmup)
     mp = sum(per_p) / len(per_p)
-    del q, k, v, o, cs, fs, ws
+    torch.cuda.synchronize()
+    N, Tn = w.num_seqs, int(w.lengths[0])
+    checks = {"two-level prefill o == two-level trainer o": same_bits(po, o),
+              "two-level final state == last chunk state (whole chunks)":
+              same_bits(fs, cs.view(N, Tn // w.chunk, Hv, dv, dk)[:, -1])}
+    del q, k, v, o, po, cs, fs, ws
     torch.cuda.empty_cache()
     dec = bench_cpr2_decode()
     torch.cuda.empty_cache()
@@ -434,7 +589,8 @@ def bench_cpr2(steps, warmup, trainer_only=False):
             "prefill_kernel_ms": round(mp, 4),
             "flops": {"transitions": trans, "boundary_sweep": boundary, "outputs": outputs},
             "workspace_bytes": int(need), "steps": steps, "roofline": roof,
-            "hbm": hbm(cpr2_bytes(w), mt), "decode": dec, "larger_workloads": big}
+            "hbm": hbm(cpr2_bytes(w), mt), "decode": dec, "larger_workloads": big,
+            "parity": verdict(checks)}
 
 
 def bench_cpr2_decode(prefix=960, nsteps=504, warmup_steps=8):
@@ -467,6 +623,41 @@ def bench_cpr2_decode(prefix=960, nsteps=504, warmup_steps=8):
 
     wall, per = timed(step, nsteps, warmup_steps)
     ms = sum(per) / len(per)
+    del dec, ds
+    torch.cuda.empty_cache()
+    # parity, after the timed run: the two-level trainer and prefill over the whole
+    # 1512-token sequences; a fresh decoder from the prefix's final state must reproduce the
+    # trainer's o at every later position, its chunk states at every resync and the
+    # prefill's final state
+    log("cpr2 decode: parity against the two-level trainer on the 1512-token sequences")
+    fu = {key: up(getattr(w, key)) for key in ("cu_seqlens", "q", "k", "v", "a", "b")}
+    o_full, cs_full = api.cpr2_trainer_fwd(fu["cu_seqlens"], fu["q"], fu["k"], fu["v"], fu["a"],
+                                           fu["b"], chunk=C, total_chunks=w.total_chunks)
+    _, fs_full = api.cpr2_prefill(fu["cu_seqlens"], fu["q"], fu["k"], fu["v"], fu["a"],
+                                  fu["b"], chunk=C, total_chunks=w.total_chunks)
+    del fu
+    T = int(w.lengths[0])
+    o_seq = o_full.view(N, T, Hv, dv)
+    cs_seq = cs_full.view(N, T // C, Hv, dv, dk)
+    dp = {key: up(getattr(pre, key)) for key in ("q", "k", "v", "a", "b")}
+    _, fs = api.cpr2_prefill(up(pre.cu_seqlens), dp["q"], dp["k"], dp["v"], dp["a"], dp["b"],
+                             chunk=C, total_chunks=pre.total_chunks)
+    del dp
+    dec = api.Cpr2Decoder(N, Hk, Hv, dk, dv, C, torch.bfloat16, "cuda", initial_state=fs)
+    del fs
+    ds = {key: up(x) for key, x in steps.items()}
+    ok_o = ok_rs = True
+    for s in range(T - prefix):
+        dec.step(ds["pos"][s], ds["q"][s], ds["k"][s], ds["v"][s], ds["a"][s], ds["b"][s],
+                 o=o, resync_states=rs)
+        ok_o = ok_o and same_bits(o, o_seq[:, prefix + s])
+        if (prefix + s + 1) % C == 0:
+            ok_rs = ok_rs and same_bits(rs, cs_seq[:, (prefix + s + 1) // C - 1])
+    checks = {f"two-level decode o == two-level trainer o ({T - prefix} steps)": ok_o,
+              "two-level resyncs == two-level trainer chunk states": ok_rs,
+              "two-level decode end state == two-level prefill final state":
+              same_bits(dec.state, fs_full)}
+    del dec, ds, o_full, cs_full, fs_full
     el = 2
     state = N * Hv * dv * dk * 4
     tok = N * (Hk * dk * el + Hv * dv * el + Hv * 8)
@@ -479,7 +670,6 @@ def bench_cpr2_decode(prefix=960, nsteps=504, warmup_steps=8):
     gbs = per_step / (ms * 1e-3) / 1e9
     boundary_steps = [p for s, p in enumerate(per) if (prefix + warmup_steps + s + 1) % C == 0]
     other = [p for s, p in enumerate(per) if (prefix + warmup_steps + s + 1) % C != 0]
-    del dec, ds
     return {"workload": f"engine_decode workload (256 sequences, 16 q/k / 32 v heads, d=128, "
                         f"C=64), two-level prefill of {prefix} tokens, then {nsteps} steps "
                         f"({warmup_steps} untimed)",
@@ -489,7 +679,7 @@ def bench_cpr2_decode(prefix=960, nsteps=504, warmup_steps=8):
             "us_other_step": round(sum(other) / max(1, len(other)) * 1e3, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
-            "algorithmic_bytes_per_step": int(per_step)}
+            "algorithmic_bytes_per_step": int(per_step), "parity": verdict(checks)}
 
 
 def bench_decode_after_prefill(w, prefix, nsteps, warmup_steps, label):
@@ -548,6 +738,39 @@ def bench_decode_after_prefill(w, prefix, nsteps, warmup_steps, label):
             "algorithmic_bytes_per_step": int(nbytes)}
 
 
+def verify_decode(w, prefix, nsteps, o_seq, cs_seq, fs_ref):
+    """Parity of the decode case, after its timed run: prefill `prefix` tokens again, then
+    decode `nsteps` steps one by one; every step's o must equal the trainer's o at that
+    position (o_seq [N, T, Hv, dv]), every resync checkpoint the trainer's chunk state there
+    (cs_seq [N, T // C, Hv, dv, dk]) and, when the steps reach the end of every sequence,
+    the state the prefill of all tokens ends with (fs_ref)."""
+    import torch
+    from bitwise_consistent_linear_amd import api
+    from bitwise_consistent_linear_amd import workloads as W
+    pre, steps = W.split_for_decode(w, prefix)
+    dp = {k: up(getattr(pre, k)) for k in ("q", "k", "v", "a", "b")}
+    _, state = api.prefill(up(pre.cu_seqlens), dp["q"], dp["k"], dp["v"], dp["a"], dp["b"],
+                           chunk=w.chunk)
+    del dp
+    ds = {k: up(x) for k, x in steps.items()}
+    rs = torch.empty_like(state)
+    o = torch.empty((w.num_seqs, w.num_v_heads, w.d_v), dtype=torch.float32, device="cuda")
+    ok_o = ok_rs = True
+    resyncs = 0
+    for s in range(nsteps):
+        api.decode_step(ds["pos"][s], ds["q"][s], ds["k"][s], ds["v"][s], ds["a"][s],
+                        ds["b"][s], state, chunk=w.chunk, o=o, resync_states=rs)
+        ok_o = ok_o and same_bits(o, o_seq[:, prefix + s])
+        if (prefix + s + 1) % w.chunk == 0:
+            resyncs += 1
+            ok_rs = ok_rs and same_bits(rs, cs_seq[:, (prefix + s + 1) // w.chunk - 1])
+    checks = {f"decode o == trainer o ({nsteps} steps)": ok_o,
+              f"resync checkpoints == trainer chunk states ({resyncs})": ok_rs}
+    if fs_ref is not None:
+        checks["decode end state == prefill final state"] = same_bits(state, fs_ref)
+    return checks
+
+
 def copy_probe_gbs(nbytes=1 << 30, reps=5):
     """A plain device copy of nbytes (read once, written once), timed with HIP events: the
     HBM rate a streaming kernel can reach on this GPU, beside the 8 TB/s peak."""
@@ -560,18 +783,38 @@ def copy_probe_gbs(nbytes=1 << 30, reps=5):
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
-def bench_decode():
+def bench_decode(verify=True, nsteps=504):
+    import torch
+    from bitwise_consistent_linear_amd import api
     from bitwise_consistent_linear_amd import workloads as W
     w = W.engine_decode()
     log("engine_decode: N=256, 1000-token prefill, 512 decode steps, 16/32 heads, d=128")
-    r = bench_decode_after_prefill(w, 1000, 504, 8, "engine_decode")
+    r = bench_decode_after_prefill(w, 1000, nsteps, 8, "engine_decode")
+    torch.cuda.empty_cache()
+    if verify:
+        # the trainer and prefill cases over the whole 1512-token sequences
+        log("engine_decode: parity against trainer_fwd on the 1512-token sequences")
+        cu, q, k, v, a, b = (up(x) for x in (w.cu_seqlens, w.q, w.k, w.v, w.a, w.b))
+        o_full, cs_full = api.trainer_fwd(cu, q, k, v, a, b, chunk=w.chunk,
+                                          total_chunks=w.total_chunks)
+        _, fs_full = api.prefill(cu, q, k, v, a, b, chunk=w.chunk)
+        del q, k, v, a, b
+        N, T = w.num_seqs, int(w.lengths[0])
+        checks = verify_decode(w, 1000, T - 1000,
+                               o_full.view(N, T, w.num_v_heads, w.d_v),
+                               cs_full.view(N, T // w.chunk, w.num_v_heads, w.d_v, w.d_k),
+                               fs_full)
+        r["parity"] = verdict(checks)
+        del o_full, cs_full, fs_full
+        torch.cuda.empty_cache()
     r["copy_probe_GBs"] = copy_probe_gbs()
     r["workload"] = ("engine_decode: 256 sequences, 16 q/k / 32 v heads, d=128, C=64, fp32 "
-                     "state in HBM, prefill 1000 tokens then 512 steps (8 untimed)")
+                     f"state in HBM, prefill 1000 tokens then {nsteps + 8} steps (8 untimed)")
+    r["roofline"]["traffic"] = traffic_for("cpr_decode_engine_decode")
     return r
 
 
-def bench_long(steps):
+def bench_long(steps, scans_only=False):
     import numpy as np
     import torch
     from bitwise_consistent_linear_amd import api
@@ -586,35 +829,57 @@ def bench_long(steps):
     wall_t, per_t = timed(lambda: api.trainer_fwd(cu, q, k, v, a, b, chunk=64, o=o,
                                                   chunk_states=cs, total_chunks=w.total_chunks),
                           steps, 1)
-    wall_p, per_p = timed(lambda: api.prefill(cu, q, k, v, a, b, chunk=64, o=o, final_state=fs),
+    po = torch.empty_like(o)
+    wall_p, per_p = timed(lambda: api.prefill(cu, q, k, v, a, b, chunk=64, o=po, final_state=fs),
                           steps, 1)
-    del q, k, v, o, cs
+    del q, k, v
+    torch.cuda.synchronize()
+    checks = {"prefill o == trainer o": same_bits(po, o),
+              "prefill final state == trainer last chunk state": same_bits(fs, cs[-1:])}
+    del po
     torch.cuda.empty_cache()
     flops = flops_per_token_head(w.d_k, w.d_v) * w.total_tokens * w.num_v_heads
     mt, mp = sum(per_t) / len(per_t), sum(per_p) / len(per_p)
+    if scans_only:
+        return {"trainer_fwd_kernel_ms": round(mt, 3), "prefill_kernel_ms": round(mp, 3),
+                "parity": verdict(checks)}
     P, S = w.extra["prefix"], w.extra["steps"]
     cut = W.Workload("long_context_decode", np.array([0, P + S], np.int32), w.q[:P + S],
                      w.k[:P + S], w.v[:P + S], w.a[:P + S], w.b[:P + S], w.chunk, w.bf16)
     dec = bench_decode_after_prefill(cut, P, S - 8, 8, "long_context decode")
+    checks.update({f"after {P} tokens: {name}": ok for name, ok in verify_decode(
+        cut, P, S, o.view(1, -1, w.num_v_heads, w.d_v)[:, :P + S],
+        cs.view(1, -1, w.num_v_heads, w.d_v, w.d_k), None).items()})
+    del o, cs
+    torch.cuda.empty_cache()
     return {"workload": "long_context: 1 x 131072 tokens, 16 q/k / 32 v heads, d=128, C=64, "
                         "bf16 q/k/v, a ~ U(0.95, 1)",
             "trainer_fwd_tokens_per_s": round(w.total_tokens / (wall_t / steps), 1),
             "trainer_fwd_kernel_ms": round(mt, 3),
-            "trainer_fwd_roofline": roofline_alu(flops, mt),
+            "trainer_fwd_roofline": dict(roofline_alu(flops, mt),
+                                         traffic=traffic_for("cpr_scan_long_context_trainer")),
             "trainer_fwd_hbm": hbm(scan_bytes(w, chunk_states=w.total_chunks), mt),
             "prefill_tokens_per_s": round(w.total_tokens / (wall_p / steps), 1),
             "prefill_kernel_ms": round(mp, 3),
-            "decode_after_65536": dec}
+            "prefill_roofline": dict(roofline_alu(flops, mp),
+                                     traffic=traffic_for("cpr_scan_long_context_prefill")),
+            "prefill_hbm": hbm(scan_bytes(w, final_states=1), mp),
+            "decode_after_65536": dec, "parity": verdict(checks)}
 
 
-def cpu_baseline(w):
-    """The CPU oracle on the whole trainer_fwd workload (all outputs), on the host's cores."""
+def cpu_baseline(w, gpu_outputs):
+    """The CPU oracle on the whole trainer_fwd workload (all outputs), on the host's cores,
+    and whether its outputs equal the GPU's trainer_fwd outputs bit for bit."""
+    import numpy as np
     from oracle import oracle as O
     threads = min(16, O.default_threads())
     t0 = time.perf_counter()
-    O.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=w.chunk, want_chunk_states=True,
-           nthreads=threads)
+    ro, rcs, _ = O.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=w.chunk,
+                        want_chunk_states=True, nthreads=threads)
     dt = time.perf_counter() - t0
+    go, gcs = gpu_outputs
+    same = (np.array_equal(np.ascontiguousarray(go).view(np.uint32), ro.view(np.uint32))
+            and np.array_equal(np.ascontiguousarray(gcs).view(np.uint32), rcs.view(np.uint32)))
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -625,7 +890,8 @@ def cpu_baseline(w):
     return {"value": round(w.total_tokens / dt, 1), "unit": "tokens/s", "cores": threads,
             "kind": "oracle", "affinity_cores": O.default_threads(), "cpu_model": model,
             "sample": f"the whole trainer_fwd workload (4 x 4096 tokens, 16 heads, o and "
-                      f"chunk states), {dt:.2f} s on {threads} threads"}
+                      f"chunk states), {dt:.2f} s on {threads} threads",
+            "bitwise_equal_to_gpu_trainer_fwd": bool(same)}
 
 
 def main():
@@ -634,15 +900,15 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cases",
-                    choices=["all", "main", "bwd", "prefill", "decode", "linear", "cpr2",
+                    choices=["all", "main", "bwd", "prefill", "decode", "long", "linear", "cpr2",
                              "traffic"],
                     default="all",
-                    help="all: every case; main: trainer_fwd only; bwd / prefill / decode / "
-                         "linear / cpr2: trainer_fwd and the backward / the engine_prefill call "
-                         "/ the engine_decode steps / the linear region / the two-level reading "
-                         "(for profiling); traffic: "
-                         "trainer_fwd, the backward and the two-level trainer calls (for the "
-                         "counter runs)")
+                    help="all: every case; main: trainer_fwd only; bwd / prefill / decode / long "
+                         "/ linear / cpr2: trainer_fwd and the backward / the engine_prefill call "
+                         "/ the engine_decode steps / the long-context calls / the linear region "
+                         "/ the two-level reading (for profiling); traffic: a few calls of every "
+                         "one-level scan, the decode step, the backward and the two-level "
+                         "trainer (for the counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (untimed), the known-size "
@@ -674,13 +940,15 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         del x, y
-    w, wall, kernel_ms, flops, nbytes = bench_trainer(args.steps, args.warmup)
+    w, wall, kernel_ms, flops, nbytes, par, outputs = bench_trainer(args.steps, args.warmup)
     ms_per_step = wall / args.steps * 1e3
     roof = roofline_alu(flops, kernel_ms)
     traffic = traffic_for("cpr_scan_trainer_fwd")
     roof["traffic"] = traffic
     log(f"trainer_fwd: {ms_per_step:.3f} ms/step, kernel {kernel_ms:.3f} ms, "
-        f"{roof['achieved']} TFLOP/s")
+        f"{roof['achieved']} TFLOP/s, parity {par['bitwise_exact']}")
+    torch.cuda.empty_cache()
+    probe = valu_probe() if args.cases != "traffic" else None
     out = {
         "metric": METRIC,
         "value": round(w.total_tokens / (wall / args.steps), 1),
@@ -700,41 +968,49 @@ def main():
                    "global_batch": 4, "seq_len": 4096, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "hbm": hbm(nbytes, kernel_ms),
-        "frac_of_packed_fp32_spec_peak": round(roof["achieved"] / FP32_PACKED_PEAK_TFLOPS, 4),
+        "parity": par,
         "kernel_ms": round(kernel_ms, 4),
+        "valu_probe": probe,
         "contract_identity": api.contract_identity(64, 128).hex(),
     }
-    if args.cases == "all":
-        cases = {}
-        cases["trainer_bwd"] = bench_trainer_bwd(max(3, args.steps // 4), 1, kernel_ms)
-        torch.cuda.empty_cache()
-        cases["engine_prefill"] = bench_prefill(max(3, args.steps // 4), 1)
-        torch.cuda.empty_cache()
-        cases["engine_decode"] = bench_decode()
-        torch.cuda.empty_cache()
-        cases["long_context"] = bench_long(max(2, args.steps // 10))
-        torch.cuda.empty_cache()
-        cases["linear"] = bench_linear(max(3, args.steps // 4), 1)
-        torch.cuda.empty_cache()
-        cases["two_level"] = bench_cpr2(max(3, args.steps // 4), 1)
-        torch.cuda.empty_cache()
-        out["cases"] = cases
-    elif args.cases == "bwd":
-        out["cases"] = {"trainer_bwd": bench_trainer_bwd(max(3, args.steps // 4), 1, kernel_ms)}
-    elif args.cases == "prefill":
-        out["cases"] = {"engine_prefill": bench_prefill(max(3, args.steps // 4), 1)}
-    elif args.cases == "decode":
-        out["cases"] = {"engine_decode": bench_decode()}
-    elif args.cases == "linear":
-        out["cases"] = {"linear": bench_linear(max(3, args.steps // 4), 1)}
-    elif args.cases == "cpr2":
-        out["cases"] = {"two_level": bench_cpr2(max(3, args.steps // 4), 1)}
-    elif args.cases == "traffic":
-        out["cases"] = {"trainer_bwd": bench_trainer_bwd(max(3, args.steps // 4), 1, kernel_ms),
-                        "two_level": bench_cpr2(max(3, args.steps // 4), 1, trainer_only=True)}
+    steps4 = max(3, args.steps // 4)
+    runners = {
+        "trainer_bwd": lambda: bench_trainer_bwd(steps4, 1, kernel_ms),
+        "engine_prefill": lambda: bench_prefill(steps4, 1),
+        "engine_decode": lambda: bench_decode(),
+        "long_context": lambda: bench_long(max(2, args.steps // 10)),
+        "linear": lambda: bench_linear(steps4, 1),
+        "two_level": lambda: bench_cpr2(steps4, 1),
+    }
+    chosen = {"all": list(runners), "main": [], "bwd": ["trainer_bwd"],
+              "prefill": ["engine_prefill"], "decode": ["engine_decode"], "long": ["long_context"],
+              "linear": ["linear"], "cpr2": ["two_level"]}
+    if args.cases == "traffic":
+        runners.update({
+            "trainer_bwd": lambda: bench_trainer_bwd(3, 1, kernel_ms, verify=False),
+            "two_level": lambda: bench_cpr2(3, 1, trainer_only=True),
+            "engine_prefill": lambda: bench_prefill(2, 1),
+            "engine_decode": lambda: bench_decode(verify=False, nsteps=16),
+            "long_context": lambda: bench_long(1, scans_only=True),
+        })
+        names = ["trainer_bwd", "two_level", "engine_prefill", "engine_decode", "long_context"]
+    else:
+        names = chosen[args.cases]
+    if names:
+        out["cases"] = {}
+        for name in names:
+            out["cases"][name] = runners[name]()
+            torch.cuda.empty_cache()
+    def verdicts(node):  # every parity verdict in the line, nested ones included
+        if isinstance(node, dict):
+            if "bitwise_exact" in node and "checks" in node:
+                yield node["bitwise_exact"]
+            for child in node.values():
+                yield from verdicts(child)
+    out["parity_all_bitwise_exact"] = all(verdicts(out))
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the trainer_fwd workload")
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, outputs)
     print(json.dumps(out), flush=True)
 
 

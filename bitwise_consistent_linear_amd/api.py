@@ -127,7 +127,6 @@ def sha256(data: bytes) -> bytes:
 
 
 @lru_cache(maxsize=None)
-@lru_cache(maxsize=None)
 def contract_identity(chunk: int, d_k: int) -> bytes:
     out = ctypes.create_string_buffer(32)
     _check(lib().gdn_contract_identity(chunk, d_k, out))
@@ -167,6 +166,18 @@ def _need(t, name, dtypes, ndim=None):
     return t
 
 
+def _same_device(*named):
+    """Every tensor given (None entries skipped) on the device of the first one: the
+    library runs on the current device and cannot check where a pointer lives."""
+    present = [(n, t) for n, t in named if t is not None]
+    if not present:
+        return
+    dev = present[0][1].device
+    for n, t in present[1:]:
+        if t.device != dev:
+            raise ValueError(f"{n} is on {t.device}, expected {dev} like {present[0][0]}")
+
+
 def _qkv(q, k, v):
     torch = _torch()
     dt = (torch.float32, torch.bfloat16)
@@ -177,7 +188,27 @@ def _qkv(q, k, v):
         raise TypeError("q, k and v must share one dtype")
     if q.shape != k.shape:
         raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} differ")
+    if v.shape[0] != q.shape[0]:
+        raise ValueError(f"v has {v.shape[0]} rows, q and k {q.shape[0]}")
     return GDN_DTYPE_BF16 if q.dtype == torch.bfloat16 else GDN_DTYPE_F32
+
+
+def _out(t, name, shape):
+    """A caller-supplied fp32 output of exactly `shape` (the kernels write all of it)."""
+    torch = _torch()
+    _need(t, name, (torch.float32,), len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _chunk_states(t, name, total_chunks, Hv, dv, dk):
+    torch = _torch()
+    _need(t, name, (torch.float32,), 4)
+    if t.shape[0] < total_chunks or tuple(t.shape[1:]) != (Hv, dv, dk):
+        raise ValueError(f"{name} must be [>= {total_chunks}, {Hv}, {dv}, {dk}], "
+                         f"got {tuple(t.shape)}")
+    return t
 
 
 def _shape(N, q, v, chunk, dtype_code):
@@ -224,13 +255,13 @@ def trainer_fwd(cu_seqlens, q, k, v, a, b, *, chunk, initial_state=None, o=None,
         total_chunks = count_chunks(cu_seqlens, chunk)
     if o is None:
         o = torch.empty((T, Hv, dv), dtype=torch.float32, device=q.device)
-    _need(o, "o", (torch.float32,), 3)
+    _out(o, "o", (T, Hv, dv))
     if chunk_states is None:
         chunk_states = torch.empty((total_chunks, Hv, dv, dk), dtype=torch.float32,
                                    device=q.device)
-    _need(chunk_states, "chunk_states", (torch.float32,), 4)
-    if chunk_states.shape[0] < total_chunks:
-        raise ValueError("chunk_states has fewer rows than total_chunks")
+    _chunk_states(chunk_states, "chunk_states", total_chunks, Hv, dv, dk)
+    _same_device(("q", q), ("k", k), ("v", v), ("a", a), ("b", b), ("cu_seqlens", cu_seqlens),
+                 ("initial_state", initial_state), ("o", o), ("chunk_states", chunk_states))
     shape = _shape(N, q, v, chunk, dt)
     ident = identity if identity is not None else contract_identity(chunk, dk)
     _check(lib().gdn_cpr_trainer_fwd(ctypes.byref(shape), ident, _ptr(cu_seqlens), T,
@@ -253,10 +284,12 @@ def prefill(cu_seqlens, q, k, v, a, b, *, chunk, initial_state=None, o=None, fin
     _state(initial_state, "initial_state", N, Hv, dv, dk)
     if o is None:
         o = torch.empty((T, Hv, dv), dtype=torch.float32, device=q.device)
-    _need(o, "o", (torch.float32,), 3)
+    _out(o, "o", (T, Hv, dv))
     if final_state is None:
         final_state = torch.empty((N, Hv, dv, dk), dtype=torch.float32, device=q.device)
     _state(final_state, "final_state", N, Hv, dv, dk)
+    _same_device(("q", q), ("k", k), ("v", v), ("a", a), ("b", b), ("cu_seqlens", cu_seqlens),
+                 ("initial_state", initial_state), ("o", o), ("final_state", final_state))
     shape = _shape(N, q, v, chunk, dt)
     ident = identity if identity is not None else contract_identity(chunk, dk)
     _check(lib().gdn_cpr_prefill(ctypes.byref(shape), ident, _ptr(cu_seqlens), T, _ptr(q),
@@ -279,11 +312,15 @@ def decode_step(pos, q, k, v, a, b, state, *, chunk, o=None, resync_states=None,
     if pos.shape[0] != N or v.shape[0] != N:
         raise ValueError("pos, q, k and v must have one row per sequence")
     _ab(a, b, N, Hv)
+    if state is None:
+        raise ValueError("state is required")
     _state(state, "state", N, Hv, dv, dk)
     _state(resync_states, "resync_states", N, Hv, dv, dk)
     if o is None:
         o = torch.empty((N, Hv, dv), dtype=torch.float32, device=q.device)
-    _need(o, "o", (torch.float32,), 3)
+    _out(o, "o", (N, Hv, dv))
+    _same_device(("q", q), ("k", k), ("v", v), ("a", a), ("b", b), ("pos", pos),
+                 ("state", state), ("o", o), ("resync_states", resync_states))
     shape = _shape(N, q, v, chunk, dt)
     ident = identity if identity is not None else contract_identity(chunk, dk)
     _check(lib().gdn_cpr_decode_step(ctypes.byref(shape), ident, _ptr(pos), _ptr(q), _ptr(k),
@@ -325,9 +362,7 @@ def trainer_bwd(cu_seqlens, q, k, v, a, b, chunk_states, d_o, *, chunk, initial_
         raise ValueError(f"d_o must be [{T}, {Hv}, {dv}], got {tuple(d_o.shape)}")
     if total_chunks is None:
         total_chunks = count_chunks(cu_seqlens, chunk)
-    _need(chunk_states, "chunk_states", (torch.float32,), 4)
-    if chunk_states.shape[0] < total_chunks or tuple(chunk_states.shape[1:]) != (Hv, dv, dk):
-        raise ValueError("chunk_states does not hold total_chunks states of this shape")
+    _chunk_states(chunk_states, "chunk_states", total_chunks, Hv, dv, dk)
     shapes = {"dq": (T, Hk, dk), "dk": (T, Hk, dk), "dv": (T, Hv, dv), "da": (T, Hv),
               "db": (T, Hv), "dS0": (N, Hv, dv, dk)}
     out = dict(out or {})
@@ -342,6 +377,10 @@ def trainer_bwd(cu_seqlens, q, k, v, a, b, chunk_states, d_o, *, chunk, initial_
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", (torch.uint8,), 1)
+    _same_device(("q", q), ("k", k), ("v", v), ("a", a), ("b", b), ("cu_seqlens", cu_seqlens),
+                 ("initial_state", initial_state), ("chunk_states", chunk_states),
+                 ("d_o", d_o), ("d_final_state", d_final_state), ("workspace", workspace),
+                 *[(name, out[name]) for name in shapes])
     ident = identity if identity is not None else contract_identity(chunk, dk)
     _check(lib().gdn_cpr_trainer_bwd(
         ctypes.byref(shape), ident, _ptr(cu_seqlens), T, _ptr(q), _ptr(k), _ptr(v), _ptr(a),
@@ -366,9 +405,8 @@ def linear_fwd(x, w, *, y=None, identity=None, stream=None):
     N = w.shape[1]
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    _need(y, "y", (torch.float32,), 2)
-    if tuple(y.shape) != (M, N):
-        raise ValueError(f"y must be [{M}, {N}]")
+    _out(y, "y", (M, N))
+    _same_device(("x", x), ("w", w), ("y", y))
     code = {torch.float32: GDN_DTYPE_F32, torch.bfloat16: GDN_DTYPE_BF16}
     shape = GdnLinearShape(M, N, K, code[x.dtype], code[w.dtype])
     ident = identity if identity is not None else contract_identity(64, 128)
@@ -389,7 +427,6 @@ def cpr2_contract_string(chunk: int, d_k: int) -> str:
     return buf.value.decode()
 
 
-@lru_cache(maxsize=None)
 @lru_cache(maxsize=None)
 def cpr2_contract_identity(chunk: int, d_k: int) -> bytes:
     out = ctypes.create_string_buffer(32)
@@ -427,7 +464,7 @@ def _cpr2_batch(prefill_case, cu_seqlens, q, k, v, a, b, chunk, initial_state, o
         total_chunks = count_chunks(cu_seqlens, chunk)
     if o is None:
         o = torch.empty((T, Hv, dv), dtype=torch.float32, device=q.device)
-    _need(o, "o", (torch.float32,), 3)
+    _out(o, "o", (T, Hv, dv))
     if prefill_case:
         if out_state is None:
             out_state = torch.empty((N, Hv, dv, dk), dtype=torch.float32, device=q.device)
@@ -436,12 +473,13 @@ def _cpr2_batch(prefill_case, cu_seqlens, q, k, v, a, b, chunk, initial_state, o
         if out_state is None:
             out_state = torch.empty((total_chunks, Hv, dv, dk), dtype=torch.float32,
                                     device=q.device)
-        _need(out_state, "chunk_states", (torch.float32,), 4)
-        if out_state.shape[0] < total_chunks:
-            raise ValueError("chunk_states has fewer rows than total_chunks")
+        _chunk_states(out_state, "chunk_states", total_chunks, Hv, dv, dk)
     shape = _shape(N, q, v, chunk, dt)
     workspace = _workspace(workspace, cpr2_workspace_bytes(shape, T, total_chunks, False),
                            q.device)
+    _same_device(("q", q), ("k", k), ("v", v), ("a", a), ("b", b), ("cu_seqlens", cu_seqlens),
+                 ("initial_state", initial_state), ("o", o), ("state output", out_state),
+                 ("workspace", workspace))
     ident = identity if identity is not None else cpr2_contract_identity(chunk, dk)
     fn = lib().gdn_cpr2_prefill if prefill_case else lib().gdn_cpr2_trainer_fwd
     state_ptr = _ptr(out_state) if (prefill_case or total_chunks) else None
@@ -502,7 +540,10 @@ class Cpr2Decoder:
         _state(resync_states, "resync_states", self.N, self.Hv, self.dv, self.dk)
         if o is None:
             o = torch.empty((self.N, self.Hv, self.dv), dtype=torch.float32, device=q.device)
-        _need(o, "o", (torch.float32,), 3)
+        _out(o, "o", (self.N, self.Hv, self.dv))
+        _same_device(("the decoder's state", self.state), ("q", q), ("k", k), ("v", v),
+                     ("a", a), ("b", b), ("pos", pos), ("o", o),
+                     ("resync_states", resync_states))
         ident = identity if identity is not None else cpr2_contract_identity(self.chunk,
                                                                              self.dk)
         _check(lib().gdn_cpr2_decode_step(

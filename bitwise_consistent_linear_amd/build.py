@@ -75,6 +75,24 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+PROBE_LIB = os.path.join(PKG, "libgdn_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile the measurement probes (csrc/probe.hip) into libgdn_probe.so, which bench.py
+    uses for the vector-issue ceiling and shader clock; the library proper does not link it."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-o", tmp, os.path.join(CSRC, "probe.hip")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed to build libgdn_probe.so")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 KERNEL_SOURCES = [s for s in SOURCES if s.endswith(".hip")]
 
 
@@ -100,3 +118,4 @@ def device_asm(out_path: str) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probe(verbose=True))

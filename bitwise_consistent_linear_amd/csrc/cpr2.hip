@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void cpr2_rows_kernel(const Cpr2Args p) {
 
   auto unit = [&](int blk) {
     int pair, rblock;
-    block_work(blk, units * Hv, RB, pair, rblock);
+    block_work(blk, units * Hv, RB, 1, pair, rblock);
     const int h = pair % Hv;
     const ChunkWork w = chunk_work(p, pair / Hv);
     if (!w.active || (!OUT && w.len < p.chunk)) return;  // uniform: full chunks' transitions
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(D * 2) void cpr2_boundary_kernel(const Cpr2Args p) 
   for (int blk = blockIdx.x; blk < total; blk += gridDim.x) {
     // the row blocks of a (sequence, head) on one XCD: they read the same A_c, once from HBM
     int pair, rblock;
-    block_work(blk, seqs * Hv, RB, pair, rblock);
+    block_work(blk, seqs * Hv, RB, 1, pair, rblock);
     const int h = pair % Hv;
     const int n = p.decode ? p.plan[kPlanHeader + pair / Hv] : pair / Hv;
     const int r0 = rblock * 32;

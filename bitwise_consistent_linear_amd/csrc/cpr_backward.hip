@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void cpr_bwd_state_kernel(const BwdArgs p
   const int Hv = p.num_v_heads, Hk = p.num_qk_heads, dv = p.d_v;
   const int rblocks = (dv + ROWS - 1) / ROWS;
   int pair, rblock;
-  block_work(blockIdx.x, p.num_seqs * Hv, rblocks, pair, rblock);
+  block_work(blockIdx.x, p.num_seqs * Hv, rblocks, Hv / Hk, pair, rblock);
   const int rank = pair / Hv;
   const int h = pair % Hv;
   const int r0 = rblock * ROWS;
@@ -298,14 +298,14 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
   int pair, rblock, n, h, c_hi, c_lo;
   int64_t bos, eos;
   if constexpr (SEQ) {
-    block_work(blockIdx.x, p.num_seqs * Hv, RB, pair, rblock);
+    block_work(blockIdx.x, p.num_seqs * Hv, RB, 1, pair, rblock);
     h = pair % Hv;
     n = ranked_sequence(p.cu_seqlens, p.num_seqs, p.total_tokens, pair / Hv, s_len, &s_pick);
     seq_range(p.cu_seqlens, n, p.total_tokens, bos, eos);
     c_hi = (int)((eos - bos + p.chunk - 1) / p.chunk) - 1;
     c_lo = 0;
   } else {
-    block_work(blockIdx.x, p.slots_max * Hv, RB, pair, rblock);
+    block_work(blockIdx.x, p.slots_max * Hv, RB, 1, pair, rblock);
     const int slot = pair / Hv;
     h = pair % Hv;
     if (slot >= p.plan[0]) return;  // uniform: this workgroup has no chunk

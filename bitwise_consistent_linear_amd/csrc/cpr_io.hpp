@@ -108,8 +108,8 @@ __device__ __forceinline__ void lds_slice(const float *vec, int lane, float (&r)
 
 // Token range of sequence n, clamped to [0, T) so that bad cu_seqlens cannot address
 // outside the buffers.
-__device__ __forceinline__ void seq_range(const int32_t *cu, int n, int64_t T, int64_t &bos,
-                                          int64_t &eos) {
+__host__ __device__ __forceinline__ void seq_range(const int32_t *cu, int n, int64_t T,
+                                                   int64_t &bos, int64_t &eos) {
   int64_t lo = cu[n], hi = cu[n + 1];
   lo = lo < 0 ? 0 : (lo > T ? T : lo);
   hi = hi < lo ? lo : (hi > T ? T : hi);
@@ -143,22 +143,31 @@ __device__ inline int ranked_sequence(const int32_t *cu, int N, int64_t T, int r
 }
 
 // Workgroup -> (head pair, row block), XCD-aware. The dispatcher hands workgroups to the
-// 8 XCDs (each with its own L2) in round-robin order of workgroup id. Pairs (work units of
-// one sequence and value head, in scheduling order) are taken 8 at a time; within such a
-// group, pair g*8+x gets every workgroup id congruent to x mod 8, so all row blocks of a
-// pair run on one XCD and read its q, k, a and b through one L2. A last group of fewer than
-// 8 pairs is laid out linearly.
+// 8 XCDs (each with its own L2) in round-robin order of workgroup id. A pair is one
+// sequence (in scheduling order) and value head; pair = unit * G + g, where a unit is one
+// sequence and q/k head and g runs over the G value heads that share that q/k head. Units
+// are taken 8 at a time; within such a group, unit u*8+x gets every workgroup id congruent
+// to x mod 8, so all row blocks of all G heads of a unit run on one XCD and read its q, k
+// (and each head's a and b) through one L2; consecutive workgroups of a unit alternate
+// between its heads, so the heads advance through the tokens side by side. A last group of
+// fewer than 8 units is laid out linearly. A bijection from [0, pairs * rblocks) onto
+// (pair, row block) for any G dividing pairs.
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ void block_work(int b, int pairs, int rblocks, int &pair, int &rb) {
-  const int group = b / (kXcds * rblocks), within = b % (kXcds * rblocks);
-  if (group < pairs / kXcds) {
-    pair = group * kXcds + within % kXcds;
-    rb = within / kXcds;
+__host__ __device__ __forceinline__ void block_work(int b, int pairs, int rblocks, int G,
+                                                    int &pair, int &rb) {
+  const int per_unit = G * rblocks, units = pairs / G;
+  const int group = b / (kXcds * per_unit), within = b % (kXcds * per_unit);
+  int unit, w;
+  if (group < units / kXcds) {
+    unit = group * kXcds + within % kXcds;
+    w = within / kXcds;
   } else {
-    pair = group * kXcds + within / rblocks;
-    rb = within % rblocks;
+    unit = group * kXcds + within / per_unit;
+    w = within % per_unit;
   }
+  pair = unit * G + w % G;
+  rb = w / G;
 }
 
 // The chunk slots of a packed batch, listed by one workgroup of 256 threads:
@@ -221,19 +230,33 @@ __device__ inline void chunk_plan(const int32_t *cu, int N, int64_t T, int C, in
   if (tid == 0) plan[0] = (int32_t)(s_carry_ceil < slots_max ? s_carry_ceil : slots_max);
 }
 
-// Index of sequence n's first chunk-boundary state: sum over m < n of floor(T_m / C).
-__device__ inline int64_t first_chunk_slot(const int32_t *cu, int n, int64_t T, int C, int *s_acc) {
+// Full chunks of sequence m after clamping its range: floor(T_m / C) >= 0.
+__host__ __device__ __forceinline__ unsigned long long full_chunks(const int32_t *cu, int m,
+                                                                   int64_t T, int C) {
+  int64_t b, e;
+  seq_range(cu, m, T, b, e);  // e >= b
+  return (unsigned long long)((e - b) / C);
+}
+
+// A sum of full_chunks terms as a chunk-state index in [0, total_chunks]. At most 2^31
+// sequences of fewer than 2^31 tokens each, so the 64-bit sum cannot wrap.
+__host__ __device__ __forceinline__ int64_t clamp_chunk_index(unsigned long long sum,
+                                                              int64_t total_chunks) {
+  return sum < (unsigned long long)total_chunks ? (int64_t)sum : total_chunks;
+}
+
+// Index of sequence n's first chunk-boundary state: sum over m < n of floor(T_m / C), in
+// 64 bits and clamped to total_chunks. The lengths come from device memory the host cannot
+// check; whatever they hold, the index is in [0, total_chunks].
+__device__ inline int64_t first_chunk_slot(const int32_t *cu, int n, int64_t T, int C,
+                                           int64_t total_chunks, unsigned long long *s_acc) {
   if (threadIdx.x == 0) *s_acc = 0;
   __syncthreads();
-  int local = 0;
-  for (int m = threadIdx.x; m < n; m += blockDim.x) {
-    int64_t b, e;
-    seq_range(cu, m, T, b, e);
-    local += (int)((e - b) / C);
-  }
+  unsigned long long local = 0;
+  for (int m = threadIdx.x; m < n; m += blockDim.x) local += full_chunks(cu, m, T, C);
   atomicAdd(s_acc, local);
   __syncthreads();
-  return *s_acc;
+  return clamp_chunk_index(*s_acc, total_chunks);
 }
 
 // Raw register copy of four input elements: bf16 stays packed until it is written to LDS.

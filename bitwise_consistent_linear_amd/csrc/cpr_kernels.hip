@@ -69,7 +69,8 @@ void cpr_scan_kernel(const ScanArgs p) {
     float sv[2][V_ITEMS];
     float so[2][V_ITEMS];
     int s_len[kMaxRankedSeqs];
-    int s_pick, s_acc;
+    int s_pick;
+    unsigned long long s_acc;
     alignas(16) float pool[2][POOL];
   };
   __shared__ Lds lds;
@@ -79,7 +80,8 @@ void cpr_scan_kernel(const ScanArgs p) {
   auto &so = lds.so;
   auto &pool = lds.pool;
   int *const s_len = lds.s_len;
-  int &s_pick = lds.s_pick, &s_acc = lds.s_acc;
+  int &s_pick = lds.s_pick;
+  unsigned long long &s_acc = lds.s_acc;
 
   const int tid = threadIdx.x, row = tid / L, lane = tid % L;
   auto SK = [&](int buf) { return &pool[buf][0]; };
@@ -87,7 +89,7 @@ void cpr_scan_kernel(const ScanArgs p) {
   const int Hv = p.num_v_heads, Hk = p.num_qk_heads, dv = p.d_v;
   const int rblocks = (dv + ROWS - 1) / ROWS;
   int pair, rblock;
-  block_work(blockIdx.x, p.num_seqs * Hv, rblocks, pair, rblock);
+  block_work(blockIdx.x, p.num_seqs * Hv, rblocks, Hv / Hk, pair, rblock);
   const int rank = pair / Hv;
   const int h = pair % Hv;
   const int r0 = rblock * ROWS;
@@ -98,7 +100,8 @@ void cpr_scan_kernel(const ScanArgs p) {
   seq_range(p.cu_seqlens, n, T, bos, eos);
   const int64_t Tn = eos - bos;
   int64_t cbase = 0;
-  if constexpr (MODE == kTrainer) cbase = first_chunk_slot(p.cu_seqlens, n, T, p.chunk, &s_acc);
+  if constexpr (MODE == kTrainer)
+    cbase = first_chunk_slot(p.cu_seqlens, n, T, p.chunk, p.total_chunks, &s_acc);
 
   const int hk = h / (Hv / Hk);
   const int i = r0 + row;
@@ -299,7 +302,7 @@ void cpr_scan_kernel(const ScanArgs p) {
     if constexpr (MODE == kTrainer) {
       if ((done & (p.chunk - 1)) == 0) {
         const int64_t c = cbase + (done >> chunk_shift) - 1;
-        if (valid && c < p.total_chunks)
+        if (valid && c >= 0 && c < p.total_chunks)
           store_row<M>(p.chunk_states + ((c * Hv + h) * dv + i) * D + lane * M, st);
       }
     }
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void cpr_decode_kernel(const DecodeArgs p
   const int Hv = p.num_v_heads, Hk = p.num_qk_heads, dv = p.d_v;
   const int rblocks = (dv + ROWS - 1) / ROWS;
   int pair, rblock;
-  block_work(blockIdx.x, p.num_seqs * Hv, rblocks, pair, rblock);
+  block_work(blockIdx.x, p.num_seqs * Hv, rblocks, Hv / Hk, pair, rblock);
   const int n = pair / Hv;
   const int h = pair % Hv;
   const int i = rblock * ROWS + row;

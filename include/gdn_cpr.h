@@ -97,13 +97,17 @@ typedef struct gdn_shape {
   int32_t qkv_dtype;
 } gdn_shape_t;
 
-/* ABI version of the loaded library (GDN_CPR_ABI_VERSION). Host only. */
+/* Library utility (it implements no passage of the pages): the ABI version of the loaded
+ * library, GDN_CPR_ABI_VERSION, so that a caller built against another header can refuse
+ * it. Host only; cannot fail. */
 int32_t gdn_abi_version(void);
 
 /* Canonical contract text for (chunk, d_k): ASCII lines "key=value\n" fixing the rule,
  * operation order, reduction tree, dtypes, rounding, head mapping, chunk boundaries and
  * resync rule. Writes at most buf_len bytes (NUL-terminated when it fits) and the full
- * length, without the NUL, to *out_len. buf may be NULL when buf_len is 0.
+ * length, without the NUL, to *out_len. buf may be NULL when buf_len is 0. The text is
+ * copied into caller memory rather than returned as a pointer into the library, so its
+ * lifetime is the caller's and the call stays thread-safe; ask with buf_len 0 for the size.
  * Host only. Errors: GDN_E_NULL (out_len NULL), GDN_E_UNSUPPORTED (chunk or d_k not
  * admitted), GDN_E_SHAPE (buffer too small; *out_len still set).
  * Identity by content digest follows IsoExec (aihirek.info, section on the contract and
@@ -116,9 +120,10 @@ gdn_status_t gdn_contract_string(int32_t chunk, int32_t d_k, char *buf, size_t b
  * when it differs. Host only. Errors: GDN_E_NULL, GDN_E_UNSUPPORTED. */
 gdn_status_t gdn_contract_identity(int32_t chunk, int32_t d_k, uint8_t digest[32]);
 
-/* SHA-256 (FIPS 180-4) of len bytes at msg (host memory) into digest[32] (host memory);
- * the routine behind gdn_contract_identity, for callers that derive identities of their
- * own texts. Host only. Errors: GDN_E_NULL (digest NULL, or msg NULL with len > 0). */
+/* Library utility: SHA-256 (FIPS 180-4) of len bytes at msg (host memory) into
+ * digest[32] (host memory); the routine behind gdn_contract_identity, exported so that a
+ * caller can hash a contract text it holds and compare identities itself. Host only.
+ * Errors: GDN_E_NULL (digest NULL, or msg NULL with len > 0). */
 gdn_status_t gdn_sha256(const void *msg, size_t len, uint8_t digest[32]);
 
 /* trainer_fwd: the recurrence over a packed batch, writing o for every token and the state
@@ -135,7 +140,11 @@ gdn_status_t gdn_sha256(const void *msg, size_t len, uint8_t digest[32]);
  *                              floor(T_n / C) states starting at sum_{m<n} floor(T_m / C).
  *                              May be NULL only when total_chunks == 0.
  *   total_chunks             : sum_n floor(T_n / C), 0 <= total_chunks < 2^31
- *   stream                   : hipStream_t or NULL. */
+ *   stream                   : hipStream_t or NULL.
+ * There is no chunk-offsets argument: each workgroup derives its sequence's first state
+ * index, sum_{m<n} floor(T_m / C), from cu_seqlens on the device (64-bit sums, clamped to
+ * total_chunks). A caller-supplied copy of those prefix sums could only disagree with
+ * cu_seqlens, and the host cannot read device memory to check it. */
 gdn_status_t gdn_cpr_trainer_fwd(const gdn_shape_t *shape, const uint8_t *expected_identity,
                                  const int32_t *cu_seqlens, int64_t total_tokens,
                                  const void *q, const void *k, const void *v, const float *a,
@@ -348,8 +357,9 @@ gdn_status_t gdn_cpr2_decode_step(const gdn_shape_t *shape, const uint8_t *expec
                                   float *resync_states, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
-/* Text describing the calling thread's last non-GDN_OK status ("" if none). The pointer
- * stays valid until the thread's next call into the library. Host only. */
+/* Library utility: text describing the calling thread's last non-GDN_OK status ("" if
+ * none). The pointer stays valid until the thread's next call into the library. Host only;
+ * cannot fail. */
 const char *gdn_last_error(void);
 
 #ifdef __cplusplus
