@@ -75,6 +75,10 @@ def lib():
         L.gdn_cpr_trainer_bwd.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_char_p, P, I64,
                                           P, P, P, P, P, P, P, I64, P, P,
                                           P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.gdn_cpr_trainer_bwd_noalloc.restype = I32
+        L.gdn_cpr_trainer_bwd_noalloc.argtypes = [ctypes.POINTER(GdnShape), ctypes.c_char_p, P,
+                                                  I64, P, P, P, P, P, P, P, I64, P, P,
+                                                  P, P, P, P, P, P, P]
         L.gdn_linear_fwd.restype = I32
         L.gdn_linear_fwd.argtypes = [ctypes.POINTER(GdnLinearShape), ctypes.c_char_p, P, P, P, P]
         L.gdn_cpr2_contract_string.restype = I32
@@ -337,15 +341,21 @@ def trainer_bwd_workspace_bytes(shape: GdnShape, total_tokens: int, total_chunks
     return n.value
 
 
+NOALLOC_MAX_BYTES = 128 << 20  # GDN_CPR_BWD_NOALLOC_MAX_BYTES
+
+
 def trainer_bwd(cu_seqlens, q, k, v, a, b, chunk_states, d_o, *, chunk, initial_state=None,
                 d_final_state=None, total_chunks=None, workspace=None, out=None,
-                identity=None, stream=None):
+                identity=None, stream=None, noalloc=False):
     """gdn_cpr_trainer_bwd: gradients through trainer_fwd, given d_o [T, Hv, dv] and
     optionally d_final_state [N, Hv, dv, dk].
 
     chunk_states is trainer_fwd's output for the same inputs. ``workspace`` is a uint8 GPU
     tensor of at least trainer_bwd_workspace_bytes() bytes (allocated here when omitted);
-    ``out`` may hold preallocated dq, dk, dv, da, db, dS0 tensors.
+    ``out`` may hold preallocated dq, dk, dv, da, db, dS0 tensors. noalloc=True calls
+    gdn_cpr_trainer_bwd_noalloc instead, whose workspace is the library's fixed array
+    (sizes up to NOALLOC_MAX_BYTES of workspace); pass every output in ``out`` to make the
+    whole call allocation-free.
     Returns a dict with dq, dk [T, Hk, dk]; dv [T, Hv, dv]; da, db [T, Hv];
     dS0 [N, Hv, dv, dk], all fp32.
     """
@@ -373,6 +383,21 @@ def trainer_bwd(cu_seqlens, q, k, v, a, b, chunk_states, d_o, *, chunk, initial_
         if tuple(out[name].shape) != shp:
             raise ValueError(f"{name} must be {list(shp)}, got {tuple(out[name].shape)}")
     shape = _shape(N, q, v, chunk, dt)
+    ident = identity if identity is not None else contract_identity(chunk, dk)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc=True takes no workspace")
+        _same_device(("q", q), ("k", k), ("v", v), ("a", a), ("b", b),
+                     ("cu_seqlens", cu_seqlens), ("initial_state", initial_state),
+                     ("chunk_states", chunk_states), ("d_o", d_o),
+                     ("d_final_state", d_final_state), *[(name, out[name]) for name in shapes])
+        _check(lib().gdn_cpr_trainer_bwd_noalloc(
+            ctypes.byref(shape), ident, _ptr(cu_seqlens), T, _ptr(q), _ptr(k), _ptr(v),
+            _ptr(a), _ptr(b), _ptr(initial_state), _ptr(chunk_states) if total_chunks else None,
+            total_chunks, _ptr(d_o), _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]),
+            _ptr(out["dv"]), _ptr(out["da"]), _ptr(out["db"]), _ptr(out["dS0"]),
+            _stream(stream)))
+        return out
     need = trainer_bwd_workspace_bytes(shape, T, total_chunks)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -381,7 +406,6 @@ def trainer_bwd(cu_seqlens, q, k, v, a, b, chunk_states, d_o, *, chunk, initial_
                  ("initial_state", initial_state), ("chunk_states", chunk_states),
                  ("d_o", d_o), ("d_final_state", d_final_state), ("workspace", workspace),
                  *[(name, out[name]) for name in shapes])
-    ident = identity if identity is not None else contract_identity(chunk, dk)
     _check(lib().gdn_cpr_trainer_bwd(
         ctypes.byref(shape), ident, _ptr(cu_seqlens), T, _ptr(q), _ptr(k), _ptr(v), _ptr(a),
         _ptr(b), _ptr(initial_state), _ptr(chunk_states) if total_chunks else None,

@@ -359,13 +359,17 @@ GDN_EXPORT gdn_status_t gdn_cpr_trainer_bwd_workspace(const gdn_shape_t *shape,
   return gdn::ok();
 }
 
-GDN_EXPORT gdn_status_t gdn_cpr_trainer_bwd(
-    const gdn_shape_t *shape, const uint8_t *expected_identity, const int32_t *cu_seqlens,
-    int64_t total_tokens, const void *q, const void *k, const void *v, const float *a,
-    const float *b, const float *initial_state, const float *chunk_states, int64_t total_chunks,
-    const float *d_o, const float *d_final_state, float *dq, float *dk, float *dv, float *da,
-    float *db, float *d_initial_state, void *workspace, size_t workspace_bytes, void *stream) {
-  const char *fn = "gdn_cpr_trainer_bwd";
+// The backward behind gdn_cpr_trainer_bwd and gdn_cpr_trainer_bwd_noalloc. workspace ==
+// nullptr (with workspace_bytes == 0) selects the library's fixed scratch array, after the
+// other claims and a size check.
+static gdn_status_t trainer_bwd_impl(
+    const char *fn, const gdn_shape_t *shape, const uint8_t *expected_identity,
+    const int32_t *cu_seqlens, int64_t total_tokens, const void *q, const void *k,
+    const void *v, const float *a, const float *b, const float *initial_state,
+    const float *chunk_states, int64_t total_chunks, const float *d_o,
+    const float *d_final_state, float *dq, float *dk, float *dv, float *da, float *db,
+    float *d_initial_state, void *workspace, size_t workspace_bytes, bool fixed_scratch,
+    void *stream) {
   gdn::ScanArgs fwd;  // the forward claims apply unchanged (o is dq here: any non-null f32)
   gdn_status_t st = gdn::scan_common(fn, shape, expected_identity, cu_seqlens, total_tokens, q,
                                      k, v, a, b, initial_state, dq, fwd);
@@ -386,6 +390,19 @@ GDN_EXPORT gdn_status_t gdn_cpr_trainer_bwd(
       return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": gradient buffers must be 4-byte aligned");
   const gdn::BwdWorkspace ws = gdn::backward_workspace(
       shape->num_seqs, shape->num_v_heads, shape->d_k, shape->d_v, total_tokens, total_chunks);
+  if (fixed_scratch) {
+    if (ws.total > (int64_t)gdn::kNoAllocScratchBytes)
+      return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": these sizes need " +
+                                        std::to_string(ws.total) + " bytes of scratch; the "
+                                        "fixed array holds " +
+                                        std::to_string(gdn::kNoAllocScratchBytes) +
+                                        " (use gdn_cpr_trainer_bwd with a workspace)");
+    const hipError_t e = gdn::noalloc_scratch(&workspace);
+    if (e != hipSuccess)
+      return gdn::fail(GDN_E_DEVICE, std::string(fn) + ": no scratch array on this device: " +
+                                         hipGetErrorString(e));
+    workspace_bytes = gdn::kNoAllocScratchBytes;
+  }
   if (!workspace) return gdn::fail(GDN_E_NULL, std::string(fn) + ": workspace is NULL");
   if (!gdn::aligned(workspace, 256))
     return gdn::fail(GDN_E_SHAPE, std::string(fn) + ": workspace must be 256-byte aligned");
@@ -437,6 +454,30 @@ GDN_EXPORT gdn_status_t gdn_cpr_trainer_bwd(
   if (e != hipSuccess)
     return gdn::fail(GDN_E_DEVICE, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
   return gdn::ok();
+}
+
+GDN_EXPORT gdn_status_t gdn_cpr_trainer_bwd(
+    const gdn_shape_t *shape, const uint8_t *expected_identity, const int32_t *cu_seqlens,
+    int64_t total_tokens, const void *q, const void *k, const void *v, const float *a,
+    const float *b, const float *initial_state, const float *chunk_states, int64_t total_chunks,
+    const float *d_o, const float *d_final_state, float *dq, float *dk, float *dv, float *da,
+    float *db, float *d_initial_state, void *workspace, size_t workspace_bytes, void *stream) {
+  return trainer_bwd_impl("gdn_cpr_trainer_bwd", shape, expected_identity, cu_seqlens,
+                          total_tokens, q, k, v, a, b, initial_state, chunk_states, total_chunks,
+                          d_o, d_final_state, dq, dk, dv, da, db, d_initial_state, workspace,
+                          workspace_bytes, false, stream);
+}
+
+GDN_EXPORT gdn_status_t gdn_cpr_trainer_bwd_noalloc(
+    const gdn_shape_t *shape, const uint8_t *expected_identity, const int32_t *cu_seqlens,
+    int64_t total_tokens, const void *q, const void *k, const void *v, const float *a,
+    const float *b, const float *initial_state, const float *chunk_states, int64_t total_chunks,
+    const float *d_o, const float *d_final_state, float *dq, float *dk, float *dv, float *da,
+    float *db, float *d_initial_state, void *stream) {
+  return trainer_bwd_impl("gdn_cpr_trainer_bwd_noalloc", shape, expected_identity, cu_seqlens,
+                          total_tokens, q, k, v, a, b, initial_state, chunk_states, total_chunks,
+                          d_o, d_final_state, dq, dk, dv, da, db, d_initial_state, nullptr, 0,
+                          true, stream);
 }
 
 // ------------------------------------------------------------------- two-level reading

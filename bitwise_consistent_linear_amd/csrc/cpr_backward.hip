@@ -21,6 +21,7 @@
 // equal the contract's single tree over the d_v rows.
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -658,6 +659,33 @@ const void *chunk_fn(bool bf16, bool seq, int chunk) {
 }
 
 }  // namespace
+
+// ------------------------------------------------------- fixed scratch for the no-alloc call
+
+// The workspace of gdn_cpr_trainer_bwd_noalloc: one array per GPU the library runs on, held
+// until the process ends. On the host, `scratch` names a stand-in, not device memory: every
+// host use goes through the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {  // once per device, with that device current
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 int backward_row_blocks(int d_v) { return (d_v + kChunkRows - 1) / kChunkRows; }
 

@@ -72,6 +72,11 @@ struct BwdWorkspace {
   int64_t partials_off, partials_bytes, total, slots_max;
 };
 
+// Bytes of the fixed device array behind gdn_cpr_trainer_bwd_noalloc, and its address on
+// the current device (looked up once per device with hipGetSymbolAddress).
+constexpr size_t kNoAllocScratchBytes = GDN_CPR_BWD_NOALLOC_MAX_BYTES;
+hipError_t noalloc_scratch(void **ptr);
+
 int backward_row_blocks(int d_v);
 BwdWorkspace backward_workspace(int64_t num_seqs, int64_t num_v_heads, int64_t d_k,
                                 int64_t d_v, int64_t total_tokens, int64_t total_chunks);

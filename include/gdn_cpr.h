@@ -239,6 +239,30 @@ gdn_status_t gdn_cpr_trainer_bwd(const gdn_shape_t *shape, const uint8_t *expect
                                  float *d_initial_state, void *workspace,
                                  size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory - code under HIP graph capture, tight
+ * serving or training loops, harnesses that forbid allocation: gdn_cpr_trainer_bwd with the
+ * workspace taken from a fixed device array inside the library instead of the caller.
+ * Arguments, outputs, bits and errors as for gdn_cpr_trainer_bwd (which it shares every
+ * kernel with), without workspace and workspace_bytes. The call allocates nothing: the
+ * array, GDN_CPR_BWD_NOALLOC_MAX_BYTES bytes, is part of the library's device code, one per
+ * GPU the library runs on, held until the process ends; its address on a device is looked
+ * up on the first call there. Sizes whose workspace (gdn_cpr_trainer_bwd_workspace) exceeds
+ * GDN_CPR_BWD_NOALLOC_MAX_BYTES are refused with GDN_E_SHAPE before anything is launched.
+ * All calls on one GPU share that GPU's array: calls that overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller. The array's contents
+ * between calls do not matter; every call writes what it reads. Host only. */
+#define GDN_CPR_BWD_NOALLOC_MAX_BYTES ((size_t)128 << 20)
+gdn_status_t gdn_cpr_trainer_bwd_noalloc(const gdn_shape_t *shape,
+                                         const uint8_t *expected_identity,
+                                         const int32_t *cu_seqlens, int64_t total_tokens,
+                                         const void *q, const void *k, const void *v,
+                                         const float *a, const float *b,
+                                         const float *initial_state, const float *chunk_states,
+                                         int64_t total_chunks, const float *d_o,
+                                         const float *d_final_state, float *dq, float *dk,
+                                         float *dv, float *da, float *db,
+                                         float *d_initial_state, void *stream);
+
 /* Host struct of the linear region: Y [m, n] = X [m, k] W [k, n], all row-major.
  * Admitted: 0 <= m, n < 2^31; k a positive multiple of 512 up to 2^24; x_dtype and w_dtype
  * GDN_DTYPE_F32 or GDN_DTYPE_BF16. */

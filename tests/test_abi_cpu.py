@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\s[TW]\s+(gdn_\w+)$", out, flags=re.M))
@@ -140,6 +140,17 @@ def bwd(L, sh, identity=None, T=128, total_chunks=2, ws_bytes=1 << 30, **ptrs):
                                  p["ds0"], p["ws"], ws_bytes, None)
 
 
+def bwd_noalloc(L, sh, identity=None, T=128, total_chunks=2, **ptrs):
+    p = dict(cu=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, b=FAKE, s0=None, cs=FAKE, do=FAKE,
+             dsf=None, dq=FAKE, dk=FAKE, dv=FAKE, da=FAKE, db=FAKE, ds0=FAKE)
+    p.update(ptrs)
+    idb = ident(sh) if identity is None else identity
+    return L.gdn_cpr_trainer_bwd_noalloc(ctypes.byref(sh), idb, p["cu"], T, p["q"], p["k"],
+                                         p["v"], p["a"], p["b"], p["s0"], p["cs"], total_chunks,
+                                         p["do"], p["dsf"], p["dq"], p["dk"], p["dv"], p["da"],
+                                         p["db"], p["ds0"], None)
+
+
 def linear(L, m=64, n=64, k=512, xdt=api.GDN_DTYPE_BF16, wdt=api.GDN_DTYPE_BF16, identity=None,
            x=FAKE, w=FAKE, y=FAKE, shape_ok=True):
     sh = api.GdnLinearShape(m, n, k, xdt, wdt)
@@ -234,6 +245,10 @@ REFUSALS = [
     ("bwd misaligned dq", lambda L: bwd(L, shape(), dq=FAKE + 2), api.GDN_E_SHAPE),
     ("bwd null q", lambda L: bwd(L, shape(), q=None), api.GDN_E_NULL),
     ("bwd heads not a multiple", lambda L: bwd(L, shape(num_qk_heads=3)), api.GDN_E_SHAPE),
+    ("bwd noalloc wrong identity", lambda L: bwd_noalloc(L, shape(), identity=bytes(32)), api.GDN_E_IDENTITY),
+    ("bwd noalloc null d_o", lambda L: bwd_noalloc(L, shape(), do=None), api.GDN_E_NULL),
+    # 2^20 tokens of 16 heads at d = 128 need gigabytes of workspace: more than the fixed array
+    ("bwd noalloc beyond the fixed array", lambda L: bwd_noalloc(L, shape(num_seqs=1, num_qk_heads=16, num_v_heads=16, d_k=128, d_v=128), T=1 << 20, total_chunks=(1 << 20) // 64), api.GDN_E_SHAPE),
     ("cpr2 one-level identity", lambda L: cpr2_batch(L, shape(), identity=api.contract_identity(64, 64)), api.GDN_E_IDENTITY),
     ("one-level call, two-level identity", lambda L: trainer(L, shape(), identity=api.cpr2_contract_identity(64, 64)), api.GDN_E_IDENTITY),
     ("cpr2 d_k 16", lambda L: cpr2_batch(L, shape(d_k=16)), api.GDN_E_UNSUPPORTED),
