@@ -894,6 +894,62 @@ def cpu_baseline(w, gpu_outputs):
             "bitwise_equal_to_gpu_trainer_fwd": bool(same)}
 
 
+TRACE_TITLES = {
+    "main": ("cpr_scan_trainer_fwd", "trainer_fwd: 4 x 4096 tokens, 16 heads, d_k = d_v = 128, "
+             "C = 64, bf16 q/k/v"),
+    "prefill": ("cpr_scan_engine_prefill", "engine_prefill: 64 varlen sequences, 262144 tokens, "
+                "16 q/k / 32 v heads, d = 128, bf16 q/k/v"),
+    "decode": ("cpr_decode_engine_decode", "engine_decode: 256 sequences, 16 q/k / 32 v heads, "
+               "d = 128, C = 64, 1000-token prefill then 512 steps"),
+    "long": ("cpr_scan_long_context", "long_context: 1 x 131072 tokens, 16 q/k / 32 v heads, "
+             "d = 128, C = 64: trainer_fwd, prefill, prefill of 65536 then 256 decode steps"),
+    "bwd": ("cpr_bwd_trainer", "trainer_bwd on the trainer_fwd workload"),
+    "cpr2": ("cpr2_two_level", "two-level CPR: trainer, prefill and decode"),
+    "linear": ("linear_leaf_16384x4096x4096", "linear region: 16384 x 4096 x 4096, bf16 in, "
+               "binary32 out"),
+}
+TRACE_COMMAND = ("export TMPDIR=/tmp; cd /tmp && rocprofv3 --kernel-trace --stats --output-format "
+                 "csv -d $R/gpurun_out/trace_{case} -o {case} -- python3 $R/bench.py --cases "
+                 "{case} --no-cpu-baseline --steps 20")
+
+
+def write_trace_summary(stats_csv, case, bench_json=None):
+    """profiles/<name>_kernel_trace.md from a rocprofv3 --kernel-trace --stats run of
+    `bench.py --cases <case>`: the command, each kernel's calls and average duration, and,
+    when the JSON line of a bench run in the same lease is given, the bench's own event
+    timings beside them."""
+    import csv
+    name, title = TRACE_TITLES[case]
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# {title} (rocprofv3 kernel-trace stats)", "",
+             "Command (one MI355X, repository root as R):", "", "```",
+             TRACE_COMMAND.format(case=case), "```", "",
+             "| kernel | calls | average ns | min ns | max ns | % |", "|---|---|---|---|---|---|"]
+    for r in rows[:12]:
+        kname = r["Name"] if len(r["Name"]) <= 110 else r["Name"][:100] + " ..."
+        lines.append(f"| `{kname}` | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{float(r['MinNs']):.0f} | {float(r['MaxNs']):.0f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    if bench_json:
+        with open(bench_json) as f:
+            line = [ln for ln in f.read().splitlines() if ln.startswith("{")][-1]
+        b = json.loads(line)
+        lines += ["", "The bench run in the same lease (HIP events on the launching stream):", ""]
+        lines.append(f"- trainer_fwd: {b['kernel_ms']} ms per call, roofline "
+                     f"{json.dumps(b['roofline'])}, parity {b['parity']['bitwise_exact']}")
+        if b.get("valu_probe"):
+            lines.append(f"- shader clock (probe): {b['valu_probe']['shader_clock_GHz']} GHz")
+        for cname, c in (b.get("cases") or {}).items():
+            keep = {k: v for k, v in c.items()
+                    if k.endswith("_ms") or k.startswith("us_") or k.endswith("roofline")}
+            lines.append(f"- {cname}: {json.dumps(keep)}; parity "
+                         f"{c.get('parity', {}).get('bitwise_exact')}")
+    path = os.path.join(ROOT, "profiles", f"{name}_kernel_trace.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -916,9 +972,17 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/*_traffic.json from two rocprofv3 counter CSVs and "
                          "exit (no GPU needed)")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "CASE"),
+                    help="write profiles/<kernel>_kernel_trace.md from the kernel_stats.csv of "
+                         "a traced `bench.py --cases CASE` run and exit (no GPU needed)")
+    ap.add_argument("--bench-json", help="with --trace-summary: the JSON line of a bench run "
+                                         "in the same lease, quoted beside the trace")
     args = ap.parse_args()
     if args.traffic_from:
         write_traffic(*args.traffic_from)
+        return
+    if args.trace_summary:
+        write_trace_summary(*args.trace_summary, bench_json=args.bench_json)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path. Every state row "
