@@ -1,4 +1,7 @@
-// Measurement probes for gfx950, built into libgdn_probe.so (not part of libgdn_cpr.so).
+// Measurement probes for gfx950, built into libgdn_probe.so (not part of libgdn_cpr.so):
+// the vector-issue ceiling and shader clock (gdn_probe_valu, below), and one wave of the
+// binary32 matrix instructions on given operands (gdn_probe_mfma), from which the tests
+// establish the order in which those instructions accumulate.
 //
 // The scan kernels are bound by the issue of binary32 vector instructions. Their roofline
 // takes the published 157.3 TFLOP/s fp32 vector peak of MI355X (256 CUs x 4 SIMDs x 2.4 GHz
@@ -74,7 +77,60 @@ __global__ __launch_bounds__(kThreads) void valu_probe_kernel(float *out, long l
   }
 }
 
+// One wave: D = C + A B on the binary32 matrix instructions, k ascending, K / 4 steps of
+// v_mfma_f32_16x16x4_f32 (FORM 0, 16 x 16 outputs) or K / 2 steps of
+// v_mfma_f32_32x32x2_f32 (FORM 1, 32 x 32). A [n x K] and B [K x n] row-major, C and D
+// [n x n] row-major, all binary32 in device memory. Operand layouts (lane l):
+//   16x16x4: A[l % 16][4 s + l / 16], B[4 s + l / 16][l % 16], register r of C/D holds
+//            row 4 (l / 16) + r, column l % 16;
+//   32x32x2: A[l % 32][2 s + l / 32], B[2 s + l / 32][l % 32], register r holds row
+//            8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+using f32x4 = float __attribute__((ext_vector_type(4)));
+using f32x16 = float __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(64) void mfma16_probe_kernel(const float *A, const float *B,
+                                                          const float *C, float *D, int K) {
+  const int l = threadIdx.x, i = l % 16, q = l / 16;
+  f32x4 acc;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = C[(4 * q + r) * 16 + i];
+  for (int st = 0; st < K / 4; ++st)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[i * K + 4 * st + q], B[(4 * st + q) * 16 + i],
+                                               acc, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) D[(4 * q + r) * 16 + i] = acc[r];
+}
+
+__global__ __launch_bounds__(64) void mfma32_probe_kernel(const float *A, const float *B,
+                                                          const float *C, float *D, int K) {
+  const int l = threadIdx.x, i = l % 32, q = l / 32;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = C[(8 * (r / 4) + 4 * q + r % 4) * 32 + i];
+  for (int st = 0; st < K / 2; ++st)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(A[i * K + 2 * st + q], B[(2 * st + q) * 32 + i],
+                                               acc, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) D[(8 * (r / 4) + 4 * q + r % 4) * 32 + i] = acc[r];
+}
+
 }  // namespace
+
+// Runs one wave of the matrix-instruction probe on `stream`: form 0 = 16x16x4 (n = 16, K a
+// multiple of 4), form 1 = 32x32x2 (n = 32, K a multiple of 2), 1 <= K <= 256; a holds
+// n * K floats, b K * n, c and d n * n (device memory). Returns 0, or -1 for other
+// arguments or a launch error.
+GDN_PROBE_EXPORT int gdn_probe_mfma(int form, const float *a, const float *b, const float *c,
+                                    float *d, int k, void *stream) {
+  if ((form != 0 && form != 1) || k < 1 || k > 256 || k % (form == 0 ? 4 : 2) != 0 || !a ||
+      !b || !c || !d)
+    return -1;
+  const void *fn = form == 0 ? (const void *)mfma16_probe_kernel : (const void *)mfma32_probe_kernel;
+  void *args[] = {&a, &b, &c, &d, &k};
+  const hipError_t e =
+      hipLaunchKernel(fn, dim3(1), dim3(64), args, 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? 0 : -1;
+}
 
 // Launches the probe on `stream` (hipStream_t or NULL). grid = 256 * waves_per_simd
 // workgroups; out must hold grid * 256 floats and clk grid * 2 int64, both device memory.
