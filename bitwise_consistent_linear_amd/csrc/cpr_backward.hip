@@ -278,8 +278,8 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
   constexpr int kThreads = kChunkThreads;
   constexpr int L = kChunkLanes, ROWS = kChunkRows, M = D / L, SB = kSub;
   constexpr int WAVES = kChunkWaves, RPW = 64 / L;  // rows per wave
-  constexpr int PW = 2 * D + 2;                       // shares of a token: dq, dk, da, db
-  constexpr int PWP = 2 * D + 4;                      // their LDS row, 16-byte aligned
+  constexpr int PWP = 2 * D + 4;  // shares of a token (dq, dk, da, db) padded to whole float4:
+                                  // their LDS row and their row in the partial sums
   constexpr int H = M >= 2 ? M / 2 : 1;               // elements each lane holds after rows4_sum
   constexpr int GROUPS = D / 4;
   constexpr int KQ_ITEMS = SB * GROUPS, V_ITEMS = SB * ROWS;
@@ -537,19 +537,28 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
           }
         }
         __syncthreads();
-        // across the waves (wave w holds rows r0 + 4w .. r0 + 4w + 3), pairwise, pass-through
-        for (int e = tid; e < nt * PW; e += kThreads) {
-          const int j = e / PW, f = e % PW;
-          float w[WAVES];
+        // across the waves (wave w holds rows r0 + 4w .. r0 + 4w + 3), pairwise, pass-through;
+        // four consecutive shares per thread (one 16-byte read per wave, one 16-byte store).
+        // The last group of a token holds da, db and two padding slots, whose sums nothing
+        // reads.
+        constexpr int G4 = PWP / 4;
+        for (int e = tid; e < nt * G4; e += kThreads) {
+          const int j = e / G4, f = 4 * (e % G4);
+          float4 w[WAVES];
 #pragma unroll
-          for (int x = 0; x < WAVES; ++x) w[x] = swave[j][x][f];
+          for (int x = 0; x < WAVES; ++x) w[x] = *reinterpret_cast<const float4 *>(&swave[j][x][f]);
 #pragma unroll
           for (int st = 1; st < WAVES; st *= 2)
 #pragma unroll
             for (int x = 0; x + st < WAVES; x += 2 * st)
-              if (r0 + (x + st) * RPW < dv) w[x] = w[x] + w[x + st];
+              if (r0 + (x + st) * RPW < dv) {
+                w[x].x = w[x].x + w[x + st].x;
+                w[x].y = w[x].y + w[x + st].y;
+                w[x].z = w[x].z + w[x + st].z;
+                w[x].w = w[x].w + w[x + st].w;
+              }
           const int64_t t = bos + c0 + sbi * SB + j;
-          p.partials[((t * Hv + h) * RB + rblock) * PW + f] = w[0];
+          *reinterpret_cast<float4 *>(&p.partials[((t * Hv + h) * RB + rblock) * PWP + f]) = w[0];
         }
         if constexpr (SEQ) {
           for (int e = tid; e < nt * ROWS; e += kThreads) {
@@ -592,7 +601,7 @@ __device__ __forceinline__ float rb_tree(const float *base, int64_t stride, int 
 
 template <int RBMAX>
 __global__ __launch_bounds__(kThreads) void cpr_bwd_combine_kernel(const BwdArgs p) {
-  const int D = p.d_k, PW = 2 * D + 2, RB = p.row_blocks;
+  const int D = p.d_k, PW = 2 * D + 4, RB = p.row_blocks;  // partial rows padded to float4
   const int Hv = p.num_v_heads, Hk = p.num_qk_heads, G = Hv / Hk;
   const int64_t T = p.total_tokens;
   const int64_t nqk = T * Hk * D, nab = T * Hv;
@@ -702,7 +711,7 @@ BwdWorkspace backward_workspace(int64_t num_seqs, int64_t num_v_heads, int64_t d
   w.dsh_bytes = up256(total_chunks * num_v_heads * d_v * d_k * 4);
   w.partials_off = w.dsh_off + w.dsh_bytes;
   w.partials_bytes =
-      up256(total_tokens * num_v_heads * backward_row_blocks((int)d_v) * (2 * d_k + 2) * 4);
+      up256(total_tokens * num_v_heads * backward_row_blocks((int)d_v) * (2 * d_k + 4) * 4);
   w.total = w.partials_off + w.partials_bytes;
   w.slots_max = slots;
   return w;

@@ -63,7 +63,8 @@ struct BwdArgs {
   int32_t *plan;        // [0]: slots used; then (sequence, chunk) pairs
   int32_t *plan_cbase;  // [N]: index of each sequence's first chunk state
   float *dsh_bnd;       // [total_chunks, Hv, d_v, d_k]: dL/ds at chunk ends
-  float *partials;      // [T, Hv, row_blocks, 2 d_k + 2]: row-block sums of the shares
+  float *partials;      // [T, Hv, row_blocks, 2 d_k + 4]: row-block sums of the shares
+                        // (dq, dk, da, db, two padding slots: rows of whole float4)
 };
 
 // Byte offsets of the backward workspace's parts (each 256-byte aligned).
