@@ -150,33 +150,55 @@ void cpr_scan_kernel(const ScanArgs p) {
     ra = p.a[(bos + t) * Hv + h];
     rb = p.b[(bos + t) * Hv + h];
   };
-  // Byte offsets of this thread's staged loads and o stores inside one full stage, fixed for
-  // the whole scan. A full stage adds them to scalar stage bases, so its global accesses
-  // need no per-stage 64-bit address arithmetic. The host admits Hv * max(d_k, d_v) <= 2^20,
-  // so every offset inside a stage of at most 64 tokens fits in 32 bits. Used where stages
-  // are pipelined (L >= 8); at 4 lanes per row the registers go to a third wave instead.
+  // Byte offsets of this thread's staged loads and o stores inside one full stage. A full
+  // stage adds them to scalar stage bases, so its global accesses need no per-stage 64-bit
+  // address arithmetic. The host admits Hv * max(d_k, d_v) <= 2^20, so every offset inside a
+  // stage of at most 64 tokens fits in 32 bits. Where stages are pipelined (L >= 8) they are
+  // computed once and held for the whole scan (FIXED); at 4 lanes per row the registers go
+  // to a third wave instead, and each full stage recomputes them in 32-bit arithmetic.
   constexpr bool FIXED = L >= 8;
   constexpr uint32_t EL = BF16 ? 2 : 4;
   const uint32_t kq_tok = (uint32_t)Hk * D;  // q/k elements per token
+  // (t is the thread index; !FIXED passes an opaque copy so that the offsets are
+  // recomputed where used instead of being hoisted into registers held across the scan)
+  auto kq_offset = [&](int t, int j) -> uint32_t {
+    const uint32_t g = (uint32_t)(t + j * kThreads) % KQ_ITEMS;
+    return ((g / GROUPS) * kq_tok + (uint32_t)hk * D + 4 * (g % GROUPS)) * EL;
+  };
+  auto v_offset = [&](int t, int j) -> uint32_t {
+    const uint32_t e = (uint32_t)(t + j * kThreads) % V_ITEMS;
+    const int r = r0 + (int)(e % ROWS) < dv ? r0 + (int)(e % ROWS) : dv - 1;
+    return ((e / ROWS) * (uint32_t)vstride + (uint32_t)(h * dv + r)) * EL;
+  };
+  auto o_offset = [&](int t, int j) -> uint32_t {
+    const int eo = t + j * kThreads;
+    return ((uint32_t)(eo / ROWS) * (uint32_t)vstride + (uint32_t)(h * dv + r0 + eo % ROWS)) * 4;
+  };
+  auto o_store_ok = [&](int t, int j) -> bool {
+    const int eo = t + j * kThreads;
+    return (V_ITEMS % kThreads == 0 || eo < V_ITEMS) && r0 + eo % ROWS < dv;
+  };
   uint32_t kq_off[KQ_PER], v_off[V_PER], o_off[V_PER];
   bool o_ok[V_PER];
+  if constexpr (FIXED) {
 #pragma unroll
-  for (int j = 0; j < KQ_PER; ++j) {
-    const uint32_t g = (uint32_t)(tid + j * kThreads) % KQ_ITEMS;
-    kq_off[j] = ((g / GROUPS) * kq_tok + (uint32_t)hk * D + 4 * (g % GROUPS)) * EL;
-  }
+    for (int j = 0; j < KQ_PER; ++j) kq_off[j] = kq_offset(tid, j);
 #pragma unroll
-  for (int j = 0; j < V_PER; ++j) {
-    const uint32_t e = (uint32_t)(tid + j * kThreads) % V_ITEMS;
-    const int r = r0 + (int)(e % ROWS) < dv ? r0 + (int)(e % ROWS) : dv - 1;
-    v_off[j] = ((e / ROWS) * (uint32_t)vstride + (uint32_t)(h * dv + r)) * EL;
-    const int eo = tid + j * kThreads;
-    o_off[j] = ((uint32_t)(eo / ROWS) * (uint32_t)vstride + (uint32_t)(h * dv + r0 + eo % ROWS)) * 4;
-    o_ok[j] = (V_ITEMS % kThreads == 0 || eo < V_ITEMS) && r0 + eo % ROWS < dv;
+    for (int j = 0; j < V_PER; ++j) {
+      v_off[j] = v_offset(tid, j);
+      o_off[j] = o_offset(tid, j);
+      o_ok[j] = o_store_ok(tid, j);
+    }
   }
   const uint32_t ab_off = (uint32_t)((tid % TS) * Hv + h) * 4;
-  // Fetch of a full stage (t0 + TS <= Tn): scalar bases plus the fixed offsets.
+  // Fetch of a full stage (t0 + TS <= Tn): scalar bases plus the 32-bit offsets.
+  auto opaque_tid = [&]() {
+    int t = tid;
+    if constexpr (!FIXED) asm volatile("" : "+v"(t));
+    return t;
+  };
   auto fetch_full = [&](int64_t t0) {
+    const int t = opaque_tid();
     const int64_t tok = bos + t0;
     const char *kb = static_cast<const char *>(p.k) + tok * kq_tok * EL;
     const char *qb = static_cast<const char *>(p.q) + tok * kq_tok * EL;
@@ -185,15 +207,17 @@ void cpr_scan_kernel(const ScanArgs p) {
     const char *bb = reinterpret_cast<const char *>(p.b + tok * Hv);
 #pragma unroll
     for (int j = 0; j < KQ_PER; ++j) {
-      rk[j] = *reinterpret_cast<const raw_t *>(kb + kq_off[j]);
-      rq[j] = *reinterpret_cast<const raw_t *>(qb + kq_off[j]);
+      const uint32_t off = FIXED ? kq_off[j] : kq_offset(t, j);
+      rk[j] = *reinterpret_cast<const raw_t *>(kb + off);
+      rq[j] = *reinterpret_cast<const raw_t *>(qb + off);
     }
 #pragma unroll
     for (int j = 0; j < V_PER; ++j) {
+      const uint32_t off = FIXED ? v_off[j] : v_offset(t, j);
       if constexpr (BF16)
-        rv[j] = *reinterpret_cast<const uint16_t *>(vb + v_off[j]);
+        rv[j] = *reinterpret_cast<const uint16_t *>(vb + off);
       else
-        rv[j] = *reinterpret_cast<const uint32_t *>(vb + v_off[j]);
+        rv[j] = *reinterpret_cast<const uint32_t *>(vb + off);
     }
     ra = *reinterpret_cast<const float *>(ab + ab_off);
     rb = *reinterpret_cast<const float *>(bb + ab_off);
@@ -219,11 +243,14 @@ void cpr_scan_kernel(const ScanArgs p) {
     }
   };
   auto write_o = [&](int64_t t0, int nt, int buf) {
-    if (FIXED && nt == TS) {  // full stage: scalar base plus the fixed offsets
+    if (nt == TS) {  // full stage: scalar base plus the 32-bit offsets
       char *ob = reinterpret_cast<char *>(p.o + (bos + t0) * vstride);
+      const int t = opaque_tid();
 #pragma unroll
       for (int j = 0; j < V_PER; ++j)
-        if (o_ok[j]) *reinterpret_cast<float *>(ob + o_off[j]) = so[buf][tid + j * kThreads];
+        if (FIXED ? o_ok[j] : o_store_ok(t, j))
+          *reinterpret_cast<float *>(ob + (FIXED ? o_off[j] : o_offset(t, j))) =
+              so[buf][tid + j * kThreads];
       return;
     }
 #pragma unroll
@@ -310,7 +337,7 @@ void cpr_scan_kernel(const ScanArgs p) {
   const int64_t nstages = (Tn + TS - 1) / TS;
 
   if (Tn > 0) {
-    if (FIXED && Tn >= TS)
+    if (Tn >= TS)
       fetch_full(0);
     else
       fetch(0);
@@ -323,7 +350,7 @@ void cpr_scan_kernel(const ScanArgs p) {
     const int nt = (int)(Tn - t0 < TS ? Tn - t0 : TS);
     const bool more = st + 1 < nstages;
     if (more) {  // global loads in flight while this stage computes
-      if (FIXED && t0 + 2 * TS <= Tn)
+      if (t0 + 2 * TS <= Tn)
         fetch_full(t0 + TS);
       else
         fetch(t0 + TS);
