@@ -446,131 +446,149 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
     const int len = clen - seg * kSeg < kSeg ? clen - seg * kSeg : kSeg;
     const int nsb = (len + SB - 1) / SB;
     auto sub_len = [&](int sbi) { return len - sbi * SB < SB ? len - sbi * SB : SB; };
-    fetch(c0, 0, sub_len(0));
-    deposit(0);  // buffer 0's last reader (the previous chunk) finished before its barrier
-    __syncthreads();
+    // The segment's sub-blocks. FAST: every sub-block whole (len a multiple of SB) and all
+    // four rows of this wave below d_v, so no token is skipped and no row passes through;
+    // the token loops then carry no per-token branch, and the scheduler can overlap one
+    // token's reduction trees with its neighbours' arithmetic. The same operations either
+    // way. Both copies hold the same barriers in the same order, so waves of one workgroup
+    // may take different copies.
+    auto segment = [&](auto fast_c) {
+      constexpr bool FAST = decltype(fast_c)::value;
+      fetch(c0, 0, sub_len(0));
+      deposit(0);  // buffer 0's last reader (the previous chunk) finished before its barrier
+      __syncthreads();
 
-    // forward over the chunk, keeping the state at the start of every sub-block
-    float ck[kMaxSub][M];
-    static_for<kMaxSub>([&](auto sbi_c) {
-      constexpr int sbi = decltype(sbi_c)::value, buf = sbi & 1;
-      if (sbi < nsb) {
-        const bool next = sbi + 1 < nsb;
-        if (next) fetch(c0, (sbi + 1) * SB, sub_len(sbi + 1));
+      // forward over the chunk, keeping the state at the start of every sub-block
+      float ck[kMaxSub][M];
+      static_for<kMaxSub>([&](auto sbi_c) {
+        constexpr int sbi = decltype(sbi_c)::value, buf = sbi & 1;
+        if (sbi < nsb) {
+          const bool next = sbi + 1 < nsb;
+          if (next) fetch(c0, (sbi + 1) * SB, sub_len(sbi + 1));
 #pragma unroll
-        for (int e = 0; e < M; ++e) ck[sbi][e] = s[e];
-        const int nt = sub_len(sbi);
-        for (int j = 0; j < nt; ++j) {
-          float kr[M], x[M];
-          lds_slice<D, L>(&sk[buf][j * D], lane, kr);
-          row_decay<D, L>(s, sa[buf][j], x);
-          const float u = contract_dot<D, L>(x, kr);
-          const float dif = sv[buf][j * ROWS + row] - u;  // d = b (v_i - u), as row_delta
-          if (lane == 0) sdif[sbi * SB + j][row] = dif;
-          row_update<D, L>(s, sb[buf][j] * dif, kr, x);
-        }
-        if (next) deposit(buf ^ 1);  // its last reader finished before the previous barrier
-        __syncthreads();
-      }
-    });
-
-    // sub-blocks in reverse: recompute the states, run sh back, sum the shares over rows
-    static_for<kMaxSub, true>([&](auto sbi_c) {
-      constexpr int sbi = decltype(sbi_c)::value, buf = sbi & 1;
-      if (sbi < nsb) {
-        const int nt = sub_len(sbi);
-        if (sbi > 0) fetch(c0, (sbi - 1) * SB, SB);
-        float st[SB + 1][M], dif[SB], del[SB];
-#pragma unroll
-        for (int e = 0; e < M; ++e) st[0][e] = ck[sbi][e];
-#pragma unroll
-        for (int j = 0; j < SB; ++j) {
-          if (j < nt) {  // the forward sweep left v_i - u of each token: no dot product here
+          for (int e = 0; e < M; ++e) ck[sbi][e] = s[e];
+          const int nt = sub_len(sbi);
+          for (int j = 0; j < nt; ++j) {
             float kr[M], x[M];
             lds_slice<D, L>(&sk[buf][j * D], lane, kr);
-            row_decay<D, L>(st[j], sa[buf][j], x);
-            dif[j] = sdif[sbi * SB + j][row];
-            del[j] = sb[buf][j] * dif[j];
-#pragma unroll
-            for (int e = 0; e < M; ++e) st[j + 1][e] = st[j][e];
-            row_update<D, L>(st[j + 1], del[j], kr, x);
+            row_decay<D, L>(s, sa[buf][j], x);
+            const float u = contract_dot<D, L>(x, kr);
+            const float dif = sv[buf][j * ROWS + row] - u;  // d = b (v_i - u), as row_delta
+            if (lane == 0) sdif[sbi * SB + j][row] = dif;
+            row_update<D, L>(s, sb[buf][j] * dif, kr, x);
           }
+          if (next) deposit(buf ^ 1);  // its last reader finished before the previous barrier
+          __syncthreads();
         }
+      });
+
+      // sub-blocks in reverse: recompute the states, run sh back, sum the shares over rows
+      static_for<kMaxSub, true>([&](auto sbi_c) {
+        constexpr int sbi = decltype(sbi_c)::value, buf = sbi & 1;
+        if (sbi < nsb) {
+          const int nt = FAST ? SB : sub_len(sbi);
+          if (sbi > 0) fetch(c0, (sbi - 1) * SB, SB);
+          float st[SB + 1][M], dif[SB], del[SB];
 #pragma unroll
-        for (int j = SB - 1; j >= 0; --j) {
-          if (j < nt) {
-            float kr[M], qr[M], x[M], xh[M], pq[M], pk[M], dh;
-            lds_slice<D, L>(&sk[buf][j * D], lane, kr);
-            lds_slice<D, L>(&sq[buf][j * D], lane, qr);
-            const float g = sg[buf][j * ROWS + row], a = sa[buf][j], b = sb[buf][j];
-            row_bwd_absorb<D, L>(sh, g, qr);
+          for (int e = 0; e < M; ++e) st[0][e] = ck[sbi][e];
 #pragma unroll
-            for (int e = 0; e < M; ++e) pq[e] = g * st[j + 1][e];
-            const float dv_i = row_bwd_delta<D, L>(sh, kr, b, xh, dh);
-            if constexpr (SEQ) {
-              if (lane == 0) sdv[j][row] = dv_i;
-            }
-            const float pb = dh * dif[j];
-            const float uh = -dv_i;
-            row_decay<D, L>(st[j], a, x);
+          for (int j = 0; j < SB; ++j) {
+            if (FAST || j < nt) {  // the forward sweep left v_i - u of each token: no dot here
+              float kr[M], x[M];
+              lds_slice<D, L>(&sk[buf][j * D], lane, kr);
+              row_decay<D, L>(st[j], sa[buf][j], x);
+              dif[j] = sdif[sbi * SB + j][row];
+              del[j] = sb[buf][j] * dif[j];
 #pragma unroll
-            for (int e = 0; e < M; ++e) {
-              const float ds = del[j] * sh[e];
-              pk[e] = __builtin_fmaf(uh, x[e], ds);
+              for (int e = 0; e < M; ++e) st[j + 1][e] = st[j][e];
+              row_update<D, L>(st[j + 1], del[j], kr, x);
             }
-            const float pa = contract_dot<D, L>(xh, st[j]);
-            row_bwd_decay<D, L>(sh, a, xh);
-            float z[H], y;
-            if (full4)
-              rows4_sum<M, true>(pq, pk, pa, pb, c1, c2, z, y);
-            else
-              rows4_sum<M, false>(pq, pk, pa, pb, c1, c2, z, y);
-            float *dst = &swave[j][wave][0];
-            if constexpr (H == 4) {
-              *reinterpret_cast<float4 *>(dst + zofs) = make_float4(z[0], z[1], z[2], z[3]);
-            } else if constexpr (H == 2) {
-              *reinterpret_cast<float2 *>(dst + zofs) = make_float2(z[0], z[1]);
-            } else {
-              if (zwrite) dst[zofs] = z[0];
-            }
-            if (ywrite) dst[yofs] = y;
           }
-        }
-        __syncthreads();
-        // across the waves (wave w holds rows r0 + 4w .. r0 + 4w + 3), pairwise, pass-through;
-        // four consecutive shares per thread (one 16-byte read per wave, one 16-byte store).
-        // The last group of a token holds da, db and two padding slots, whose sums nothing
-        // reads.
-        constexpr int G4 = PWP / 4;
-        for (int e = tid; e < nt * G4; e += kThreads) {
-          const int j = e / G4, f = 4 * (e % G4);
-          float4 w[WAVES];
 #pragma unroll
-          for (int x = 0; x < WAVES; ++x) w[x] = *reinterpret_cast<const float4 *>(&swave[j][x][f]);
+          for (int j = SB - 1; j >= 0; --j) {
+            if (FAST || j < nt) {
+              float kr[M], qr[M], x[M], xh[M], pq[M], pk[M], dh;
+              lds_slice<D, L>(&sk[buf][j * D], lane, kr);
+              lds_slice<D, L>(&sq[buf][j * D], lane, qr);
+              const float g = sg[buf][j * ROWS + row], a = sa[buf][j], b = sb[buf][j];
+              row_bwd_absorb<D, L>(sh, g, qr);
 #pragma unroll
-          for (int st = 1; st < WAVES; st *= 2)
-#pragma unroll
-            for (int x = 0; x + st < WAVES; x += 2 * st)
-              if (r0 + (x + st) * RPW < dv) {
-                w[x].x = w[x].x + w[x + st].x;
-                w[x].y = w[x].y + w[x + st].y;
-                w[x].z = w[x].z + w[x + st].z;
-                w[x].w = w[x].w + w[x + st].w;
+              for (int e = 0; e < M; ++e) pq[e] = g * st[j + 1][e];
+              const float dv_i = row_bwd_delta<D, L>(sh, kr, b, xh, dh);
+              if constexpr (SEQ) {
+                if (lane == 0) sdv[j][row] = dv_i;
               }
-          const int64_t t = bos + c0 + sbi * SB + j;
-          *reinterpret_cast<float4 *>(&p.partials[((t * Hv + h) * RB + rblock) * PWP + f]) = w[0];
-        }
-        if constexpr (SEQ) {
-          for (int e = tid; e < nt * ROWS; e += kThreads) {
-            const int j = e / ROWS, r = e % ROWS;
-            if (r0 + r < dv)
-              p.dv[(bos + c0 + sbi * SB + j) * vstride + (int64_t)h * dv + r0 + r] = sdv[j][r];
+              const float pb = dh * dif[j];
+              const float uh = -dv_i;
+              row_decay<D, L>(st[j], a, x);
+#pragma unroll
+              for (int e = 0; e < M; ++e) {
+                const float ds = del[j] * sh[e];
+                pk[e] = __builtin_fmaf(uh, x[e], ds);
+              }
+              const float pa = contract_dot<D, L>(xh, st[j]);
+              row_bwd_decay<D, L>(sh, a, xh);
+              float z[H], y;
+              if (FAST || full4)
+                rows4_sum<M, true>(pq, pk, pa, pb, c1, c2, z, y);
+              else
+                rows4_sum<M, false>(pq, pk, pa, pb, c1, c2, z, y);
+              float *dst = &swave[j][wave][0];
+              if constexpr (H == 4) {
+                *reinterpret_cast<float4 *>(dst + zofs) = make_float4(z[0], z[1], z[2], z[3]);
+              } else if constexpr (H == 2) {
+                *reinterpret_cast<float2 *>(dst + zofs) = make_float2(z[0], z[1]);
+              } else {
+                if (zwrite) dst[zofs] = z[0];
+              }
+              if (ywrite) dst[yofs] = y;
+            }
           }
+          __syncthreads();
+          // across the waves (wave w holds rows r0 + 4w .. r0 + 4w + 3), pairwise, pass-through;
+          // four consecutive shares per thread (one 16-byte read per wave, one 16-byte store).
+          // The last group of a token holds da, db and two padding slots, whose sums nothing
+          // reads.
+          constexpr int G4 = PWP / 4;
+          for (int e = tid; e < nt * G4; e += kThreads) {
+            const int j = e / G4, f = 4 * (e % G4);
+            float4 w[WAVES];
+#pragma unroll
+            for (int x = 0; x < WAVES; ++x) w[x] = *reinterpret_cast<const float4 *>(&swave[j][x][f]);
+#pragma unroll
+            for (int st = 1; st < WAVES; st *= 2)
+#pragma unroll
+              for (int x = 0; x + st < WAVES; x += 2 * st)
+                if (r0 + (x + st) * RPW < dv) {
+                  w[x].x = w[x].x + w[x + st].x;
+                  w[x].y = w[x].y + w[x + st].y;
+                  w[x].z = w[x].z + w[x + st].z;
+                  w[x].w = w[x].w + w[x + st].w;
+                }
+            const int64_t t = bos + c0 + sbi * SB + j;
+            *reinterpret_cast<float4 *>(&p.partials[((t * Hv + h) * RB + rblock) * PWP + f]) = w[0];
+          }
+          if constexpr (SEQ) {
+            for (int e = tid; e < nt * ROWS; e += kThreads) {
+              const int j = e / ROWS, r = e % ROWS;
+              if (r0 + r < dv)
+                p.dv[(bos + c0 + sbi * SB + j) * vstride + (int64_t)h * dv + r0 + r] = sdv[j][r];
+            }
+          }
+          if (sbi > 0) deposit(buf ^ 1);  // its last reader finished before the barrier above
+          __syncthreads();
         }
-        if (sbi > 0) deposit(buf ^ 1);  // its last reader finished before the barrier above
-        __syncthreads();
-      }
-    });
+      });
+    };
+    // full4 is the same in every lane of a wave and len in every lane of the workgroup.
+    // Chunks longer than a segment keep the general copy only: with both, the d_k = 128
+    // kernels for them run out of registers.
+    if constexpr (LONG)
+      segment(std::false_type{});
+    else if (__builtin_expect(__builtin_amdgcn_readfirstlane((int)(full4 && len % SB == 0)), 1))
+      segment(std::true_type{});
+    else
+      segment(std::false_type{});
    }  // segments
   }
   if constexpr (SEQ) {

@@ -66,12 +66,14 @@ def test_dpp_steps_are_adds(asm):
     assert dpp and set(dpp) <= {"v_add_f32_dpp", "v_mov_b32_dpp"}
 
 
-# The d_k = 128 backward chunk kernels for chunks longer than one 64-token segment, one
-# workgroup per chunk: the segment loop holds a 64-bit state-row address across the
-# segment advance, and the allocator keeps it in 8 bytes of scratch, reloaded once per
-# segment (not per token). Every other kernel uses no scratch.
+# The d_k = 128 backward chunk kernels for chunks longer than one 64-token segment: the
+# segment loop holds a 64-bit address across the segment advance, and the allocator keeps
+# it in 8 bytes of scratch, stored before the loop and reloaded once per segment (not per
+# token). Every other kernel uses no scratch.
 SPILL_ALLOWED = {"cpr_bwd_chunk_kernelILi128ELb0ELb0ELb1E": 16,
-                 "cpr_bwd_chunk_kernelILi128ELb1ELb0ELb1E": 16}
+                 "cpr_bwd_chunk_kernelILi128ELb1ELb0ELb1E": 16,
+                 "cpr_bwd_chunk_kernelILi128ELb0ELb1ELb1E": 16,
+                 "cpr_bwd_chunk_kernelILi128ELb1ELb1ELb1E": 16}
 
 
 def test_no_spills(asm):
