@@ -164,8 +164,10 @@ def verdict(checks):
 def valu_probe():
     """Vector-issue ceiling and shader clock of this GPU, from libgdn_probe.so: SIMD-cycles
     per wave instruction for plain multiplies, fused multiply-adds and DPP adds with one, two
-    and four waves per SIMD, the fused multiply-add rate at two waves per SIMD, and the shader
-    clock (s_memtime against the 100 MHz s_memrealtime)."""
+    and four waves per SIMD, the fused multiply-add rate at two waves per SIMD, the latency
+    of a dependent fused multiply-add and of a dependent DPP add level (shader cycles per step
+    of one chain per lane, one wave per SIMD), and the shader clock (s_memtime against the
+    100 MHz s_memrealtime)."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "bitwise_consistent_linear_amd", "libgdn_probe.so")
@@ -205,6 +207,17 @@ def valu_probe():
                 fma2 = 2 * 64 * 1024 * insts_per_simd / (ms * 1e-3) / 1e12
         out[name] = row
     out["v_fmac_f32_TFLOPs_at_2_waves_per_simd"] = round(fma2, 1)
+    # latency: one dependent chain per lane, one wave per SIMD, shader cycles per step
+    for form, name in ((3, "dependent_v_fmac_f32"), (4, "dependent_dpp_add_level")):
+        grid = 256
+        buf = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+        clk = torch.empty(grid * 2, dtype=torch.int64, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        if L.gdn_probe_valu(form, 1, iters, buf.data_ptr(), clk.data_ptr(), stream):
+            return None
+        torch.cuda.synchronize()
+        c = clk.view(grid, 2).double().sum(0)
+        out[name + "_cycles_per_step"] = round(float(c[0]) / grid / (iters * per_iter), 2)
     out["shader_clock_GHz"] = round(sum(clocks) / len(clocks), 3)
     return out
 

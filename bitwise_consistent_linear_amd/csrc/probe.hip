@@ -21,7 +21,11 @@
 // clock (s_memtime) and constant 100 MHz clock (s_memrealtime) of its first wave, from which
 // the caller derives the clock frequency. Forms: 0 = v_mul_f32 (vector x vector),
 // 1 = v_fmac_f32 (vector x vector + accumulator), 2 = v_add_f32 with a DPP row_mirror
-// operand. All reads and writes stay inside out[grid * 256] and clk[grid * 2].
+// operand. Forms 3 and 4 measure latency instead: one dependent chain per lane of
+// `iters` x 128 steps, 3 = v_fmac_f32 whose accumulator is the previous step's result,
+// 4 = v_add_f32 whose DPP quad_perm [1,0,3,2] operand is the partner lane's previous result
+// (the shape of a reduction tree's levels). Every form issues 128 instructions per lane per
+// iteration. All reads and writes stay inside out[grid * 256] and clk[grid * 2].
 
 #include <hip/hip_runtime.h>
 
@@ -49,18 +53,33 @@ __global__ __launch_bounds__(kThreads) void valu_probe_kernel(float *out, long l
   const long long t0 = __builtin_amdgcn_s_memtime();
   const long long r0 = __builtin_amdgcn_s_memrealtime();
   for (int i = 0; i < iters; ++i) {
+    if constexpr (FORM <= 2) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+      for (int u = 0; u < 16; ++u) {
 #pragma unroll
-      for (int c = 0; c < kChains; ++c) {
-        if constexpr (FORM == 0) {
-          x[c] = x[c] * z;
-        } else if constexpr (FORM == 1) {
-          x[c] = __builtin_fmaf(y[c], z, x[c]);
+        for (int c = 0; c < kChains; ++c) {
+          if constexpr (FORM == 0) {
+            x[c] = x[c] * z;
+          } else if constexpr (FORM == 1) {
+            x[c] = __builtin_fmaf(y[c], z, x[c]);
+          } else {
+            const int moved = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x[c]),
+                                                          0x140, 0xF, 0xF, true);
+            x[c] = y[c] + __builtin_bit_cast(float, moved);
+          }
+        }
+      }
+    } else {
+      // one chain: each step reads the previous step's result; it grows by at most
+      // about 0.5 per step, so it stays finite for any iteration count the host asks for
+#pragma unroll
+      for (int u = 0; u < 16 * kChains; ++u) {
+        if constexpr (FORM == 3) {
+          x[0] = __builtin_fmaf(y[u % kChains], z, x[0]);
         } else {
-          const int moved = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x[c]),
-                                                        0x140, 0xF, 0xF, true);
-          x[c] = y[c] + __builtin_bit_cast(float, moved);
+          const int moved = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x[0]),
+                                                        0xB1, 0xF, 0xF, true);
+          x[0] = y[u % kChains] + __builtin_bit_cast(float, moved);
         }
       }
     }
@@ -135,15 +154,17 @@ GDN_PROBE_EXPORT int gdn_probe_mfma(int form, const float *a, const float *b, co
 // Launches the probe on `stream` (hipStream_t or NULL). grid = 256 * waves_per_simd
 // workgroups; out must hold grid * 256 floats and clk grid * 2 int64, both device memory.
 // Returns 0, or -1 for arguments outside 1 <= waves_per_simd <= 16, iters >= 1,
-// 0 <= form <= 2, non-null buffers, or a launch error.
+// 0 <= form <= 4, non-null buffers, or a launch error.
 GDN_PROBE_EXPORT int gdn_probe_valu(int form, int waves_per_simd, int iters, float *out,
                                     long long *clk, void *stream) {
-  if (form < 0 || form > 2 || waves_per_simd < 1 || waves_per_simd > 16 || iters < 1 || !out ||
+  if (form < 0 || form > 4 || waves_per_simd < 1 || waves_per_simd > 16 || iters < 1 || !out ||
       !clk)
     return -1;
   const void *fn = form == 0   ? (const void *)valu_probe_kernel<0>
                    : form == 1 ? (const void *)valu_probe_kernel<1>
-                               : (const void *)valu_probe_kernel<2>;
+                   : form == 2 ? (const void *)valu_probe_kernel<2>
+                   : form == 3 ? (const void *)valu_probe_kernel<3>
+                               : (const void *)valu_probe_kernel<4>;
   float seed = 0.999f;
   void *args[] = {&out, &clk, &iters, &seed};
   const hipError_t e = hipLaunchKernel(fn, dim3(256u * (unsigned)waves_per_simd),
