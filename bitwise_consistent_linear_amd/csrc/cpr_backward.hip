@@ -61,6 +61,18 @@ __device__ __forceinline__ void static_for(F &&f) {
 __global__ __launch_bounds__(kThreads) void cpr_bwd_plan_kernel(const BwdArgs p) {
   chunk_plan(p.cu_seqlens, p.num_seqs, p.total_tokens, p.chunk, p.total_chunks, p.slots_max,
              p.plan, p.plan_cbase);
+  // plan[1] = 1 when some sequence's length is not a multiple of the 8-token sub-block, so
+  // that only the chunk kernel with the general token loops may run
+  __shared__ int s_ragged;
+  if (threadIdx.x == 0) s_ragged = 0;
+  __syncthreads();
+  for (int m = threadIdx.x; m < p.num_seqs; m += kThreads) {
+    int64_t b, e;
+    seq_range(p.cu_seqlens, m, p.total_tokens, b, e);
+    if ((e - b) % kSub != 0) atomicOr(&s_ragged, 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) p.plan[1] = s_ragged;
 }
 
 // ---------------------------------------------------------------------------- state pass
@@ -272,9 +284,23 @@ __device__ __forceinline__ void rows4_sum(const float (&pq)[M], const float (&pk
 //                writes dv and dS0 itself, so the state pass does not run.
 // Checkpoints and a sub-block of recomputed states live in registers: allow up to 256
 // VGPRs (two waves per SIMD) rather than spill.
-template <int D, bool BF16, bool SEQ, bool LONG>
+// WHOLE: every sub-block of the batch is whole (plan[1] == 0) and d_v is a multiple of the
+// four rows of a wave, so no token is skipped and no row of a wave that counts passes
+// through: the token loops (the forward sweep's included) run a fixed 8 tokens with no
+// per-token branch, every lane of a row stores the row's values to LDS (the same value to
+// the same place), and the scheduler can overlap one token's reduction trees with its
+// neighbours' arithmetic. The host launches the WHOLE kernel next to the general one where
+// d_v allows (p.whole = 1); whichever does not match plan[1] returns at once. The same
+// operations either way.
+template <int D, bool BF16, bool SEQ, bool LONG, bool WHOLE>
 __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void cpr_bwd_chunk_kernel(const BwdArgs p) {
+  static_assert(!(WHOLE && LONG), "chunks longer than a segment take the general loops");
+  if constexpr (WHOLE) {
+    if (p.plan[1] != 0) return;  // uniform: a ragged batch
+  } else {
+    if (p.whole && p.plan[1] == 0) return;  // uniform: the WHOLE kernel has the batch
+  }
   constexpr int kThreads = kChunkThreads;
   constexpr int L = kChunkLanes, ROWS = kChunkRows, M = D / L, SB = kSub;
   constexpr int WAVES = kChunkWaves, RPW = 64 / L;  // rows per wave
@@ -446,149 +472,131 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
     const int len = clen - seg * kSeg < kSeg ? clen - seg * kSeg : kSeg;
     const int nsb = (len + SB - 1) / SB;
     auto sub_len = [&](int sbi) { return len - sbi * SB < SB ? len - sbi * SB : SB; };
-    // The segment's sub-blocks. FAST: every sub-block whole (len a multiple of SB) and all
-    // four rows of this wave below d_v, so no token is skipped and no row passes through;
-    // the token loops then carry no per-token branch, and the scheduler can overlap one
-    // token's reduction trees with its neighbours' arithmetic. The same operations either
-    // way. Both copies hold the same barriers in the same order, so waves of one workgroup
-    // may take different copies.
-    auto segment = [&](auto fast_c) {
-      constexpr bool FAST = decltype(fast_c)::value;
-      fetch(c0, 0, sub_len(0));
-      deposit(0);  // buffer 0's last reader (the previous chunk) finished before its barrier
-      __syncthreads();
+    fetch(c0, 0, sub_len(0));
+    deposit(0);  // buffer 0's last reader (the previous chunk) finished before its barrier
+    __syncthreads();
 
-      // forward over the chunk, keeping the state at the start of every sub-block
-      float ck[kMaxSub][M];
-      static_for<kMaxSub>([&](auto sbi_c) {
-        constexpr int sbi = decltype(sbi_c)::value, buf = sbi & 1;
-        if (sbi < nsb) {
-          const bool next = sbi + 1 < nsb;
-          if (next) fetch(c0, (sbi + 1) * SB, sub_len(sbi + 1));
+    // forward over the chunk, keeping the state at the start of every sub-block
+    float ck[kMaxSub][M];
+    static_for<kMaxSub>([&](auto sbi_c) {
+      constexpr int sbi = decltype(sbi_c)::value, buf = sbi & 1;
+      if (sbi < nsb) {
+        const bool next = sbi + 1 < nsb;
+        if (next) fetch(c0, (sbi + 1) * SB, sub_len(sbi + 1));
 #pragma unroll
-          for (int e = 0; e < M; ++e) ck[sbi][e] = s[e];
-          const int nt = sub_len(sbi);
-          for (int j = 0; j < nt; ++j) {
+        for (int e = 0; e < M; ++e) ck[sbi][e] = s[e];
+        const int nt = WHOLE ? SB : sub_len(sbi);
+        for (int j = 0; j < nt; ++j) {
+          float kr[M], x[M];
+          lds_slice<D, L>(&sk[buf][j * D], lane, kr);
+          row_decay<D, L>(s, sa[buf][j], x);
+          const float u = contract_dot<D, L>(x, kr);
+          const float dif = sv[buf][j * ROWS + row] - u;  // d = b (v_i - u), as row_delta
+          if (WHOLE || lane == 0) sdif[sbi * SB + j][row] = dif;
+          row_update<D, L>(s, sb[buf][j] * dif, kr, x);
+        }
+        if (next) deposit(buf ^ 1);  // its last reader finished before the previous barrier
+        __syncthreads();
+      }
+    });
+
+    // sub-blocks in reverse: recompute the states, run sh back, sum the shares over rows
+    static_for<kMaxSub, true>([&](auto sbi_c) {
+      constexpr int sbi = decltype(sbi_c)::value, buf = sbi & 1;
+      if (sbi < nsb) {
+        const int nt = WHOLE ? SB : sub_len(sbi);
+        if (sbi > 0) fetch(c0, (sbi - 1) * SB, SB);
+        float st[SB + 1][M], dif[SB], del[SB];
+#pragma unroll
+        for (int e = 0; e < M; ++e) st[0][e] = ck[sbi][e];
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+          if (WHOLE || j < nt) {  // the forward sweep left v_i - u of each token: no dot here
             float kr[M], x[M];
             lds_slice<D, L>(&sk[buf][j * D], lane, kr);
-            row_decay<D, L>(s, sa[buf][j], x);
-            const float u = contract_dot<D, L>(x, kr);
-            const float dif = sv[buf][j * ROWS + row] - u;  // d = b (v_i - u), as row_delta
-            if (lane == 0) sdif[sbi * SB + j][row] = dif;
-            row_update<D, L>(s, sb[buf][j] * dif, kr, x);
+            row_decay<D, L>(st[j], sa[buf][j], x);
+            dif[j] = sdif[sbi * SB + j][row];
+            del[j] = sb[buf][j] * dif[j];
+#pragma unroll
+            for (int e = 0; e < M; ++e) st[j + 1][e] = st[j][e];
+            row_update<D, L>(st[j + 1], del[j], kr, x);
           }
-          if (next) deposit(buf ^ 1);  // its last reader finished before the previous barrier
-          __syncthreads();
         }
-      });
-
-      // sub-blocks in reverse: recompute the states, run sh back, sum the shares over rows
-      static_for<kMaxSub, true>([&](auto sbi_c) {
-        constexpr int sbi = decltype(sbi_c)::value, buf = sbi & 1;
-        if (sbi < nsb) {
-          const int nt = FAST ? SB : sub_len(sbi);
-          if (sbi > 0) fetch(c0, (sbi - 1) * SB, SB);
-          float st[SB + 1][M], dif[SB], del[SB];
 #pragma unroll
-          for (int e = 0; e < M; ++e) st[0][e] = ck[sbi][e];
+        for (int j = SB - 1; j >= 0; --j) {
+          if (WHOLE || j < nt) {
+            float kr[M], qr[M], x[M], xh[M], pq[M], pk[M], dh;
+            lds_slice<D, L>(&sk[buf][j * D], lane, kr);
+            lds_slice<D, L>(&sq[buf][j * D], lane, qr);
+            const float g = sg[buf][j * ROWS + row], a = sa[buf][j], b = sb[buf][j];
+            row_bwd_absorb<D, L>(sh, g, qr);
 #pragma unroll
-          for (int j = 0; j < SB; ++j) {
-            if (FAST || j < nt) {  // the forward sweep left v_i - u of each token: no dot here
-              float kr[M], x[M];
-              lds_slice<D, L>(&sk[buf][j * D], lane, kr);
-              row_decay<D, L>(st[j], sa[buf][j], x);
-              dif[j] = sdif[sbi * SB + j][row];
-              del[j] = sb[buf][j] * dif[j];
-#pragma unroll
-              for (int e = 0; e < M; ++e) st[j + 1][e] = st[j][e];
-              row_update<D, L>(st[j + 1], del[j], kr, x);
+            for (int e = 0; e < M; ++e) pq[e] = g * st[j + 1][e];
+            const float dv_i = row_bwd_delta<D, L>(sh, kr, b, xh, dh);
+            if constexpr (SEQ) {
+              if (WHOLE || lane == 0) sdv[j][row] = dv_i;
             }
-          }
+            const float pb = dh * dif[j];
+            const float uh = -dv_i;
+            row_decay<D, L>(st[j], a, x);
 #pragma unroll
-          for (int j = SB - 1; j >= 0; --j) {
-            if (FAST || j < nt) {
-              float kr[M], qr[M], x[M], xh[M], pq[M], pk[M], dh;
-              lds_slice<D, L>(&sk[buf][j * D], lane, kr);
-              lds_slice<D, L>(&sq[buf][j * D], lane, qr);
-              const float g = sg[buf][j * ROWS + row], a = sa[buf][j], b = sb[buf][j];
-              row_bwd_absorb<D, L>(sh, g, qr);
-#pragma unroll
-              for (int e = 0; e < M; ++e) pq[e] = g * st[j + 1][e];
-              const float dv_i = row_bwd_delta<D, L>(sh, kr, b, xh, dh);
-              if constexpr (SEQ) {
-                if (lane == 0) sdv[j][row] = dv_i;
-              }
-              const float pb = dh * dif[j];
-              const float uh = -dv_i;
-              row_decay<D, L>(st[j], a, x);
-#pragma unroll
-              for (int e = 0; e < M; ++e) {
-                const float ds = del[j] * sh[e];
-                pk[e] = __builtin_fmaf(uh, x[e], ds);
-              }
-              const float pa = contract_dot<D, L>(xh, st[j]);
-              row_bwd_decay<D, L>(sh, a, xh);
-              float z[H], y;
-              if (FAST || full4)
-                rows4_sum<M, true>(pq, pk, pa, pb, c1, c2, z, y);
-              else
-                rows4_sum<M, false>(pq, pk, pa, pb, c1, c2, z, y);
-              float *dst = &swave[j][wave][0];
-              if constexpr (H == 4) {
-                *reinterpret_cast<float4 *>(dst + zofs) = make_float4(z[0], z[1], z[2], z[3]);
-              } else if constexpr (H == 2) {
-                *reinterpret_cast<float2 *>(dst + zofs) = make_float2(z[0], z[1]);
-              } else {
-                if (zwrite) dst[zofs] = z[0];
-              }
-              if (ywrite) dst[yofs] = y;
+            for (int e = 0; e < M; ++e) {
+              const float ds = del[j] * sh[e];
+              pk[e] = __builtin_fmaf(uh, x[e], ds);
             }
-          }
-          __syncthreads();
-          // across the waves (wave w holds rows r0 + 4w .. r0 + 4w + 3), pairwise, pass-through;
-          // four consecutive shares per thread (one 16-byte read per wave, one 16-byte store).
-          // The last group of a token holds da, db and two padding slots, whose sums nothing
-          // reads.
-          constexpr int G4 = PWP / 4;
-          for (int e = tid; e < nt * G4; e += kThreads) {
-            const int j = e / G4, f = 4 * (e % G4);
-            float4 w[WAVES];
-#pragma unroll
-            for (int x = 0; x < WAVES; ++x) w[x] = *reinterpret_cast<const float4 *>(&swave[j][x][f]);
-#pragma unroll
-            for (int st = 1; st < WAVES; st *= 2)
-#pragma unroll
-              for (int x = 0; x + st < WAVES; x += 2 * st)
-                if (r0 + (x + st) * RPW < dv) {
-                  w[x].x = w[x].x + w[x + st].x;
-                  w[x].y = w[x].y + w[x + st].y;
-                  w[x].z = w[x].z + w[x + st].z;
-                  w[x].w = w[x].w + w[x + st].w;
-                }
-            const int64_t t = bos + c0 + sbi * SB + j;
-            *reinterpret_cast<float4 *>(&p.partials[((t * Hv + h) * RB + rblock) * PWP + f]) = w[0];
-          }
-          if constexpr (SEQ) {
-            for (int e = tid; e < nt * ROWS; e += kThreads) {
-              const int j = e / ROWS, r = e % ROWS;
-              if (r0 + r < dv)
-                p.dv[(bos + c0 + sbi * SB + j) * vstride + (int64_t)h * dv + r0 + r] = sdv[j][r];
+            const float pa = contract_dot<D, L>(xh, st[j]);
+            row_bwd_decay<D, L>(sh, a, xh);
+            float z[H], y;
+            if (WHOLE || full4)
+              rows4_sum<M, true>(pq, pk, pa, pb, c1, c2, z, y);
+            else
+              rows4_sum<M, false>(pq, pk, pa, pb, c1, c2, z, y);
+            float *dst = &swave[j][wave][0];
+            if constexpr (H == 4) {
+              *reinterpret_cast<float4 *>(dst + zofs) = make_float4(z[0], z[1], z[2], z[3]);
+            } else if constexpr (H == 2) {
+              *reinterpret_cast<float2 *>(dst + zofs) = make_float2(z[0], z[1]);
+            } else {
+              if (zwrite) dst[zofs] = z[0];
             }
+            if (ywrite) dst[yofs] = y;
           }
-          if (sbi > 0) deposit(buf ^ 1);  // its last reader finished before the barrier above
-          __syncthreads();
         }
-      });
-    };
-    // full4 is the same in every lane of a wave and len in every lane of the workgroup.
-    // Chunks longer than a segment keep the general copy only: with both, the d_k = 128
-    // kernels for them run out of registers.
-    if constexpr (LONG)
-      segment(std::false_type{});
-    else if (__builtin_expect(__builtin_amdgcn_readfirstlane((int)(full4 && len % SB == 0)), 1))
-      segment(std::true_type{});
-    else
-      segment(std::false_type{});
+        __syncthreads();
+        // across the waves (wave w holds rows r0 + 4w .. r0 + 4w + 3), pairwise, pass-through;
+        // four consecutive shares per thread (one 16-byte read per wave, one 16-byte store).
+        // The last group of a token holds da, db and two padding slots, whose sums nothing
+        // reads.
+        constexpr int G4 = PWP / 4;
+        for (int e = tid; e < nt * G4; e += kThreads) {
+          const int j = e / G4, f = 4 * (e % G4);
+          float4 w[WAVES];
+#pragma unroll
+          for (int x = 0; x < WAVES; ++x) w[x] = *reinterpret_cast<const float4 *>(&swave[j][x][f]);
+#pragma unroll
+          for (int st = 1; st < WAVES; st *= 2)
+#pragma unroll
+            for (int x = 0; x + st < WAVES; x += 2 * st)
+              if (r0 + (x + st) * RPW < dv) {
+                w[x].x = w[x].x + w[x + st].x;
+                w[x].y = w[x].y + w[x + st].y;
+                w[x].z = w[x].z + w[x + st].z;
+                w[x].w = w[x].w + w[x + st].w;
+              }
+          const int64_t t = bos + c0 + sbi * SB + j;
+          *reinterpret_cast<float4 *>(&p.partials[((t * Hv + h) * RB + rblock) * PWP + f]) = w[0];
+        }
+        if constexpr (SEQ) {
+          for (int e = tid; e < nt * ROWS; e += kThreads) {
+            const int j = e / ROWS, r = e % ROWS;
+            if (r0 + r < dv)
+              p.dv[(bos + c0 + sbi * SB + j) * vstride + (int64_t)h * dv + r0 + r] = sdv[j][r];
+          }
+        }
+        if (sbi > 0) deposit(buf ^ 1);  // its last reader finished before the barrier above
+        __syncthreads();
+      }
+    });
    }  // segments
   }
   if constexpr (SEQ) {
@@ -670,19 +678,21 @@ const void *state_fn(int L, bool bf16) {
   }
 }
 
-template <int D, bool LONG>
+template <int D, bool LONG, bool WHOLE>
 const void *chunk_fn_len(bool bf16, bool seq) {
   if (seq)
-    return bf16 ? (const void *)cpr_bwd_chunk_kernel<D, true, true, LONG>
-                : (const void *)cpr_bwd_chunk_kernel<D, false, true, LONG>;
-  return bf16 ? (const void *)cpr_bwd_chunk_kernel<D, true, false, LONG>
-              : (const void *)cpr_bwd_chunk_kernel<D, false, false, LONG>;
+    return bf16 ? (const void *)cpr_bwd_chunk_kernel<D, true, true, LONG, WHOLE>
+                : (const void *)cpr_bwd_chunk_kernel<D, false, true, LONG, WHOLE>;
+  return bf16 ? (const void *)cpr_bwd_chunk_kernel<D, true, false, LONG, WHOLE>
+              : (const void *)cpr_bwd_chunk_kernel<D, false, false, LONG, WHOLE>;
 }
 
-// Chunks of at most kSeg tokens take the kernels without the segment advance.
+// Chunks of at most kSeg tokens take the kernels without the segment advance; `whole`
+// picks their branch-free variant (nullptr for longer chunks).
 template <int D>
-const void *chunk_fn(bool bf16, bool seq, int chunk) {
-  return chunk > kSeg ? chunk_fn_len<D, true>(bf16, seq) : chunk_fn_len<D, false>(bf16, seq);
+const void *chunk_fn(bool bf16, bool seq, int chunk, bool whole) {
+  if (chunk > kSeg) return whole ? nullptr : chunk_fn_len<D, true, false>(bf16, seq);
+  return whole ? chunk_fn_len<D, false, true>(bf16, seq) : chunk_fn_len<D, false, false>(bf16, seq);
 }
 
 }  // namespace
@@ -744,21 +754,30 @@ int64_t backward_chunk_grid(const BwdArgs &a, bool seq) {
   return (int64_t)(seq ? a.num_seqs : a.slots_max) * a.num_v_heads * a.row_blocks;
 }
 
-hipError_t launch_backward(const BwdArgs &a, int L, bool seq, hipStream_t st) {
-  if (a.row_blocks < 1 || a.row_blocks > 32) return hipErrorInvalidValue;  // d_v in [1, 1024]
+hipError_t launch_backward(const BwdArgs &args, int L, bool seq, hipStream_t st) {
+  if (args.row_blocks < 1 || args.row_blocks > 32) return hipErrorInvalidValue;  // d_v <= 1024
+  BwdArgs a = args;
+  // The branch-free chunk kernel needs whole waves of rows (every wave's four rows below d_v
+  // or none) and chunks of one segment; it runs when the plan finds no ragged sequence.
+  a.whole = a.chunk <= kSeg && a.d_v % (64 / kChunkLanes) == 0;
   hipError_t e = launch1((const void *)cpr_bwd_plan_kernel, 1, a, st);
   if (e != hipSuccess) return e;
-  const void *sf, *cf;
+  const void *sf, *cf, *wf;
   switch (a.d_k) {
-    case 16: sf = state_fn<16>(L, a.bf16); cf = chunk_fn<16>(a.bf16, seq, a.chunk); break;
-    case 32: sf = state_fn<32>(L, a.bf16); cf = chunk_fn<32>(a.bf16, seq, a.chunk); break;
-    case 64: sf = state_fn<64>(L, a.bf16); cf = chunk_fn<64>(a.bf16, seq, a.chunk); break;
-    case 128: sf = state_fn<128>(L, a.bf16); cf = chunk_fn<128>(a.bf16, seq, a.chunk); break;
+    case 16: sf = state_fn<16>(L, a.bf16); cf = chunk_fn<16>(a.bf16, seq, a.chunk, false);
+             wf = chunk_fn<16>(a.bf16, seq, a.chunk, true); break;
+    case 32: sf = state_fn<32>(L, a.bf16); cf = chunk_fn<32>(a.bf16, seq, a.chunk, false);
+             wf = chunk_fn<32>(a.bf16, seq, a.chunk, true); break;
+    case 64: sf = state_fn<64>(L, a.bf16); cf = chunk_fn<64>(a.bf16, seq, a.chunk, false);
+             wf = chunk_fn<64>(a.bf16, seq, a.chunk, true); break;
+    case 128: sf = state_fn<128>(L, a.bf16); cf = chunk_fn<128>(a.bf16, seq, a.chunk, false);
+              wf = chunk_fn<128>(a.bf16, seq, a.chunk, true); break;
     default: return hipErrorInvalidValue;
   }
   if (!seq && (e = launch1(sf, backward_state_grid(a, L), a, st)) != hipSuccess) return e;
-  if ((e = launch1(cf, backward_chunk_grid(a, seq), a, st, kChunkThreads)) != hipSuccess)
-    return e;
+  const int64_t cgrid = backward_chunk_grid(a, seq);
+  if (a.whole && (e = launch1(wf, cgrid, a, st, kChunkThreads)) != hipSuccess) return e;
+  if ((e = launch1(cf, cgrid, a, st, kChunkThreads)) != hipSuccess) return e;
   const int64_t items = a.total_tokens * (a.num_qk_heads * (int64_t)a.d_k + a.num_v_heads);
   const int64_t grid = std::min<int64_t>((items + kThreads - 1) / kThreads, 65536);
   const void *comb;
