@@ -61,18 +61,6 @@ __device__ __forceinline__ void static_for(F &&f) {
 __global__ __launch_bounds__(kThreads) void cpr_bwd_plan_kernel(const BwdArgs p) {
   chunk_plan(p.cu_seqlens, p.num_seqs, p.total_tokens, p.chunk, p.total_chunks, p.slots_max,
              p.plan, p.plan_cbase);
-  // plan[1] = 1 when some sequence's length is not a multiple of the 8-token sub-block, so
-  // that only the chunk kernel with the general token loops may run
-  __shared__ int s_ragged;
-  if (threadIdx.x == 0) s_ragged = 0;
-  __syncthreads();
-  for (int m = threadIdx.x; m < p.num_seqs; m += kThreads) {
-    int64_t b, e;
-    seq_range(p.cu_seqlens, m, p.total_tokens, b, e);
-    if ((e - b) % kSub != 0) atomicOr(&s_ragged, 1);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) p.plan[1] = s_ragged;
 }
 
 // ---------------------------------------------------------------------------- state pass
@@ -284,23 +272,21 @@ __device__ __forceinline__ void rows4_sum(const float (&pq)[M], const float (&pk
 //                writes dv and dS0 itself, so the state pass does not run.
 // Checkpoints and a sub-block of recomputed states live in registers: allow up to 256
 // VGPRs (two waves per SIMD) rather than spill.
-// WHOLE: every sub-block of the batch is whole (plan[1] == 0) and d_v is a multiple of the
-// four rows of a wave, so no token is skipped and no row of a wave that counts passes
-// through: the token loops (the forward sweep's included) run a fixed 8 tokens with no
-// per-token branch, every lane of a row stores the row's values to LDS (the same value to
-// the same place), and the scheduler can overlap one token's reduction trees with its
-// neighbours' arithmetic. The host launches the WHOLE kernel next to the general one where
-// d_v allows (p.whole = 1); whichever does not match plan[1] returns at once. The same
-// operations either way.
+// WHOLE: every sub-block it takes is whole (8 tokens) and d_v is a multiple of the four rows
+// of a wave, so no token is skipped and no row of a wave that counts passes through: the
+// token loops (the forward sweep's included) run a fixed 8 tokens with no per-token branch,
+// every lane of a row stores the row's values to LDS (the same value to the same place),
+// and the scheduler can overlap one token's reduction trees with its neighbours'
+// arithmetic. Where d_v allows and C <= 64 the host sets p.whole and launches the general
+// kernel, then the WHOLE one. Only a sequence's last chunk can hold a partial sub-block (C
+// is a multiple of 8), so the general kernel then takes just those chunks of ragged
+// sequences (length not a multiple of 8): on the sequence schedule it runs that chunk and
+// leaves dL/ds at its start in the boundary buffer (or dS0 for a one-chunk sequence), and
+// the WHOLE kernel sweeps the chunks below it from there. The same operations either way.
 template <int D, bool BF16, bool SEQ, bool LONG, bool WHOLE>
 __global__ __launch_bounds__(kChunkThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void cpr_bwd_chunk_kernel(const BwdArgs p) {
   static_assert(!(WHOLE && LONG), "chunks longer than a segment take the general loops");
-  if constexpr (WHOLE) {
-    if (p.plan[1] != 0) return;  // uniform: a ragged batch
-  } else {
-    if (p.whole && p.plan[1] == 0) return;  // uniform: the WHOLE kernel has the batch
-  }
   constexpr int kThreads = kChunkThreads;
   constexpr int L = kChunkLanes, ROWS = kChunkRows, M = D / L, SB = kSub;
   constexpr int WAVES = kChunkWaves, RPW = 64 / L;  // rows per wave
@@ -324,6 +310,7 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
   const int Hv = p.num_v_heads, Hk = p.num_qk_heads, dv = p.d_v, RB = p.row_blocks;
   int pair, rblock, n, h, c_hi, c_lo;
   int64_t bos, eos;
+  bool from_bnd = !SEQ;  // dL/ds at the end of chunk c_hi comes from the boundary buffer
   if constexpr (SEQ) {
     block_work(blockIdx.x, p.num_seqs * Hv, RB, 1, pair, rblock);
     h = pair % Hv;
@@ -331,6 +318,17 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
     seq_range(p.cu_seqlens, n, p.total_tokens, bos, eos);
     c_hi = (int)((eos - bos + p.chunk - 1) / p.chunk) - 1;
     c_lo = 0;
+    if (p.whole && (eos - bos) % SB != 0) {  // uniform: a ragged sequence
+      if constexpr (WHOLE) {
+        if (c_hi == 0) return;  // its only chunk is the general kernel's
+        c_hi -= 1;              // from the boundary the general kernel left
+        from_bnd = true;
+      } else {
+        c_lo = c_hi;  // its last chunk only
+      }
+    } else if (!WHOLE && p.whole) {
+      return;  // uniform: the WHOLE kernel has this sequence
+    }
   } else {
     block_work(blockIdx.x, p.slots_max * Hv, RB, 1, pair, rblock);
     const int slot = pair / Hv;
@@ -340,6 +338,11 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
     c_hi = c_lo = p.plan[kPlanHeader + 2 * slot + 1];
     seq_range(p.cu_seqlens, n, p.total_tokens, bos, eos);
     if ((int64_t)c_hi * p.chunk >= eos - bos) return;  // uniform
+    if (p.whole) {  // uniform: a chunk with a partial sub-block is the general kernel's
+      const int64_t clen = eos - bos - (int64_t)c_hi * p.chunk;
+      const bool ragged = (clen < p.chunk ? clen : p.chunk) % SB != 0;
+      if (ragged == WHOLE) return;
+    }
   }
   const int64_t Tn = eos - bos;
   const int64_t cbase = p.plan_cbase[n];
@@ -355,7 +358,7 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
   {
     const int lane = threadIdx.x % L, i = r0 + (int)threadIdx.x / L;
     if (i < dv) {
-      if (!SEQ && ((int64_t)c_hi + 1) * p.chunk <= Tn) {
+      if (from_bnd && ((int64_t)c_hi + 1) * p.chunk <= Tn) {
         if (cbase + c_hi < p.total_chunks)
           load_row<M>(p.dsh_bnd + (((cbase + c_hi) * Hv + h) * dv + i) * D + lane * M, sh);
       } else if (p.d_final_state) {
@@ -603,7 +606,14 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
     int t = threadIdx.x;
     asm volatile("" : "+v"(t));  // recomputed here rather than held across the chunk loop
     const int lane = t % L, i = r0 + t / L;
-    if (i < dv) store_row<M>(p.d_initial_state + row_offset(i, lane), sh);
+    if (i < dv) {
+      if (!WHOLE && c_lo > 0) {  // a ragged sequence's last chunk: dL/ds at its start
+        if (cbase + c_lo - 1 < p.total_chunks)
+          store_row<M>(p.dsh_bnd + (((cbase + c_lo - 1) * Hv + h) * dv + i) * D + lane * M, sh);
+      } else {
+        store_row<M>(p.d_initial_state + row_offset(i, lane), sh);
+      }
+    }
   }
 }
 
@@ -758,7 +768,8 @@ hipError_t launch_backward(const BwdArgs &args, int L, bool seq, hipStream_t st)
   if (args.row_blocks < 1 || args.row_blocks > 32) return hipErrorInvalidValue;  // d_v <= 1024
   BwdArgs a = args;
   // The branch-free chunk kernel needs whole waves of rows (every wave's four rows below d_v
-  // or none) and chunks of one segment; it runs when the plan finds no ragged sequence.
+  // or none) and chunks of one segment; it runs after the general kernel, which then takes
+  // only the chunks with a partial sub-block.
   a.whole = a.chunk <= kSeg && a.d_v % (64 / kChunkLanes) == 0;
   hipError_t e = launch1((const void *)cpr_bwd_plan_kernel, 1, a, st);
   if (e != hipSuccess) return e;
@@ -776,8 +787,8 @@ hipError_t launch_backward(const BwdArgs &args, int L, bool seq, hipStream_t st)
   }
   if (!seq && (e = launch1(sf, backward_state_grid(a, L), a, st)) != hipSuccess) return e;
   const int64_t cgrid = backward_chunk_grid(a, seq);
-  if (a.whole && (e = launch1(wf, cgrid, a, st, kChunkThreads)) != hipSuccess) return e;
   if ((e = launch1(cf, cgrid, a, st, kChunkThreads)) != hipSuccess) return e;
+  if (a.whole && (e = launch1(wf, cgrid, a, st, kChunkThreads)) != hipSuccess) return e;
   const int64_t items = a.total_tokens * (a.num_qk_heads * (int64_t)a.d_k + a.num_v_heads);
   const int64_t grid = std::min<int64_t>((items + kThreads - 1) / kThreads, 65536);
   const void *comb;

@@ -53,7 +53,8 @@ struct BwdArgs {
   int32_t bf16;
   int32_t slots_max;   // chunk slots the plan may fill: total_chunks + num_seqs
   int32_t row_blocks;  // blocks of 32 rows per value head in the chunk kernel
-  int32_t whole;       // set by the launcher: the branch-free chunk kernel is launched too
+  int32_t whole;       // set by the launcher: the branch-free chunk kernel runs after the
+                       // general one, which then takes only chunks with a partial sub-block
   int64_t total_tokens;
   int64_t total_chunks;
   const int32_t *cu_seqlens;
@@ -61,8 +62,7 @@ struct BwdArgs {
   const float *a, *b, *initial_state, *chunk_states, *d_o, *d_final_state;
   float *dq, *dk, *dv, *da, *db, *d_initial_state;
   // workspace
-  int32_t *plan;        // [0]: slots used; [1]: 1 if a length is not a multiple of 8;
-                        // then (sequence, chunk) pairs
+  int32_t *plan;        // [0]: slots used; then (sequence, chunk) pairs
   int32_t *plan_cbase;  // [N]: index of each sequence's first chunk state
   float *dsh_bnd;       // [total_chunks, Hv, d_v, d_k]: dL/ds at chunk ends
   float *partials;      // [T, Hv, row_blocks, 2 d_k + 4]: row-block sums of the shares
