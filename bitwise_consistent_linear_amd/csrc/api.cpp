@@ -73,14 +73,29 @@ int scan_lanes(const ScanArgs &a) {
   return 4;
 }
 
-// Tokens per LDS stage of the scan: 64 for a lone wave per SIMD at 16 lanes per row with
-// bf16 inputs (its 149 KiB of LDS at d_k = 128 then fits the one workgroup per CU it needs;
-// measured 3.7 % faster than 32 on the long-context prefill), for the trainer case only
-// when C >= 64. Chunk boundaries inside a 64-token stage would have to be kept in
-// registers, and binary32 inputs double the staging registers: either takes the kernel
-// past 256 registers, which ran 3.3 times slower. 32 for 8 or 16 lanes otherwise (two
-// workgroups per CU), 16 for 4 lanes per row.
+// Threads per scan workgroup: 512 (32 rows at 16 lanes per row) where two waves per SIMD
+// run at 16 lanes per row with bf16 inputs, d_v a multiple of 32 and, for the trainer,
+// C >= 64: one workgroup per CU then stages 64 tokens once for both waves of every SIMD,
+// where two 256-thread workgroups would each stage 32. 256 otherwise.
+// GDN_CPR_SCAN_THREADS=256 keeps 256 (the same bits either way).
+int scan_threads(const ScanArgs &a, int L) {
+  const char *env = std::getenv("GDN_CPR_SCAN_THREADS");
+  if (env && std::strcmp(env, "256") == 0) return 256;
+  if (L != 16 || !a.bf16 || a.d_v % 32 != 0 || (a.mode == kTrainer && a.chunk < 64)) return 256;
+  const int64_t rows = (int64_t)a.num_seqs * a.num_v_heads * a.d_v;
+  const int64_t simds = device_simds();
+  return rows / 4 > simds && rows / 4 <= 2 * simds ? 512 : 256;
+}
+
+// Tokens per LDS stage of the scan: 64 in a 512-thread workgroup, and for a lone wave per
+// SIMD at 16 lanes per row with bf16 inputs (its 145 KiB of LDS at d_k = 128 then fits the
+// one workgroup per CU it needs; measured 3.7 % faster than 32 on the long-context
+// prefill), for the trainer case only when C >= 64. Chunk boundaries inside a 64-token
+// stage would have to be kept in registers, and binary32 inputs double the staging
+// registers: either takes the kernel past 256 registers, which ran 3.3 times slower. 32
+// for 8 or 16 lanes otherwise (two workgroups per CU), 16 for 4 lanes per row.
 int scan_stage_tokens(const ScanArgs &a, int L) {
+  if (scan_threads(a, L) == 512) return 64;
   if (L == 16 && a.bf16 && (a.mode == kPrefill || a.chunk >= 64)) {
     const int64_t rows = (int64_t)a.num_seqs * a.num_v_heads * a.d_v;
     return rows / 4 <= device_simds() ? 64 : 32;
@@ -214,11 +229,11 @@ gdn_status_t scan_common(const char *fn, const gdn_shape_t *sh, const uint8_t *i
 }
 
 gdn_status_t run_scan(const char *fn, ScanArgs &args, void *stream) {
-  const int L = scan_lanes(args);
-  if (scan_grid(args, L) > kMaxInt32)
+  const int L = scan_lanes(args), threads = scan_threads(args, L);
+  if (scan_grid(args, L, threads) > kMaxInt32)
     return fail(GDN_E_SHAPE, std::string(fn) + ": num_seqs * num_v_heads * row blocks too large");
-  const hipError_t e =
-      launch_scan(args, L, scan_stage_tokens(args, L), static_cast<hipStream_t>(stream));
+  const hipError_t e = launch_scan(args, L, scan_stage_tokens(args, L), threads,
+                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(GDN_E_DEVICE, std::string(fn) + ": launch failed: " + hipGetErrorString(e));
   return ok();

@@ -41,10 +41,16 @@ using namespace io;
 
 // At 4 lanes per row the scan is issue-bound with many waves to run: it asks for three
 // waves per SIMD (at most 168 registers), which hides each wave's dependency chains.
-template <int D, int L, int TS, bool BF16, int MODE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(L == 4 ? 3 : 1)))
+// NT threads per workgroup: 256, or 512 for two waves per SIMD from one workgroup per CU
+// (64-token stages staged once for 32 rows). With 512 the o buffer has one stage, not two,
+// to fit the LDS, and each wave stores only its own rows' o from it, so that a wave's next
+// stage cannot overwrite what another wave is still reading.
+template <int D, int L, int TS, bool BF16, int MODE, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(L == 4 ? 3 : 1)))
 void cpr_scan_kernel(const ScanArgs p) {
   static_assert(TS % 16 == 0, "a stage holds whole 16-token groups");
+  constexpr int kThreads = NT;
+  constexpr int SO_BUFS = NT == 512 ? 1 : 2;
   constexpr int ROWS = kThreads / L;
   constexpr int M = D / L;
   // Chunk boundaries inside a full stage (after its tokens 15, 31, ...) are kept from the
@@ -63,12 +69,17 @@ void cpr_scan_kernel(const ScanArgs p) {
   constexpr int KQ_FLOATS = TS * D;
   constexpr int POOL = 2 * KQ_FLOATS;
   // One block with the small arrays first, so that they sit below 64 KiB and every read of
-  // them takes an immediate offset from a fixed base.
+  // them takes an immediate offset from a fixed base. The sequence lengths are read only
+  // by the ranking, which ends with a barrier before the first deposit, so they share the
+  // v buffers.
+  static_assert(2 * V_ITEMS >= kMaxRankedSeqs, "the ranking fits in the v buffers");
   struct alignas(16) Lds {
     float sa[2][TS], sb[2][TS];
-    float sv[2][V_ITEMS];
-    float so[2][V_ITEMS];
-    int s_len[kMaxRankedSeqs];
+    union {
+      float sv[2][V_ITEMS];
+      int s_len[kMaxRankedSeqs];
+    };
+    float so[SO_BUFS][V_ITEMS];
     int s_pick;
     unsigned long long s_acc;
     alignas(16) float pool[2][POOL];
@@ -243,7 +254,17 @@ void cpr_scan_kernel(const ScanArgs p) {
     }
   };
   auto write_o = [&](int64_t t0, int nt, int buf) {
-    if (nt == TS) {  // full stage: scalar base plus the 32-bit offsets
+    if constexpr (SO_BUFS == 1) {
+      // this wave's own rows (64 / L of them) for every token of the stage
+      constexpr int RW = 64 / L;
+      const int wave = tid / 64, wl = tid % 64;
+#pragma unroll
+      for (int j = 0; j < TS * RW / 64; ++j) {
+        const int e = wl + 64 * j, tt = e / RW, r = wave * RW + e % RW;
+        if (tt < nt && r0 + r < dv)
+          p.o[(bos + t0 + tt) * vstride + (int64_t)h * dv + r0 + r] = so[0][tt * ROWS + r];
+      }
+    } else if (nt == TS) {  // full stage: scalar base plus the 32-bit offsets
       char *ob = reinterpret_cast<char *>(p.o + (bos + t0) * vstride);
       const int t = opaque_tid();
 #pragma unroll
@@ -251,15 +272,19 @@ void cpr_scan_kernel(const ScanArgs p) {
         if (FIXED ? o_ok[j] : o_store_ok(t, j))
           *reinterpret_cast<float *>(ob + (FIXED ? o_off[j] : o_offset(t, j))) =
               so[buf][tid + j * kThreads];
-      return;
-    }
+    } else {
 #pragma unroll
-    for (int j = 0; j < V_PER; ++j) {
-      const int e = tid + j * kThreads;
-      const int tt = e / ROWS, r = e % ROWS;
-      if ((V_ITEMS % kThreads == 0 || e < V_ITEMS) && tt < nt && r0 + r < dv)
-        p.o[(bos + t0 + tt) * vstride + (int64_t)h * dv + r0 + r] = so[buf][e];
+      for (int j = 0; j < V_PER; ++j) {
+        const int e = tid + j * kThreads;
+        const int tt = e / ROWS, r = e % ROWS;
+        if ((V_ITEMS % kThreads == 0 || e < V_ITEMS) && tt < nt && r0 + r < dv)
+          p.o[(bos + t0 + tt) * vstride + (int64_t)h * dv + r0 + r] = so[buf][e];
+      }
     }
+  };
+  // o of token tt of the stage, into the coalescing buffer
+  auto store_o = [&](int buf, int tt, float value) {
+    so[SO_BUFS == 1 ? 0 : buf][tt * ROWS + row] = value;
   };
   // One token of a stage, in row_token's order of operations (decay, key dot, delta,
   // update, readout); q is read from LDS only once k is no longer needed, so the two are
@@ -272,7 +297,7 @@ void cpr_scan_kernel(const ScanArgs p) {
     const float u = contract_dot<D, L>(x, kr);
     row_update<D, L>(s, row_delta(sb[buf][tt], sv[buf][tt * ROWS + row], u), kr, x);
     lds_slice<D, L>(&SQ(buf)[tt * D], lane, qr);
-    so[buf][tt * ROWS + row] = contract_dot<D, L>(s, qr);
+    store_o(buf, tt, contract_dot<D, L>(s, qr));
   };
 
   // A full stage, software-pipelined: the inputs of token t+2 are read from LDS while token
@@ -314,10 +339,10 @@ void cpr_scan_kernel(const ScanArgs p) {
           ys[1][e] = rk_[nxt][e];
         }
         contract_dots<D, L, 2>(xs, ys, r);
-        so[buf][tt * ROWS + row] = r[0];
+        store_o(buf, tt, r[0]);
         u = r[1];
       } else {
-        so[buf][tt * ROWS + row] = contract_dot<D, L>(s, rq_[cur]);
+        store_o(buf, tt, contract_dot<D, L>(s, rq_[cur]));
       }
     }
   };
@@ -428,28 +453,34 @@ __global__ __launch_bounds__(kThreads) void cpr_decode_kernel(const DecodeArgs p
 // ---------------------------------------------------------------------------- launchers
 
 template <typename Args>
-hipError_t launch(const void *fn, int64_t grid, Args args, hipStream_t stream) {
+hipError_t launch(const void *fn, int64_t grid, Args args, hipStream_t stream,
+                  int threads = kThreads) {
   if (grid <= 0) return hipSuccess;
   void *kargs[] = {&args};
-  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(threads), kargs, 0, stream);
 }
 
-template <int D, int L, int TS>
+template <int D, int L, int TS, int NT = kThreads>
 hipError_t scan_dl(const ScanArgs &a, hipStream_t st) {
-  const int64_t grid = scan_grid(a, L);
+  const int64_t grid = scan_grid(a, L, NT);
   const void *fn;
-  if constexpr (TS > 32) {  // bf16 inputs only; a trainer launch needs C >= TS
+  if constexpr (NT == 512) {  // bf16, d_v a multiple of 32; a trainer launch needs C >= TS
+    if (!a.bf16 || a.d_v % 32 != 0 || (a.mode == kTrainer && a.chunk < TS))
+      return hipErrorInvalidValue;
+    fn = a.mode == kTrainer ? (const void *)cpr_scan_kernel<D, L, TS, true, kTrainer, NT>
+                            : (const void *)cpr_scan_kernel<D, L, TS, true, kPrefill, NT>;
+  } else if constexpr (TS > 32) {  // bf16 inputs only; a trainer launch needs C >= TS
     if (!a.bf16 || (a.mode == kTrainer && a.chunk < TS)) return hipErrorInvalidValue;
-    fn = a.mode == kTrainer ? (const void *)cpr_scan_kernel<D, L, TS, true, kTrainer>
-                            : (const void *)cpr_scan_kernel<D, L, TS, true, kPrefill>;
+    fn = a.mode == kTrainer ? (const void *)cpr_scan_kernel<D, L, TS, true, kTrainer, NT>
+                            : (const void *)cpr_scan_kernel<D, L, TS, true, kPrefill, NT>;
   } else if (a.mode == kTrainer) {
-    fn = a.bf16 ? (const void *)cpr_scan_kernel<D, L, TS, true, kTrainer>
-                : (const void *)cpr_scan_kernel<D, L, TS, false, kTrainer>;
+    fn = a.bf16 ? (const void *)cpr_scan_kernel<D, L, TS, true, kTrainer, NT>
+                : (const void *)cpr_scan_kernel<D, L, TS, false, kTrainer, NT>;
   } else {
-    fn = a.bf16 ? (const void *)cpr_scan_kernel<D, L, TS, true, kPrefill>
-                : (const void *)cpr_scan_kernel<D, L, TS, false, kPrefill>;
+    fn = a.bf16 ? (const void *)cpr_scan_kernel<D, L, TS, true, kPrefill, NT>
+                : (const void *)cpr_scan_kernel<D, L, TS, false, kPrefill, NT>;
   }
-  return launch(fn, grid, a, st);
+  return launch(fn, grid, a, st, NT);
 }
 
 template <int D, int L>
@@ -460,7 +491,8 @@ hipError_t decode_dl(const DecodeArgs &a, hipStream_t st) {
 }
 
 template <int D>
-hipError_t scan_d(const ScanArgs &a, int L, int TS, hipStream_t st) {
+hipError_t scan_d(const ScanArgs &a, int L, int TS, int NT, hipStream_t st) {
+  if (NT == 512) return L == 16 && TS == 64 ? scan_dl<D, 16, 64, 512>(a, st) : hipErrorInvalidValue;
   if (L == 16 && TS == 64 && a.bf16) return scan_dl<D, 16, 64>(a, st);
   if (L == 16 && TS == 32) return scan_dl<D, 16, 32>(a, st);
   if (L == 8 && TS == 32) return scan_dl<D, 8, 32>(a, st);
@@ -480,8 +512,8 @@ hipError_t decode_d(const DecodeArgs &a, int L, hipStream_t st) {
 
 }  // namespace
 
-int64_t scan_grid(const ScanArgs &a, int L) {
-  const int64_t rows = kThreads / L;
+int64_t scan_grid(const ScanArgs &a, int L, int threads) {
+  const int64_t rows = threads / L;
   return (int64_t)a.num_seqs * a.num_v_heads * ((a.d_v + rows - 1) / rows);
 }
 
@@ -490,12 +522,12 @@ int64_t decode_grid(const DecodeArgs &a, int L) {
   return (int64_t)a.num_seqs * a.num_v_heads * ((a.d_v + rows - 1) / rows);
 }
 
-hipError_t launch_scan(const ScanArgs &a, int L, int TS, hipStream_t st) {
+hipError_t launch_scan(const ScanArgs &a, int L, int TS, int threads, hipStream_t st) {
   switch (a.d_k) {
-    case 16: return scan_d<16>(a, L, TS, st);
-    case 32: return scan_d<32>(a, L, TS, st);
-    case 64: return scan_d<64>(a, L, TS, st);
-    case 128: return scan_d<128>(a, L, TS, st);
+    case 16: return scan_d<16>(a, L, TS, threads, st);
+    case 32: return scan_d<32>(a, L, TS, threads, st);
+    case 64: return scan_d<64>(a, L, TS, threads, st);
+    case 128: return scan_d<128>(a, L, TS, threads, st);
     default: return hipErrorInvalidValue;
   }
 }
