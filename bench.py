@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -228,6 +229,13 @@ def hbm(bytes_, ms):
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def is_scan_kernel(name, mode):
+    """Whether a kernel name from a profile is a one-level scan of the case `mode` (0 trainer,
+    1 prefill): template arguments (d_k, lanes, stage tokens, bf16, case, threads)."""
+    return re.search(rf"cpr_scan_kernel<\d+, \d+, \d+, (true|false), {mode}, \d+>"
+                     r"\(gdn::ScanArgs\)$", name) is not None
+
+
 def traffic_for(name, launches_bytes_fn=None):
     """Measured HBM bytes per launch from a committed rocprofv3 counter summary, if it was
     taken on the current kernel sources; otherwise None."""
@@ -270,9 +278,8 @@ def write_traffic(fetch_csv, write_csv):
                 by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return {k: statistics.median(v) for k, v in by.items()}
 
-    def scan(mode, grid):  # one scan launch: the template's last argument is the case
-        return lambda name, g: ("cpr_scan_kernel<" in name and name.endswith(f", {mode}>(gdn::ScanArgs)")
-                                and g == grid)
+    def scan(mode, grid):  # one scan launch of the case at that many threads
+        return lambda name, g: is_scan_kernel(name, mode) and g == grid
 
     fr, wr = rows(fetch_csv, "FETCH_SIZE"), rows(write_csv, "WRITE_SIZE")
     cf, cw = copy_kib(fr), copy_kib(wr)

@@ -89,3 +89,14 @@ def test_alu_peak_is_the_published_fp32_vector_peak():
     assert abs(256 * 4 * 2.4e9 * 64 / 1e12 - bench.FP32_VECTOR_PEAK_TFLOPS) < 0.05
     r = bench.roofline_alu(157.3e12 * 1e-3, 2.0)  # half the peak
     assert r["peak"] == 157.3 and abs(r["frac"] - 0.5) < 1e-4 and r["bound"] == "alu"
+
+
+def test_scan_kernel_names_are_matched_by_case():
+    # the names rocprofv3 prints for the scan kernels (template: d_k, lanes per row, stage
+    # tokens, bf16, case, threads per workgroup)
+    trainer = "void gdn::(anonymous namespace)::cpr_scan_kernel<128, 16, 64, true, 0, 512>(gdn::ScanArgs)"
+    prefill = "void gdn::(anonymous namespace)::cpr_scan_kernel<128, 4, 16, true, 1, 256>(gdn::ScanArgs)"
+    assert bench.is_scan_kernel(trainer, 0) and not bench.is_scan_kernel(trainer, 1)
+    assert bench.is_scan_kernel(prefill, 1) and not bench.is_scan_kernel(prefill, 0)
+    assert not bench.is_scan_kernel(
+        "void gdn::(anonymous namespace)::cpr_decode_kernel<128, 16, true>(gdn::DecodeArgs)", 0)
