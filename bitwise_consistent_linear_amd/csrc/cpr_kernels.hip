@@ -2,15 +2,15 @@
 // engine_prefill) and the one-token decode step.
 //
 // Work decomposition: every state row (sequence n, value head h, row i) evolves on its own
-// (the gated delta rule updates S row by row: row i only sees v_i). A workgroup of 256
-// threads owns ROWS = 256/L consecutive rows of one (n, h); each row sits in the VGPRs of
-// L lanes (cpr_row.hpp). No MFMA: each token is a matrix-vector step on a d_k x d_v state
+// (the gated delta rule updates S row by row: row i only sees v_i). A workgroup of NT
+// threads (256; 512 for the two-waves-per-SIMD trainer shape) owns ROWS = NT/L consecutive
+// rows of one (n, h); each row sits in the VGPRs of L lanes (cpr_row.hpp). No MFMA: each token is a matrix-vector step on a d_k x d_v state
 // whose every element is touched four times, not a dense contraction.
 //
 // Scan: tokens are staged TS at a time - q and k of the (n, q/k head) in the order the
 // lanes read them, v of the workgroup's rows, a and b - into LDS as binary32 (bf16 widened
 // exactly) with coalesced loads; the token loop then runs from LDS and registers only. The
-// outputs o of a stage go back through LDS so that each token's ROWS values are stored
+// outputs o of a stage go back through LDS so that each token's rows are stored
 // contiguously. Chunk-boundary states (trainer) and the final state (prefill) are stored
 // straight from the registers, each lane its contiguous slice of the row.
 //
@@ -28,10 +28,11 @@
 namespace gdn {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // decode, and the scan unless the launcher picks 512
 // TS, the tokens staged in LDS at a time, is chosen by the launcher: 64 for a lone wave per
-// SIMD at 16 lanes per row with bf16 inputs (a trainer launch only when C >= 64), 32 for 8
-// or 16 lanes per row otherwise, 16 for 4 (where occupancy matters). Longer stages halve
+// SIMD at 16 lanes per row with bf16 inputs and in 512-thread workgroups (a trainer launch
+// only when C >= 64), 32 for 8 or 16 lanes per row otherwise, 16 for 4 (where occupancy
+// matters). Longer stages halve
 // the per-stage barrier and pipeline restart but take more LDS. Stages start at in-sequence
 // index 0 and every admitted C is a multiple of 16, so a chunk boundary falls on a token
 // 16 m - 1 of a stage.

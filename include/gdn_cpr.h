@@ -51,11 +51,15 @@
  * All functions are thread-safe.
  *
  * TUNING. How many lanes of a wavefront share one state row is chosen per call from the
- * number of rows: 16 when that gives at most one wavefront per SIMD, 8 when 8 lanes do, 4
- * otherwise (decode: 16; the backward's reverse pass over dL/dS: the widest that keeps at
- * most two wavefronts per SIMD). The environment variable GDN_CPR_LANES_PER_ROW (16, 8 or
- * 4) overrides the choice; the contract makes every admitted value give the same bits,
- * which the tests check.
+ * number of rows: 16 when that gives at most two wavefronts per SIMD, 8 when 8 lanes give
+ * at most one, 4 otherwise (decode: 16; the backward's reverse pass over dL/dS: the widest
+ * that keeps at most two wavefronts per SIMD). The environment variable
+ * GDN_CPR_LANES_PER_ROW (16, 8 or 4) overrides the choice. With two wavefronts per SIMD at
+ * 16 lanes, bf16 inputs and d_v a multiple of 32 a scan workgroup has 512 threads
+ * (GDN_CPR_SCAN_THREADS=256 keeps 256), and the backward picks its schedule by the number
+ * of (sequence, head, row block) units (GDN_CPR_BWD_SCHEDULE=sequences or chunks
+ * overrides). The contract makes every admitted choice give the same bits, which the
+ * tests check.
  */
 #ifndef GDN_CPR_H
 #define GDN_CPR_H

@@ -95,6 +95,24 @@ class schedule:
 SCHEDULES = ("chunks", "sequences")
 
 
+class scan_threads:
+    """Context manager: with "256", keep 256-thread scan workgroups where the library would
+    take 512 (two waves per SIMD at 16 lanes per row)."""
+
+    def __init__(self, n):
+        self.n = str(n)
+
+    def __enter__(self):
+        self.old = os.environ.get("GDN_CPR_SCAN_THREADS")
+        os.environ["GDN_CPR_SCAN_THREADS"] = self.n
+
+    def __exit__(self, *exc):
+        if self.old is None:
+            os.environ.pop("GDN_CPR_SCAN_THREADS", None)
+        else:
+            os.environ["GDN_CPR_SCAN_THREADS"] = self.old
+
+
 def decode_steps(dev_steps, state, chunk, s_range=None, resync=True):
     """Run decode steps; yields (step index, o, resync tensor or None)."""
     S = dev_steps["q"].shape[0]

@@ -16,8 +16,8 @@ import torch
 
 from bitwise_consistent_linear_amd import api
 from bitwise_consistent_linear_amd import workloads as W
-from gpu_util import (DEV, LANES, assert_bits, assert_dev_equal, decode_steps, lanes, log, up,
-                      up_steps, up_workload)
+from gpu_util import (DEV, LANES, assert_bits, assert_dev_equal, decode_steps, lanes, log,
+                      scan_threads, up, up_steps, up_workload)
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -236,6 +236,15 @@ def test_config_trainer_fwd():
             o2, cs2 = run_trainer(w, d)
         assert_dev_equal(o2, o, f"L={L} vs L=16 o")
         assert_dev_equal(cs2, cs, f"L={L} vs L=16 chunk states")
+    # this shape runs in 512-thread workgroups with 64-token stages; 256 threads and
+    # 32-token stages give the same bits
+    with scan_threads(256):
+        o3, cs3 = run_trainer(w, d)
+        po3, fs3 = run_prefill(w, d)
+    assert_dev_equal(o3, o, "256 vs 512 threads o")
+    assert_dev_equal(cs3, cs, "256 vs 512 threads chunk states")
+    assert_dev_equal(po3, po, "256 vs 512 threads prefill o")
+    assert_dev_equal(fs3, fs, "256 vs 512 threads final states")
     sampled_oracle(w, [(0, 0), (3, 15), (1, 6)], o, cs, fs)
 
 
