@@ -635,33 +635,35 @@ __device__ __forceinline__ float rb_tree(const float *base, int64_t stride, int 
   return v[0];
 }
 
+// One token per workgroup iteration (grid-stride over tokens): its Hk * d_k elements of dq
+// and dk and Hv pairs (da, db), indexed in 32 bits (d_k a power of two).
 template <int RBMAX>
 __global__ __launch_bounds__(kThreads) void cpr_bwd_combine_kernel(const BwdArgs p) {
   const int D = p.d_k, PW = 2 * D + 4, RB = p.row_blocks;  // partial rows padded to float4
   const int Hv = p.num_v_heads, Hk = p.num_qk_heads, G = Hv / Hk;
+  const int dshift = __builtin_ctz((unsigned)D), nqk = Hk << dshift;
   const int64_t T = p.total_tokens;
-  const int64_t nqk = T * Hk * D, nab = T * Hv;
-  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < nqk + nab;
-       idx += (int64_t)gridDim.x * kThreads) {
-    if (idx < nqk) {
-      const int64_t t = idx / ((int64_t)Hk * D);
-      const int hk = (int)((idx / D) % Hk), e = (int)(idx % D);
-      float aq = 0.0f, ak = 0.0f;
-      for (int g = 0; g < G; ++g) {
-        const float *base = p.partials + ((t * Hv + hk * G + g) * RB) * PW;
-        const float vq = rb_tree<RBMAX>(base + e, PW, RB);
-        const float vk = rb_tree<RBMAX>(base + D + e, PW, RB);
-        aq = g == 0 ? vq : aq + vq;
-        ak = g == 0 ? vk : ak + vk;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    const float *tok = p.partials + t * Hv * RB * PW;
+    for (int i = threadIdx.x; i < nqk + Hv; i += kThreads) {
+      if (i < nqk) {
+        const int hk = i >> dshift, e = i & (D - 1);
+        float aq = 0.0f, ak = 0.0f;
+        for (int g = 0; g < G; ++g) {
+          const float *base = tok + ((hk * G + g) * RB) * PW;
+          const float vq = rb_tree<RBMAX>(base + e, PW, RB);
+          const float vk = rb_tree<RBMAX>(base + D + e, PW, RB);
+          aq = g == 0 ? vq : aq + vq;
+          ak = g == 0 ? vk : ak + vk;
+        }
+        p.dq[(t * Hk + hk) * D + e] = aq;
+        p.dk[(t * Hk + hk) * D + e] = ak;
+      } else {
+        const int h = i - nqk;
+        const float *base = tok + (h * RB) * PW;
+        p.da[t * Hv + h] = rb_tree<RBMAX>(base + 2 * D, PW, RB);
+        p.db[t * Hv + h] = rb_tree<RBMAX>(base + 2 * D + 1, PW, RB);
       }
-      p.dq[(t * Hk + hk) * D + e] = aq;
-      p.dk[(t * Hk + hk) * D + e] = ak;
-    } else {
-      const int64_t r = idx - nqk, t = r / Hv;
-      const int h = (int)(r % Hv);
-      const float *base = p.partials + ((t * Hv + h) * RB) * PW;
-      p.da[t * Hv + h] = rb_tree<RBMAX>(base + 2 * D, PW, RB);
-      p.db[t * Hv + h] = rb_tree<RBMAX>(base + 2 * D + 1, PW, RB);
     }
   }
 }
@@ -789,8 +791,7 @@ hipError_t launch_backward(const BwdArgs &args, int L, bool seq, hipStream_t st)
   const int64_t cgrid = backward_chunk_grid(a, seq);
   if ((e = launch1(cf, cgrid, a, st, kChunkThreads)) != hipSuccess) return e;
   if (a.whole && (e = launch1(wf, cgrid, a, st, kChunkThreads)) != hipSuccess) return e;
-  const int64_t items = a.total_tokens * (a.num_qk_heads * (int64_t)a.d_k + a.num_v_heads);
-  const int64_t grid = std::min<int64_t>((items + kThreads - 1) / kThreads, 65536);
+  const int64_t grid = std::min<int64_t>(a.total_tokens, 65536);  // tokens, grid-strided
   const void *comb;
   if (a.row_blocks <= 1) comb = (const void *)cpr_bwd_combine_kernel<1>;
   else if (a.row_blocks <= 2) comb = (const void *)cpr_bwd_combine_kernel<2>;
