@@ -77,11 +77,13 @@ int scan_lanes(const ScanArgs &a) {
 // run at 16 lanes per row with bf16 inputs, d_v a multiple of 32 and, for the trainer,
 // C >= 64: one workgroup per CU then stages 64 tokens once for both waves of every SIMD,
 // where two 256-thread workgroups would each stage 32. 256 otherwise.
-// GDN_CPR_SCAN_THREADS=256 keeps 256 (the same bits either way).
+// GDN_CPR_SCAN_THREADS=256 keeps 256; =512 takes 512 wherever it is admitted, whatever the
+// number of rows (the same bits either way).
 int scan_threads(const ScanArgs &a, int L) {
   const char *env = std::getenv("GDN_CPR_SCAN_THREADS");
   if (env && std::strcmp(env, "256") == 0) return 256;
   if (L != 16 || !a.bf16 || a.d_v % 32 != 0 || (a.mode == kTrainer && a.chunk < 64)) return 256;
+  if (env && std::strcmp(env, "512") == 0) return 512;
   const int64_t rows = (int64_t)a.num_seqs * a.num_v_heads * a.d_v;
   const int64_t simds = device_simds();
   return rows / 4 > simds && rows / 4 <= 2 * simds ? 512 : 256;

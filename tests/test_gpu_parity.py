@@ -125,6 +125,34 @@ def test_small_cases_match_oracle(case):
         assert_bits(fs, rfs, f"{case[0]} L={L} prefill final")
 
 
+# 512-thread workgroups (32 rows, 64-token stages, a one-stage o buffer written back per
+# wave) forced on small bf16 batches whose d_v is a multiple of 32: ragged and empty
+# sequences, last stages of every length, GQA, C = 64 and 128, an initial state
+SMALL_512 = [
+    ("d128_c64_ragged_stages", [0, 1, 63, 64, 65, 200, 130], 2, 4, 128, 128, 64, True, True),
+    ("d64_dv96_c128_gqa", [129, 300, 7], 1, 4, 64, 96, 128, True, False),
+    ("d32_dv32_c64", [1, 127, 64], 1, 1, 32, 32, 64, True, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_512, ids=[c[0] for c in SMALL_512])
+def test_small_cases_512_threads_match_oracle(case):
+    w, s0 = small_workload(*case)
+    log(f"small, 512-thread scan: {case}")
+    ro, rcs, rfs = O.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=w.chunk,
+                          initial_state=s0, want_chunk_states=True, want_final_state=True)
+    d = up_workload(w)
+    ds0 = None if s0 is None else up(s0)
+    with lanes(16), scan_threads(512):
+        o, cs = run_trainer(w, d, ds0)
+        po, fs = run_prefill(w, d, ds0)
+        torch.cuda.synchronize()
+    assert_bits(o, ro, f"{case[0]} trainer o")
+    assert_bits(cs, rcs, f"{case[0]} trainer chunk states")
+    assert_bits(po, ro, f"{case[0]} prefill o")
+    assert_bits(fs, rfs, f"{case[0]} prefill final")
+
+
 @pytest.mark.parametrize("L", LANES)
 def test_decode_matches_oracle_and_trainer(L):
     # equal-length batch: prefix by prefill, then decode steps across several boundaries
