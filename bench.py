@@ -164,8 +164,9 @@ def verdict(checks):
 
 def valu_probe():
     """Vector-issue ceiling and shader clock of this GPU, from libgdn_probe.so: SIMD-cycles
-    per wave instruction for plain multiplies, fused multiply-adds and DPP adds with one, two
-    and four waves per SIMD, the fused multiply-add rate at two waves per SIMD, the latency
+    per wave instruction for plain multiplies, fused multiply-adds, DPP adds and a single
+    dependent chain of fused multiply-adds per lane with one, two and four waves per SIMD,
+    the fused multiply-add rate at two waves per SIMD, the latency
     of a dependent fused multiply-add and of a dependent DPP add level (shader cycles per step
     of one chain per lane, one wave per SIMD), and the shader clock (s_memtime against the
     100 MHz s_memrealtime)."""
@@ -183,7 +184,8 @@ def valu_probe():
     out = {"unit": "SIMD-cycles per wave instruction at the measured clock"}
     clocks = []
     fma2 = None
-    for form, name in ((0, "v_mul_f32"), (1, "v_fmac_f32"), (2, "v_add_f32_dpp")):
+    for form, name in ((0, "v_mul_f32"), (1, "v_fmac_f32"), (2, "v_add_f32_dpp"),
+                       (3, "v_fmac_f32_one_dependent_chain")):
         row = {}
         for wps in (1, 2, 4):
             grid = 256 * wps
