@@ -13,10 +13,15 @@
 //
 // Workgroup: 8 waves, a 128 x 128 tile of Y; wave (wm, wn) owns rows 64 wm .. 64 wm + 63 and
 // columns 32 wn .. 32 wn + 31 as two 32 x 32 blocks that share the B operand (two
-// independent accumulator chains); two waves per SIMD. K is staged 32 at a time into LDS as
-// binary32, double-buffered, the next stage's global loads in registers while the current
-// one computes: W k-major; X row-major with each row's even and odd k apart, so one 16-byte
-// read gives a lane its A operands for four steps.
+// independent accumulator chains); two waves per SIMD. K is staged KS at a time into LDS as
+// binary32, double-buffered, the next stage's global loads held in registers as loaded (bf16
+// bits or binary32) while the current one computes: W k-major; X row-major with each row's
+// even and odd k apart, so one 16-byte read gives a lane its A operands for four steps.
+// KS = 64 for bf16 X and W when a leaf is whole 64-k stages and N is a multiple of 128 (one
+// workgroup barrier per 64 k; 141 KiB of LDS), 32 otherwise. KS changes which instructions wait for which, never an
+// operation or its operands, so both give the same bits.
+
+#include <type_traits>
 
 #include "internal.h"
 
@@ -26,18 +31,68 @@ namespace {
 using f32x16 = float __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = 8, kThreads = 64 * kWaves;
-constexpr int TM = 128, TN = 128, KS = 32;     // workgroup tile, k per stage
-constexpr int QS = KS / 2 + 4, WS = TN + 4;    // LDS row strides (conflict-free reads)
+constexpr int TM = 128, TN = 128;  // workgroup tile
 constexpr int kLeaves = 16;
-constexpr int XPT = TM * KS / kThreads;        // staged X values per thread (8)
-constexpr int WPT = KS * TN / kThreads;        // staged W values per thread (8)
-static_assert(XPT == 8 && WPT == 8, "staging assumes 8 values per thread");
 
-__device__ __forceinline__ float widen_bf16(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ uint32_t comp(const uint4 &v, int c) {
+  return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ float comp(const float4 &v, int c) {
+  return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+}
 
-template <bool XBF16, bool WBF16>
+// V consecutive inputs of one row, kept as loaded (bf16 bits or binary32) until they are
+// written to LDS; get(e) widens element e exactly (e a compile-time index).
+template <bool BF16, int V>
+struct Run {
+  static constexpr int NV = BF16 ? V / 8 : V / 4;
+  using vec = std::conditional_t<BF16, uint4, float4>;
+  vec r[NV];
+  // elements [idx, idx + V) of base; the run is 16-byte aligned
+  __device__ __forceinline__ void load(const void *base, int64_t idx) {
+    const vec *src = BF16 ? reinterpret_cast<const vec *>(static_cast<const uint16_t *>(base) + idx)
+                          : reinterpret_cast<const vec *>(static_cast<const float *>(base) + idx);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) r[i] = src[i];
+  }
+  // element e from base[row + min(c0 + e, n - 1)]: columns past n repeat the last one
+  __device__ __forceinline__ void load_clamped(const void *base, int64_t row, int64_t c0,
+                                               int64_t n) {
+    auto col = [&](int e) { return row + (c0 + e < n ? c0 + e : n - 1); };
+    if constexpr (BF16) {
+      const uint16_t *b = static_cast<const uint16_t *>(base);
+      uint32_t w[V / 2];
+#pragma unroll
+      for (int e = 0; e < V / 2; ++e)
+        w[e] = (uint32_t)b[col(2 * e)] | ((uint32_t)b[col(2 * e + 1)] << 16);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) r[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+    } else {
+      const float *b = static_cast<const float *>(base);
+      float f[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) f[e] = b[col(e)];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) r[i] = make_float4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
+    }
+  }
+  __device__ __forceinline__ float get(int e) const {
+    if constexpr (BF16) {
+      const uint32_t w = comp(r[e / 8], (e % 8) / 2);
+      return __uint_as_float(e % 2 == 0 ? w << 16 : w & 0xFFFF0000u);
+    } else {
+      return comp(r[e / 4], e % 4);
+    }
+  }
+};
+
+template <bool XBF16, bool WBF16, int KS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void linear_leaf_kernel(const LinearArgs p) {
+  constexpr int QS = KS / 2 + 4, WS = TN + 4;  // LDS row strides (conflict-free reads)
+  constexpr int XPT = TM * KS / kThreads;      // staged X values per thread (8 or 16)
+  constexpr int WPT = KS * TN / kThreads;      // staged W values per thread (8 or 16)
+  static_assert((KS == 32 || KS == 64) && XPT % 8 == 0 && WPT % 8 == 0, "staging shape");
   __shared__ __align__(16) float sx[2][2][TM][QS];  // sx[buf][k % 2][row][k / 2]
   __shared__ __align__(16) float sw[2][KS][WS];      // sw[buf][k][col]
 
@@ -49,74 +104,43 @@ void linear_leaf_kernel(const LinearArgs p) {
   const int64_t tile_m = blockIdx.x / tiles_n, tile_n = blockIdx.x % tiles_n;
   const int64_t m0 = tile_m * TM, n0 = tile_n * TN;
 
-  // staging: X tile [128 rows x 32 k]: one row, 8 consecutive k per thread;
-  //          W tile [32 k x 128 cols]: one k, 8 consecutive columns per thread
-  const int xr = tid / 4, xk = (tid % 4) * 8;
-  const int wk = tid / 16, wc = (tid % 16) * 8;
+  // staging: X tile [128 rows x KS k]: one row, XPT consecutive k per thread;
+  //          W tile [KS k x 128 cols]: one k, WPT consecutive columns per thread
+  const int xr = tid / (KS / XPT), xk = (tid % (KS / XPT)) * XPT;
+  const int wk = tid / (TN / WPT), wc = (tid % (TN / WPT)) * WPT;
   const int64_t xrow = m0 + xr < M ? m0 + xr : M - 1;  // rows past M repeat the last row
   const bool w_vec = N % (WBF16 ? 8 : 4) == 0;           // every W row 16-byte aligned
-  float xv[XPT], wv[WPT];
+  Run<XBF16, XPT> xv;
+  Run<WBF16, WPT> wv;
   auto fetch = [&](int k0) {
-    const int64_t xo = xrow * K + k0 + xk;
-    if constexpr (XBF16) {
-      const uint4 r = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.x) + xo);
-      const uint32_t u[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xv[2 * e] = widen_bf16(u[e] & 0xFFFFu);
-        xv[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
-      }
-    } else {
-      const float4 a = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.x) + xo);
-      const float4 b = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.x) + xo + 4);
-      xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
-      xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
-    }
+    xv.load(p.x, xrow * K + k0 + xk);
     const int64_t wrow = (int64_t)(k0 + wk) * N;
-    if (w_vec && n0 + wc + WPT <= N) {  // all columns in range, rows 16-byte aligned
-      if constexpr (WBF16) {
-        const uint4 r = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.w) +
-                                                         wrow + n0 + wc);
-        const uint32_t u[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wv[2 * e] = widen_bf16(u[e] & 0xFFFFu);
-          wv[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
-        }
-      } else {
-        const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(p.w) +
-                                                             wrow + n0 + wc);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float4 r = src[e];
-          wv[4 * e] = r.x; wv[4 * e + 1] = r.y; wv[4 * e + 2] = r.z; wv[4 * e + 3] = r.w;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < WPT; ++e) {  // columns past N repeat the last column
-        const int64_t c = n0 + wc + e < N ? n0 + wc + e : N - 1;
-        if constexpr (WBF16)
-          wv[e] = widen_bf16(static_cast<const uint16_t *>(p.w)[wrow + c]);
-        else
-          wv[e] = static_cast<const float *>(p.w)[wrow + c];
-      }
-    }
+    if constexpr (KS == 64)  // launched only for N a multiple of the tile: every column in range
+      wv.load(p.w, wrow + n0 + wc);
+    else if (w_vec && n0 + wc + WPT <= N)  // all columns in range, rows 16-byte aligned
+      wv.load(p.w, wrow + n0 + wc);
+    else
+      wv.load_clamped(p.w, wrow, n0 + wc, N);
   };
   auto deposit = [&](int buf) {
     // k = xk + e: even k to half 0, odd k to half 1, at position k / 2
-    *reinterpret_cast<float4 *>(&sx[buf][0][xr][xk / 2]) = make_float4(xv[0], xv[2], xv[4], xv[6]);
-    *reinterpret_cast<float4 *>(&sx[buf][1][xr][xk / 2]) = make_float4(xv[1], xv[3], xv[5], xv[7]);
+#pragma unroll
+    for (int h = 0; h < XPT / 8; ++h) {
+      *reinterpret_cast<float4 *>(&sx[buf][0][xr][xk / 2 + 4 * h]) =
+          make_float4(xv.get(8 * h), xv.get(8 * h + 2), xv.get(8 * h + 4), xv.get(8 * h + 6));
+      *reinterpret_cast<float4 *>(&sx[buf][1][xr][xk / 2 + 4 * h]) =
+          make_float4(xv.get(8 * h + 1), xv.get(8 * h + 3), xv.get(8 * h + 5), xv.get(8 * h + 7));
+    }
 #pragma unroll
     for (int e = 0; e < WPT; e += 4)
       *reinterpret_cast<float4 *>(&sw[buf][wk][wc + e]) =
-          make_float4(wv[e], wv[e + 1], wv[e + 2], wv[e + 3]);
+          make_float4(wv.get(e), wv.get(e + 1), wv.get(e + 2), wv.get(e + 3));
   };
 
   // per lane: A operands for both blocks (rows 64 wm + l%32 and 32 more, k = 2q + l/32), the
   // shared B operand (column 32 wn + l%32)
   const int arow = 64 * wm + l % 32, bcol = 32 * wn + l % 32, kl = l / 32;
-  const int stages_per_leaf = K / (KS * kLeaves);  // K % 512 == 0: a leaf is whole stages
+  const int stages_per_leaf = K / (KS * kLeaves);  // KS * 16 divides K: a leaf is whole stages
   f32x16 acc0, acc1;              // the current leaf, blocks 0 and 1
   f32x16 t0[4], t1[4];            // pending subtrees: slot j holds a sum of 2^j leaves
   int leaf = 0;
@@ -185,8 +209,8 @@ void linear_leaf_kernel(const LinearArgs p) {
 
 }  // namespace
 
-bool linear_k_admitted(int64_t k) {  // leaves of whole stages: K a multiple of 16 * 32
-  return k >= KS * kLeaves && k <= (1 << 24) && k % (KS * kLeaves) == 0;
+bool linear_k_admitted(int64_t k) {  // leaves of whole 32-k stages: K a multiple of 16 * 32
+  return k >= 32 * kLeaves && k <= (1 << 24) && k % (32 * kLeaves) == 0;
 }
 
 int64_t linear_grid(const LinearArgs &a) { return ((a.m + TM - 1) / TM) * ((a.n + TN - 1) / TN); }
@@ -194,10 +218,14 @@ int64_t linear_grid(const LinearArgs &a) { return ((a.m + TM - 1) / TM) * ((a.n 
 hipError_t launch_linear(const LinearArgs &a, hipStream_t stream) {
   const int64_t grid = linear_grid(a);
   if (grid <= 0) return hipSuccess;
-  const void *fn = a.x_bf16 ? (a.w_bf16 ? (const void *)linear_leaf_kernel<true, true>
-                                        : (const void *)linear_leaf_kernel<true, false>)
-                            : (a.w_bf16 ? (const void *)linear_leaf_kernel<false, true>
-                                        : (const void *)linear_leaf_kernel<false, false>);
+  // 64-k stages for bf16 inputs whose leaves are whole 64-k stages (K a multiple of 1024) and
+  // whose tiles are all whole in N (that kernel has no path for columns past N)
+  const bool deep = a.x_bf16 && a.w_bf16 && a.k % (64 * kLeaves) == 0 && a.n % TN == 0;
+  const void *fn = deep       ? (const void *)linear_leaf_kernel<true, true, 64>
+                   : a.x_bf16 ? (a.w_bf16 ? (const void *)linear_leaf_kernel<true, true, 32>
+                                          : (const void *)linear_leaf_kernel<true, false, 32>)
+                              : (a.w_bf16 ? (const void *)linear_leaf_kernel<false, true, 32>
+                                          : (const void *)linear_leaf_kernel<false, false, 32>);
   LinearArgs args = a;
   void *kargs[] = {&args};
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kThreads), kargs, 0, stream);

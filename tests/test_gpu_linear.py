@@ -3,7 +3,8 @@ bit for bit, and its batch invariance.
 
 Small products cover ragged m and n (tiles that end part-way in both directions), n that
 does and does not allow vector loads of W, every dtype mix, k from 512 to 4096 (leaves of
-1 to 8 stages), signed zeros and denormals. The bench-size product (16384 x 4096 x 4096,
+1 to 8 stages), both stage depths (64-k stages for bf16 inputs with k a multiple of 1024
+and n of 128, 32-k stages otherwise), signed zeros and denormals. The bench-size product (16384 x 4096 x 4096,
 bf16) is compared with the oracle on sampled rows, and rows must not change with m.
 """
 
@@ -34,6 +35,12 @@ SMALL = [
     (65, 129, 512, False, True, 5),
     (3, 8, 4096, True, True, 6),
     (200, 64, 2048, False, False, 7),
+    # bf16 inputs with K a multiple of 1024 and N of 128 take 64-k stages: ragged M, several
+    # column tiles; the neighbours that do not (K = 1536, N = 200) take 32-k stages
+    (70, 256, 2048, True, True, 8),
+    (129, 384, 1024, True, True, 9),
+    (40, 128, 1536, True, True, 10),
+    (17, 200, 1024, True, True, 11),
 ]
 
 
@@ -76,6 +83,21 @@ def test_linear_batch_invariance():
         assert_dev_equal(part, full[:M], f"M={M} rows vs M=1000")
     torch.cuda.synchronize()
     assert_bits(full, O.linear(x, w), "M=1000 vs oracle")
+
+
+def test_linear_batch_invariance_64k_stages():
+    """The same at a shape that takes 64-k stages (bf16, K = 2048, N = 256); the oracle
+    checks that its bits are the 32-k stage kernel's too."""
+    N, K = 256, 2048
+    x, w = W.make_linear(300, N, K, True, 22)
+    log("linear: batch invariance over M in {1, 129, 300} with 64-k stages")
+    dw = up(w)
+    full = api.linear_fwd(up(x), dw)
+    for M in (1, 129):
+        part = api.linear_fwd(up(x[:M]), dw)
+        assert_dev_equal(part, full[:M], f"M={M} rows vs M=300")
+    torch.cuda.synchronize()
+    assert_bits(full, O.linear(x, w), "M=300 vs oracle")
 
 
 def test_linear_bench_size_sampled_rows():

@@ -36,7 +36,7 @@ def test_all_kernels_present(asm):
     # for shorter chunks, the branch-free loops for shorter chunks)
     assert sum("cpr_bwd_chunk_kernel" in n for n in names) == 4 * 2 * 2 * 3
     assert sum("cpr_bwd_combine_kernel" in n for n in names) == 6
-    assert sum("linear_leaf_kernel" in n for n in names) == 4
+    assert sum("linear_leaf_kernel" in n for n in names) == 4 + 1  # dtypes x 32-k, bf16 64-k
     assert sum("cpr2_plan_kernel" in n for n in names) == 1
     assert sum("cpr2_rows_kernel" in n for n in names) == 3 * 2 * 3  # d_k, dtype, variant
     assert sum("cpr2_boundary_kernel" in n for n in names) == 3 * 2  # d_k, prefetch
