@@ -46,6 +46,7 @@ KERNEL_SOURCES = {  # sources whose hash a traffic summary must match to be used
     "cpr_decode_engine_decode": ["cpr_kernels.hip", "cpr_row.hpp", "cpr_io.hpp"],
     "cpr_bwd_trainer": ["cpr_backward.hip", "cpr_row.hpp", "cpr_io.hpp"],
     "cpr2_two_level_trainer": ["cpr2.hip", "cpr_row.hpp", "cpr_io.hpp"],
+    "linear_leaf_16384x4096x4096": ["linear.hip"],
 }
 PMC_COMMAND = ("rocprofv3 --pmc {counter} --output-format csv -d <dir> -o {name} -- python3 "
                "bench.py --cases traffic --no-cpu-baseline --steps 3 --warmup 1 --copy-probe")
@@ -253,8 +254,8 @@ def traffic_for(name, launches_bytes_fn=None):
 
 def write_traffic(fetch_csv, write_csv):
     """From two rocprofv3 --pmc runs of `bench.py --cases traffic --copy-probe` (FETCH_SIZE,
-    then WRITE_SIZE; KiB per dispatch), write profiles/cpr_scan_trainer_fwd_traffic.json,
-    profiles/cpr_bwd_trainer_traffic.json and profiles/cpr2_two_level_trainer_traffic.json:
+    then WRITE_SIZE; KiB per dispatch), write profiles/<name>_traffic.json for every one-level
+    scan case, the decode step, the backward, the two-level trainer and the linear region:
     HBM bytes per launch (per call for the multi-kernel ones), each counter scaled by what
     it reads for the 256 MiB calibration copy (read once, written once)."""
     import csv
@@ -322,6 +323,10 @@ def write_traffic(fetch_csv, write_csv):
         ("cpr2_two_level_trainer", lambda name, g: "cpr2_" in name,
          "two-level trainer_fwd on the trainer_fwd workload (every kernel of one call)",
          cpr2_bytes(w)),
+        ("linear_leaf_16384x4096x4096",
+         lambda name, g: "linear_leaf_kernel<" in name and g == LINEAR_GRID_THREADS,
+         "linear region: Y[16384, 4096] = X[16384, 4096] W[4096, 4096], bf16 X and W, "
+         "binary32 Y", linear_bytes(16384, 4096, 4096)),
     ]
     for name, match, workload, alg in targets:
         kf, kw = per_kernel(fr, match), per_kernel(wr, match)
@@ -493,6 +498,15 @@ def bench_trainer_bwd(steps, warmup, fwd_kernel_ms, verify=True):
             "hbm": hbm(bwd_bytes(w), ms), "parity": par}
 
 
+LINEAR_GRID_THREADS = (16384 // 128) * (4096 // 128) * 512  # the bench product's launch
+
+
+def linear_bytes(M, N, K):
+    """Algorithmic bytes of one linear-region call: bf16 X and W read once, binary32 Y
+    written once."""
+    return M * K * 2 + K * N * 2 + M * N * 4
+
+
 def bench_linear(steps, warmup, M=16384, N=4096, K=4096):
     """gdn_linear_fwd: Y = X W with every output the contract dot, on the matrix cores."""
     import torch
@@ -505,7 +519,7 @@ def bench_linear(steps, warmup, M=16384, N=4096, K=4096):
     wall, per = timed(lambda: api.linear_fwd(dx, dw, y=y), steps, warmup)
     ms = sum(per) / len(per)
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-    nbytes = M * K * 2 + K * N * 2 + M * N * 4
+    nbytes = linear_bytes(M, N, K)
     # parity, after the timed region: batch invariance - rows computed in a batch of 65
     # equal the same rows of the full product
     part = api.linear_fwd(dx[:65].contiguous(), dw)
@@ -519,7 +533,8 @@ def bench_linear(steps, warmup, M=16384, N=4096, K=4096):
             "steps": steps,
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                          "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4)},
+                         "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4),
+                         "traffic": traffic_for(f"linear_leaf_{M}x{N}x{K}")},
             "hbm": hbm(nbytes, ms), "parity": par}
 
 
@@ -985,8 +1000,8 @@ def main():
                          "/ linear / cpr2: trainer_fwd and the backward / the engine_prefill call "
                          "/ the engine_decode steps / the long-context calls / the linear region "
                          "/ the two-level reading (for profiling); traffic: a few calls of every "
-                         "one-level scan, the decode step, the backward and the two-level "
-                         "trainer (for the counter runs)")
+                         "one-level scan, the decode step, the backward, the two-level "
+                         "trainer and the linear region (for the counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (untimed), the known-size "
@@ -1078,8 +1093,10 @@ def main():
             "engine_prefill": lambda: bench_prefill(2, 1),
             "engine_decode": lambda: bench_decode(verify=False, nsteps=16),
             "long_context": lambda: bench_long(1, scans_only=True),
+            "linear": lambda: bench_linear(2, 1),
         })
-        names = ["trainer_bwd", "two_level", "engine_prefill", "engine_decode", "long_context"]
+        names = ["trainer_bwd", "two_level", "engine_prefill", "engine_decode", "long_context",
+                 "linear"]
     else:
         names = chosen[args.cases]
     if names:
