@@ -12,8 +12,9 @@
 //               states recomputed from the trainer's chunk state (checkpoints every 8 tokens
 //               in registers, each token's v_i - u in LDS), sh re-run from the boundary value the state pass stored (the
 //               same operations, so the same bits), and every token's shares summed over
-//               the block's rows: pairwise in natural row order, within the wave through
-//               LDS, then across the 4 waves; one partial per (token, head, row block);
+//               the block's rows: pairwise in natural row order, within the wave by row
+//               swaps, then across the 8 waves through LDS; one partial per (token, head,
+//               row block);
 //   4. combine: the pairwise tree continued over the row blocks, then the value heads of a
 //               q/k group left to right.
 // A pair of the row tree whose second half holds no row (d_v not a power of two) passes its
@@ -301,10 +302,16 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
   __shared__ __align__(16) float sk[2][SB * D];
   __shared__ __align__(16) float sq[2][SB * D];
   __shared__ float sv[2][V_ITEMS], sg[2][V_ITEMS], sa[2][SB], sb[2][SB];
-  __shared__ __align__(16) float swave[SB][WAVES][PWP];  // wave sums of a sub-block's tokens
-  __shared__ float sdif[kMaxSub * SB][ROWS];             // v_i - u of every token of the chunk
-  __shared__ float sdv[SEQ ? SB : 1][ROWS];               // dv of a sub-block (SEQ only)
-  __shared__ int s_len[SEQ ? kMaxRankedSeqs : 1];
+  // wave sums of a sub-block's tokens, two buffers: sub-block sbi uses swave[sbi & 1], so the
+  // next sub-block's tokens can be summed while other waves still read these (one barrier
+  // per sub-block). The sequence ranking's lengths, used once before the first chunk, share
+  // the second buffer.
+  __shared__ __align__(16) float swave[2][SB][WAVES][PWP];
+  static_assert(kMaxRankedSeqs <= SB * WAVES * PWP, "ranking lengths fit one wave-sum buffer");
+  int *const s_len = reinterpret_cast<int *>(&swave[1][0][0][0]);
+  // v_i - u of every token of the chunk; once the reverse pass has rebuilt a sub-block's
+  // states from its entries, the sequence schedule keeps that sub-block's dv_i there
+  __shared__ float sdif[kMaxSub * SB][ROWS];
   __shared__ int s_pick;
 
   const int Hv = p.num_v_heads, Hk = p.num_qk_heads, dv = p.d_v, RB = p.row_blocks;
@@ -536,8 +543,8 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
 #pragma unroll
             for (int e = 0; e < M; ++e) pq[e] = g * st[j + 1][e];
             const float dv_i = row_bwd_delta<D, L>(sh, kr, b, xh, dh);
-            if constexpr (SEQ) {
-              if (WHOLE || lane == 0) sdv[j][row] = dv_i;
+            if constexpr (SEQ) {  // this row's entry was read by the rebuild above (this wave)
+              if (WHOLE || lane == 0) sdif[sbi * SB + j][row] = dv_i;
             }
             const float pb = dh * dif[j];
             const float uh = -dv_i;
@@ -554,7 +561,7 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
               rows4_sum<M, true>(pq, pk, pa, pb, c1, c2, z, y);
             else
               rows4_sum<M, false>(pq, pk, pa, pb, c1, c2, z, y);
-            float *dst = &swave[j][wave][0];
+            float *dst = &swave[sbi & 1][j][wave][0];
             if constexpr (H == 4) {
               *reinterpret_cast<float4 *>(dst + zofs) = make_float4(z[0], z[1], z[2], z[3]);
             } else if constexpr (H == 2) {
@@ -565,6 +572,9 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
             if (ywrite) dst[yofs] = y;
           }
         }
+        // the previous sub-block's inputs: buffer buf ^ 1 was last read by sub-block sbi + 1,
+        // before the barrier that ended it; its readers come after the barrier below
+        if (sbi > 0) deposit(buf ^ 1);
         __syncthreads();
         // across the waves (wave w holds rows r0 + 4w .. r0 + 4w + 3), pairwise, pass-through;
         // four consecutive shares per thread (one 16-byte read per wave, one 16-byte store).
@@ -575,7 +585,8 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
           const int j = e / G4, f = 4 * (e % G4);
           float4 w[WAVES];
 #pragma unroll
-          for (int x = 0; x < WAVES; ++x) w[x] = *reinterpret_cast<const float4 *>(&swave[j][x][f]);
+          for (int x = 0; x < WAVES; ++x)
+            w[x] = *reinterpret_cast<const float4 *>(&swave[sbi & 1][j][x][f]);
 #pragma unroll
           for (int st = 1; st < WAVES; st *= 2)
 #pragma unroll
@@ -593,11 +604,12 @@ void cpr_bwd_chunk_kernel(const BwdArgs p) {
           for (int e = tid; e < nt * ROWS; e += kThreads) {
             const int j = e / ROWS, r = e % ROWS;
             if (r0 + r < dv)
-              p.dv[(bos + c0 + sbi * SB + j) * vstride + (int64_t)h * dv + r0 + r] = sdv[j][r];
+              p.dv[(bos + c0 + sbi * SB + j) * vstride + (int64_t)h * dv + r0 + r] =
+                  sdif[sbi * SB + j][r];
           }
         }
-        if (sbi > 0) deposit(buf ^ 1);  // its last reader finished before the barrier above
-        __syncthreads();
+        // No barrier here: the next sub-block writes the other wave-sum buffer and its own
+        // sdif rows, and reads the input buffer deposited before the barrier above.
       }
     });
    }  // segments
