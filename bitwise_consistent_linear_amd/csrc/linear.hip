@@ -18,7 +18,8 @@
 // bits or binary32) while the current one computes: W k-major; X row-major with each row's
 // even and odd k apart, so one 16-byte read gives a lane its A operands for four steps.
 // KS = 64 for bf16 X and W when a leaf is whole 64-k stages and N is a multiple of 128 (one
-// workgroup barrier per 64 k; 141 KiB of LDS), 32 otherwise. KS changes which instructions wait for which, never an
+// workgroup barrier per 64 k; 141 KiB of LDS; W's columns interleaved over the lanes so that
+// its deposit is free of LDS bank conflicts), 32 otherwise. KS changes which instructions wait for which, never an
 // operation or its operands, so both give the same bits.
 
 #include <type_traits>
@@ -111,16 +112,26 @@ void linear_leaf_kernel(const LinearArgs p) {
   const int64_t xrow = m0 + xr < M ? m0 + xr : M - 1;  // rows past M repeat the last row
   const bool w_vec = N % (WBF16 ? 8 : 4) == 0;           // every W row 16-byte aligned
   Run<XBF16, XPT> xv;
-  Run<WBF16, WPT> wv;
+  Run<WBF16, WPT> wv;  // KS = 32
+  // KS = 64 (bf16 W): lane c of a W row (eight lanes per row) holds columns 32 j + 4 c .. + 3,
+  // j = 0 .. 3, so that each of the four 16-byte LDS writes of the deposit puts the row's
+  // eight lanes in eight different groups of four banks (consecutive 16-column runs per
+  // lane put them in two, a four-way conflict)
+  uint2 wq[4];
+  const int wcl = tid % (TN / WPT);
   auto fetch = [&](int k0) {
     xv.load(p.x, xrow * K + k0 + xk);
     const int64_t wrow = (int64_t)(k0 + wk) * N;
-    if constexpr (KS == 64)  // launched only for N a multiple of the tile: every column in range
+    if constexpr (KS == 64) {  // launched only for N a multiple of the tile: every column in range
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        wq[j] = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.w) + wrow + n0 +
+                                                 32 * j + 4 * wcl);
+    } else if (w_vec && n0 + wc + WPT <= N) {  // all columns in range, rows 16-byte aligned
       wv.load(p.w, wrow + n0 + wc);
-    else if (w_vec && n0 + wc + WPT <= N)  // all columns in range, rows 16-byte aligned
-      wv.load(p.w, wrow + n0 + wc);
-    else
+    } else {
       wv.load_clamped(p.w, wrow, n0 + wc, N);
+    }
   };
   auto deposit = [&](int buf) {
     // k = xk + e: even k to half 0, odd k to half 1, at position k / 2
@@ -131,10 +142,18 @@ void linear_leaf_kernel(const LinearArgs p) {
       *reinterpret_cast<float4 *>(&sx[buf][1][xr][xk / 2 + 4 * h]) =
           make_float4(xv.get(8 * h + 1), xv.get(8 * h + 3), xv.get(8 * h + 5), xv.get(8 * h + 7));
     }
+    if constexpr (KS == 64) {
 #pragma unroll
-    for (int e = 0; e < WPT; e += 4)
-      *reinterpret_cast<float4 *>(&sw[buf][wk][wc + e]) =
-          make_float4(wv.get(e), wv.get(e + 1), wv.get(e + 2), wv.get(e + 3));
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4 *>(&sw[buf][wk][32 * j + 4 * wcl]) =
+            make_float4(__uint_as_float(wq[j].x << 16), __uint_as_float(wq[j].x & 0xFFFF0000u),
+                        __uint_as_float(wq[j].y << 16), __uint_as_float(wq[j].y & 0xFFFF0000u));
+    } else {
+#pragma unroll
+      for (int e = 0; e < WPT; e += 4)
+        *reinterpret_cast<float4 *>(&sw[buf][wk][wc + e]) =
+            make_float4(wv.get(e), wv.get(e + 1), wv.get(e + 2), wv.get(e + 3));
+    }
   };
 
   // per lane: A operands for both blocks (rows 64 wm + l%32 and 32 more, k = 2q + l/32), the
