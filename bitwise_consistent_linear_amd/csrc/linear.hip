@@ -94,6 +94,7 @@ void linear_leaf_kernel(const LinearArgs p) {
   constexpr int XPT = TM * KS / kThreads;      // staged X values per thread (8 or 16)
   constexpr int WPT = KS * TN / kThreads;      // staged W values per thread (8 or 16)
   static_assert((KS == 32 || KS == 64) && XPT % 8 == 0 && WPT % 8 == 0, "staging shape");
+  static_assert(KS == 32 || (XBF16 && WBF16), "64-k stages stage bf16 X and W");
   __shared__ __align__(16) float sx[2][2][TM][QS];  // sx[buf][k % 2][row][k / 2]
   __shared__ __align__(16) float sw[2][KS][WS];      // sw[buf][k][col]
 
