@@ -234,8 +234,9 @@ def hbm(bytes_, ms):
 
 def is_scan_kernel(name, mode):
     """Whether a kernel name from a profile is a one-level scan of the case `mode` (0 trainer,
-    1 prefill): template arguments (d_k, lanes, stage tokens, bf16, case, threads)."""
-    return re.search(rf"cpr_scan_kernel<\d+, \d+, \d+, (true|false), {mode}, \d+>"
+    1 prefill): template arguments (d_k, lanes, stage tokens, bf16, case, threads, rows per
+    group of lanes)."""
+    return re.search(rf"cpr_scan_kernel<\d+, \d+, \d+, (true|false), {mode}, \d+, \d+>"
                      r"\(gdn::ScanArgs\)$", name) is not None
 
 
@@ -293,8 +294,8 @@ def write_traffic(fetch_csv, write_csv):
     wp, wl, wd = W.engine_prefill(), W.long_context(), W.engine_decode()
     threads = 256
 
-    def grid(wk, lanes):  # threads of a one-level launch at `lanes` lanes per row
-        rows = threads // lanes
+    def grid(wk, lanes, per_group=1):  # threads of a one-level launch at `lanes` lanes per row
+        rows = per_group * (threads // lanes)
         return wk.num_seqs * wk.num_v_heads * -(-wk.d_v // rows) * threads
 
     dec_state = wd.num_seqs * wd.num_v_heads * wd.d_v * wd.d_k * 4
@@ -302,7 +303,7 @@ def write_traffic(fetch_csv, write_csv):
         ("cpr_scan_trainer_fwd", scan(0, grid(w, 16)),
          "trainer_fwd: 4 x 4096 tokens, 16 heads, d=128, C=64, bf16 q/k/v",
          scan_bytes(w, chunk_states=w.total_chunks)),
-        ("cpr_scan_engine_prefill", scan(1, grid(wp, 4)),
+        ("cpr_scan_engine_prefill", scan(1, grid(wp, 4, 2)),
          "engine_prefill: 64 varlen sequences, 262144 tokens, 16 q/k / 32 v heads, d=128, "
          "bf16 q/k/v; o and the final states", scan_bytes(wp, final_states=wp.num_seqs)),
         ("cpr_scan_long_context_trainer", scan(0, grid(wl, 16)),

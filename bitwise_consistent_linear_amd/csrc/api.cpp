@@ -105,6 +105,23 @@ int scan_stage_tokens(const ScanArgs &a, int L) {
   return L >= 8 ? 32 : 16;
 }
 
+// Rows per group of L lanes at 4 lanes per row in 256-thread workgroups: two rows (128
+// per workgroup) share each token's k and q read from LDS, which halves the LDS reads per
+// row; the kernel then holds up to 256 registers and 64 KiB of LDS, so two waves per SIMD
+// run where one row per group runs three. Taken where there are rows for two such waves
+// on every SIMD and the 128-row blocks pad d_v no more than 64-row blocks would (engine
+// prefill workload: 13.9 against 14.4 ms). GDN_CPR_ROWS_PER_GROUP=1 or 2 overrides
+// wherever two are admitted (the same bits either way).
+int scan_rows_per_group(const ScanArgs &a, int L, int threads) {
+  if (L != 4 || threads != 256) return 1;
+  const char *env = std::getenv("GDN_CPR_ROWS_PER_GROUP");
+  if (env && std::strcmp(env, "1") == 0) return 1;
+  if (env && std::strcmp(env, "2") == 0) return 2;
+  const int64_t rows = (int64_t)a.num_seqs * a.num_v_heads * a.d_v;
+  const bool same_padding = (a.d_v + 127) / 128 * 2 == (a.d_v + 63) / 64;
+  return same_padding && rows / 32 >= 2 * device_simds() ? 2 : 1;
+}
+
 // The backward's state pass is one dependent chain per row (no readout beside it to
 // overlap), so it takes the widest rows that keep at most 2 waves per SIMD.
 int bwd_state_lanes(const ScanArgs &a) {
@@ -232,9 +249,10 @@ gdn_status_t scan_common(const char *fn, const gdn_shape_t *sh, const uint8_t *i
 
 gdn_status_t run_scan(const char *fn, ScanArgs &args, void *stream) {
   const int L = scan_lanes(args), threads = scan_threads(args, L);
-  if (scan_grid(args, L, threads) > kMaxInt32)
+  const int R = scan_rows_per_group(args, L, threads);
+  if (scan_grid(args, L, threads, R) > kMaxInt32)
     return fail(GDN_E_SHAPE, std::string(fn) + ": num_seqs * num_v_heads * row blocks too large");
-  const hipError_t e = launch_scan(args, L, scan_stage_tokens(args, L), threads,
+  const hipError_t e = launch_scan(args, L, scan_stage_tokens(args, L), threads, R,
                                    static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(GDN_E_DEVICE, std::string(fn) + ": launch failed: " + hipGetErrorString(e));

@@ -46,13 +46,17 @@ using namespace io;
 // (64-token stages staged once for 32 rows). With 512 the o buffer has one stage, not two,
 // to fit the LDS, and each wave stores only its own rows' o from it, so that a wave's next
 // stage cannot overwrite what another wave is still reading.
-template <int D, int L, int TS, bool BF16, int MODE, int NT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(L == 4 ? 3 : 1)))
+template <int D, int L, int TS, bool BF16, int MODE, int NT, int R>
+__global__ __launch_bounds__(NT)
+__attribute__((amdgpu_waves_per_eu(L == 4 ? 4 - R : 1)))
 void cpr_scan_kernel(const ScanArgs p) {
+  static_assert(R == 1 || (R == 2 && L == 4 && NT == 256), "row pairs at 4 lanes per row");
   static_assert(TS % 16 == 0, "a stage holds whole 16-token groups");
   constexpr int kThreads = NT;
   constexpr int SO_BUFS = NT == 512 ? 1 : 2;
-  constexpr int ROWS = kThreads / L;
+  // GR groups of L lanes; group g holds the R rows g, g + GR, ... of the workgroup's ROWS.
+  constexpr int GR = kThreads / L;
+  constexpr int ROWS = R * GR;
   constexpr int M = D / L;
   // Chunk boundaries inside a full stage (after its tokens 15, 31, ...) are kept from the
   // registers and stored after the stage; a trainer launch with 64-token stages is made only
@@ -116,22 +120,34 @@ void cpr_scan_kernel(const ScanArgs p) {
     cbase = first_chunk_slot(p.cu_seqlens, n, T, p.chunk, p.total_chunks, &s_acc);
 
   const int hk = h / (Hv / Hk);
-  const int i = r0 + row;
-  const bool valid = i < dv;
-  const int64_t row_off = (((int64_t)n * Hv + h) * dv + i) * D + lane * M;
+  int irow[R];
+  bool valid[R];
+  int64_t row_off[R];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    irow[rr] = r0 + row + GR * rr;
+    valid[rr] = irow[rr] < dv;
+    row_off[rr] = (((int64_t)n * Hv + h) * dv + irow[rr]) * D + lane * M;
+  }
   const int64_t vstride = (int64_t)Hv * dv;
 
-  float s[M];
-  if (p.initial_state && valid) {
-    load_row<M>(p.initial_state + row_off, s);
-  } else {
+  float s[R][M];
 #pragma unroll
-    for (int e = 0; e < M; ++e) s[e] = 0.0f;
+  for (int rr = 0; rr < R; ++rr) {
+    if (p.initial_state && valid[rr]) {
+      load_row<M>(p.initial_state + row_off[rr], s[rr]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < M; ++e) s[rr][e] = 0.0f;
+    }
   }
+  float(&s_first)[M] = s[0];
   // Complete the state loads here, once: otherwise the first use of s inside the stage
   // loop waits on the in-order load counter and with it on that stage's prefetch loads.
 #pragma unroll
-  for (int e = 0; e < M; ++e) asm volatile("" ::"v"(s[e]));
+  for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+    for (int e = 0; e < M; ++e) asm volatile("" ::"v"(s[rr][e]));
 
   // Staged inputs in registers, between their global load and their LDS deposit. Token and
   // row indices are clamped to valid addresses so the loads need no branches; the extra
@@ -283,22 +299,37 @@ void cpr_scan_kernel(const ScanArgs p) {
       }
     }
   };
-  // o of token tt of the stage, into the coalescing buffer
-  auto store_o = [&](int buf, int tt, float value) {
-    so[SO_BUFS == 1 ? 0 : buf][tt * ROWS + row] = value;
+  // o of token tt of the stage for the group's row rr, into the coalescing buffer
+  auto store_o = [&](int buf, int tt, int rr, float value) {
+    so[SO_BUFS == 1 ? 0 : buf][tt * ROWS + row + GR * rr] = value;
   };
   // One token of a stage, in row_token's order of operations (decay, key dot, delta,
-  // update, readout); q is read from LDS only once k is no longer needed, so the two are
+  // update, readout) on each of the group's R rows, whose dots run side by side and share
+  // the k and q read from LDS; q is read only once k is no longer needed, so the two are
   // never held together. Every lane of a row holds the same o_i and stores it (no branch),
   // which keeps an unrolled stage in one basic block.
   auto run_token = [&](int buf, int tt) {
-    float kr[M], qr[M], x[M];
+    float kr[M], qr[M], x[R][M], y[R][M], r[R];
     lds_slice<D, L>(&SK(buf)[tt * D], lane, kr);
-    row_decay<D, L>(s, sa[buf][tt], x);
-    const float u = contract_dot<D, L>(x, kr);
-    row_update<D, L>(s, row_delta(sb[buf][tt], sv[buf][tt * ROWS + row], u), kr, x);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      row_decay<D, L>(s[rr], sa[buf][tt], x[rr]);
+#pragma unroll
+      for (int e = 0; e < M; ++e) y[rr][e] = kr[e];
+    }
+    contract_dots<D, L, R>(x, y, r);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+      row_update<D, L>(s[rr], row_delta(sb[buf][tt], sv[buf][tt * ROWS + row + GR * rr], r[rr]),
+                       kr, x[rr]);
     lds_slice<D, L>(&SQ(buf)[tt * D], lane, qr);
-    store_o(buf, tt, contract_dot<D, L>(s, qr));
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+      for (int e = 0; e < M; ++e) y[rr][e] = qr[e];
+    contract_dots<D, L, R>(s, y, r);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) store_o(buf, tt, rr, r[rr]);
   };
 
   // A full stage, software-pipelined: the inputs of token t+2 are read from LDS while token
@@ -308,6 +339,7 @@ void cpr_scan_kernel(const ScanArgs p) {
   // interleaved, so the bits are the same. Used where few waves share a SIMD and latency,
   // not issue, bounds the stage.
   auto run_stage_pipelined = [&](int buf, float (&snap)[SNAPS][M]) {
+    float(&s)[M] = s_first;
     float rk_[3][M], rq_[3][M], ra_[3], rb_[3], rv_[3], x[M];
     auto load_token = [&](int tt, int slot) {
       lds_slice<D, L>(&SK(buf)[tt * D], lane, rk_[slot]);
@@ -340,10 +372,10 @@ void cpr_scan_kernel(const ScanArgs p) {
           ys[1][e] = rk_[nxt][e];
         }
         contract_dots<D, L, 2>(xs, ys, r);
-        store_o(buf, tt, r[0]);
+        store_o(buf, tt, 0, r[0]);
         u = r[1];
       } else {
-        store_o(buf, tt, contract_dot<D, L>(s, rq_[cur]));
+        store_o(buf, tt, 0, contract_dot<D, L>(s, rq_[cur]));
       }
     }
   };
@@ -351,14 +383,18 @@ void cpr_scan_kernel(const ScanArgs p) {
   // A chunk boundary (j + 1) % C == 0 falls on a token 16 m - 1 of a stage (see TS above).
   // `done` = tokens absorbed.
   const int chunk_shift = __builtin_ctz((unsigned)p.chunk);
-  auto store_chunk_state = [&](int64_t done, const float (&st)[M]) {
+  auto store_chunk_state = [&](int64_t done, int rr, const float (&st)[M]) {
     if constexpr (MODE == kTrainer) {
       if ((done & (p.chunk - 1)) == 0) {
         const int64_t c = cbase + (done >> chunk_shift) - 1;
-        if (valid && c >= 0 && c < p.total_chunks)
-          store_row<M>(p.chunk_states + ((c * Hv + h) * dv + i) * D + lane * M, st);
+        if (valid[rr] && c >= 0 && c < p.total_chunks)
+          store_row<M>(p.chunk_states + ((c * Hv + h) * dv + irow[rr]) * D + lane * M, st);
       }
     }
+  };
+  auto store_chunk_states = [&](int64_t done) {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) store_chunk_state(done, rr, s[rr]);
   };
   const int64_t nstages = (Tn + TS - 1) / TS;
 
@@ -387,18 +423,18 @@ void cpr_scan_kernel(const ScanArgs p) {
         run_stage_pipelined(buf, snap);
         if constexpr (INNER) {
 #pragma unroll
-          for (int m = 0; m + 1 < TS / 16; ++m) store_chunk_state(t0 + 16 * (m + 1), snap[m]);
+          for (int m = 0; m + 1 < TS / 16; ++m) store_chunk_state(t0 + 16 * (m + 1), 0, snap[m]);
         }
       } else {
 #pragma unroll
         for (int tt = 0; tt < TS; ++tt) run_token(buf, tt);
       }
-      store_chunk_state(t0 + TS, s);
+      store_chunk_states(t0 + TS);
     } else {
 #pragma unroll 1
       for (int tt = 0; tt < nt; ++tt) {
         run_token(buf, tt);
-        store_chunk_state(t0 + tt + 1, s);
+        store_chunk_states(t0 + tt + 1);
       }
     }
     if (more) deposit(buf ^ 1);
@@ -406,7 +442,9 @@ void cpr_scan_kernel(const ScanArgs p) {
     write_o(t0, nt, buf);
   }
   if constexpr (MODE == kPrefill) {
-    if (valid) store_row<M>(p.final_state + row_off, s);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+      if (valid[rr]) store_row<M>(p.final_state + row_off[rr], s[rr]);
   }
 }
 
@@ -461,25 +499,25 @@ hipError_t launch(const void *fn, int64_t grid, Args args, hipStream_t stream,
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(threads), kargs, 0, stream);
 }
 
-template <int D, int L, int TS, int NT = kThreads>
+template <int D, int L, int TS, int NT = kThreads, int R = 1>
 hipError_t scan_dl(const ScanArgs &a, hipStream_t st) {
-  const int64_t grid = scan_grid(a, L, NT);
+  const int64_t grid = scan_grid(a, L, NT, R);
   const void *fn;
   if constexpr (NT == 512) {  // bf16, d_v a multiple of 32; a trainer launch needs C >= TS
     if (!a.bf16 || a.d_v % 32 != 0 || (a.mode == kTrainer && a.chunk < TS))
       return hipErrorInvalidValue;
-    fn = a.mode == kTrainer ? (const void *)cpr_scan_kernel<D, L, TS, true, kTrainer, NT>
-                            : (const void *)cpr_scan_kernel<D, L, TS, true, kPrefill, NT>;
+    fn = a.mode == kTrainer ? (const void *)cpr_scan_kernel<D, L, TS, true, kTrainer, NT, R>
+                            : (const void *)cpr_scan_kernel<D, L, TS, true, kPrefill, NT, R>;
   } else if constexpr (TS > 32) {  // bf16 inputs only; a trainer launch needs C >= TS
     if (!a.bf16 || (a.mode == kTrainer && a.chunk < TS)) return hipErrorInvalidValue;
-    fn = a.mode == kTrainer ? (const void *)cpr_scan_kernel<D, L, TS, true, kTrainer, NT>
-                            : (const void *)cpr_scan_kernel<D, L, TS, true, kPrefill, NT>;
+    fn = a.mode == kTrainer ? (const void *)cpr_scan_kernel<D, L, TS, true, kTrainer, NT, R>
+                            : (const void *)cpr_scan_kernel<D, L, TS, true, kPrefill, NT, R>;
   } else if (a.mode == kTrainer) {
-    fn = a.bf16 ? (const void *)cpr_scan_kernel<D, L, TS, true, kTrainer, NT>
-                : (const void *)cpr_scan_kernel<D, L, TS, false, kTrainer, NT>;
+    fn = a.bf16 ? (const void *)cpr_scan_kernel<D, L, TS, true, kTrainer, NT, R>
+                : (const void *)cpr_scan_kernel<D, L, TS, false, kTrainer, NT, R>;
   } else {
-    fn = a.bf16 ? (const void *)cpr_scan_kernel<D, L, TS, true, kPrefill, NT>
-                : (const void *)cpr_scan_kernel<D, L, TS, false, kPrefill, NT>;
+    fn = a.bf16 ? (const void *)cpr_scan_kernel<D, L, TS, true, kPrefill, NT, R>
+                : (const void *)cpr_scan_kernel<D, L, TS, false, kPrefill, NT, R>;
   }
   return launch(fn, grid, a, st, NT);
 }
@@ -492,7 +530,11 @@ hipError_t decode_dl(const DecodeArgs &a, hipStream_t st) {
 }
 
 template <int D>
-hipError_t scan_d(const ScanArgs &a, int L, int TS, int NT, hipStream_t st) {
+hipError_t scan_d(const ScanArgs &a, int L, int TS, int NT, int R, hipStream_t st) {
+  if (R == 2)
+    return L == 4 && TS == 16 && NT == 256 ? scan_dl<D, 4, 16, 256, 2>(a, st)
+                                           : hipErrorInvalidValue;
+  if (R != 1) return hipErrorInvalidValue;
   if (NT == 512) return L == 16 && TS == 64 ? scan_dl<D, 16, 64, 512>(a, st) : hipErrorInvalidValue;
   if (L == 16 && TS == 64 && a.bf16) return scan_dl<D, 16, 64>(a, st);
   if (L == 16 && TS == 32) return scan_dl<D, 16, 32>(a, st);
@@ -513,8 +555,8 @@ hipError_t decode_d(const DecodeArgs &a, int L, hipStream_t st) {
 
 }  // namespace
 
-int64_t scan_grid(const ScanArgs &a, int L, int threads) {
-  const int64_t rows = threads / L;
+int64_t scan_grid(const ScanArgs &a, int L, int threads, int rows_per_group) {
+  const int64_t rows = (int64_t)rows_per_group * (threads / L);
   return (int64_t)a.num_seqs * a.num_v_heads * ((a.d_v + rows - 1) / rows);
 }
 
@@ -523,12 +565,13 @@ int64_t decode_grid(const DecodeArgs &a, int L) {
   return (int64_t)a.num_seqs * a.num_v_heads * ((a.d_v + rows - 1) / rows);
 }
 
-hipError_t launch_scan(const ScanArgs &a, int L, int TS, int threads, hipStream_t st) {
+hipError_t launch_scan(const ScanArgs &a, int L, int TS, int threads, int rows_per_group,
+                       hipStream_t st) {
   switch (a.d_k) {
-    case 16: return scan_d<16>(a, L, TS, threads, st);
-    case 32: return scan_d<32>(a, L, TS, threads, st);
-    case 64: return scan_d<64>(a, L, TS, threads, st);
-    case 128: return scan_d<128>(a, L, TS, threads, st);
+    case 16: return scan_d<16>(a, L, TS, threads, rows_per_group, st);
+    case 32: return scan_d<32>(a, L, TS, threads, rows_per_group, st);
+    case 64: return scan_d<64>(a, L, TS, threads, rows_per_group, st);
+    case 128: return scan_d<128>(a, L, TS, threads, rows_per_group, st);
     default: return hipErrorInvalidValue;
   }
 }

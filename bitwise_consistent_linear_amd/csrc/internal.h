@@ -134,13 +134,15 @@ int64_t linear_grid(const LinearArgs &args);
 hipError_t launch_linear(const LinearArgs &args, hipStream_t stream);
 
 // Enqueue the kernels. lanes_per_row is 16, 8 or 4; a scan workgroup has 256 threads, or
-// 512 with 16 lanes per row and 64-token stages. Return the HIP launch status.
+// 512 with 16 lanes per row and 64-token stages; each group of lanes_per_row lanes holds one
+// row, or two (rows_per_group = 2, at 4 lanes per row in 256-thread workgroups with
+// 16-token stages). Return the HIP launch status.
 hipError_t launch_scan(const ScanArgs &args, int lanes_per_row, int stage_tokens, int threads,
-                       hipStream_t stream);
+                       int rows_per_group, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &args, int lanes_per_row, hipStream_t stream);
 
 // Number of workgroups a scan or decode launch uses (for the host-side size claims).
-int64_t scan_grid(const ScanArgs &args, int lanes_per_row, int threads);
+int64_t scan_grid(const ScanArgs &args, int lanes_per_row, int threads, int rows_per_group);
 int64_t decode_grid(const DecodeArgs &args, int lanes_per_row);
 
 }  // namespace gdn

@@ -113,6 +113,24 @@ class scan_threads:
             os.environ["GDN_CPR_SCAN_THREADS"] = self.old
 
 
+class rows_per_group:
+    """Context manager: at 4 lanes per row in 256-thread scan workgroups, hold R rows (1 or
+    2) in each group of lanes; without it the library picks."""
+
+    def __init__(self, R):
+        self.R = str(R)
+
+    def __enter__(self):
+        self.old = os.environ.get("GDN_CPR_ROWS_PER_GROUP")
+        os.environ["GDN_CPR_ROWS_PER_GROUP"] = self.R
+
+    def __exit__(self, *exc):
+        if self.old is None:
+            os.environ.pop("GDN_CPR_ROWS_PER_GROUP", None)
+        else:
+            os.environ["GDN_CPR_ROWS_PER_GROUP"] = self.old
+
+
 def decode_steps(dev_steps, state, chunk, s_range=None, resync=True):
     """Run decode steps; yields (step index, o, resync tensor or None)."""
     S = dev_steps["q"].shape[0]

@@ -93,9 +93,9 @@ def test_alu_peak_is_the_published_fp32_vector_peak():
 
 def test_scan_kernel_names_are_matched_by_case():
     # the names rocprofv3 prints for the scan kernels (template: d_k, lanes per row, stage
-    # tokens, bf16, case, threads per workgroup)
-    trainer = "void gdn::(anonymous namespace)::cpr_scan_kernel<128, 16, 64, true, 0, 512>(gdn::ScanArgs)"
-    prefill = "void gdn::(anonymous namespace)::cpr_scan_kernel<128, 4, 16, true, 1, 256>(gdn::ScanArgs)"
+    # tokens, bf16, case, threads per workgroup, rows per group of lanes)
+    trainer = "void gdn::(anonymous namespace)::cpr_scan_kernel<128, 16, 64, true, 0, 512, 1>(gdn::ScanArgs)"
+    prefill = "void gdn::(anonymous namespace)::cpr_scan_kernel<128, 4, 16, true, 1, 256, 2>(gdn::ScanArgs)"
     assert bench.is_scan_kernel(trainer, 0) and not bench.is_scan_kernel(trainer, 1)
     assert bench.is_scan_kernel(prefill, 1) and not bench.is_scan_kernel(prefill, 0)
     assert not bench.is_scan_kernel(

@@ -17,7 +17,7 @@ import torch
 from bitwise_consistent_linear_amd import api
 from bitwise_consistent_linear_amd import workloads as W
 from gpu_util import (DEV, LANES, assert_bits, assert_dev_equal, decode_steps, lanes, log,
-                      scan_threads, up, up_steps, up_workload)
+                      rows_per_group, scan_threads, up, up_steps, up_workload)
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -123,6 +123,15 @@ def test_small_cases_match_oracle(case):
         assert_bits(cs, rcs, f"{case[0]} L={L} trainer chunk states")
         assert_bits(po, ro, f"{case[0]} L={L} prefill o")
         assert_bits(fs, rfs, f"{case[0]} L={L} prefill final")
+    # two rows per group of 4 lanes (128-row workgroups)
+    with lanes(4), rows_per_group(2):
+        o, cs = run_trainer(w, d, ds0)
+        po, fs = run_prefill(w, d, ds0)
+        torch.cuda.synchronize()
+    assert_bits(o, ro, f"{case[0]} L=4 row pairs trainer o")
+    assert_bits(cs, rcs, f"{case[0]} L=4 row pairs trainer chunk states")
+    assert_bits(po, ro, f"{case[0]} L=4 row pairs prefill o")
+    assert_bits(fs, rfs, f"{case[0]} L=4 row pairs prefill final")
 
 
 # 512-thread workgroups (32 rows, 64-token stages, a one-stage o buffer written back per
@@ -259,11 +268,11 @@ def test_config_trainer_fwd():
     assert_dev_equal(po, o, "trainer vs prefill o")
     last = cs.view(4, 64, 16, 128, 128)[:, -1]
     assert_dev_equal(fs, last, "prefill final vs last chunk state")
-    for L in (8, 4):
-        with lanes(L):
+    for L, R in ((8, 1), (4, 1), (4, 2)):
+        with lanes(L), rows_per_group(R):
             o2, cs2 = run_trainer(w, d)
-        assert_dev_equal(o2, o, f"L={L} vs L=16 o")
-        assert_dev_equal(cs2, cs, f"L={L} vs L=16 chunk states")
+        assert_dev_equal(o2, o, f"L={L} R={R} vs L=16 o")
+        assert_dev_equal(cs2, cs, f"L={L} R={R} vs L=16 chunk states")
     # this shape runs in 512-thread workgroups with 64-token stages; 256 threads and
     # 32-token stages give the same bits
     with scan_threads(256):
@@ -285,6 +294,11 @@ def test_config_engine_prefill():
     o, cs = run_trainer(w, d)
     torch.cuda.synchronize()
     assert_dev_equal(o, po, "trainer vs prefill o")
+    # this shape runs two rows per group of 4 lanes; one row per group gives the same bits
+    with rows_per_group(1):
+        po1, fs1 = run_prefill(w, d)
+    assert_dev_equal(po1, po, "one vs two rows per group prefill o")
+    assert_dev_equal(fs1, fs, "one vs two rows per group final states")
     longest, shortest = int(np.argmax(L)), int(np.argmin(L))
     sampled_oracle(w, [(longest, 31), (shortest, 0), (7, 13)], po, cs, fs)
 

@@ -5,7 +5,7 @@ mixes them: every admitted d_k and C, GQA groups, ragged d_v (row blocks that en
 and d_v below a wave's rows), empty and ragged sequences whose lengths end anywhere
 relative to C and to the scan's stages, f32 and bf16 storage, initial states and
 dL/dS_final present or absent, and a launch configuration (lanes per row, scan workgroup
-size, backward schedule) drawn with them. The forward's trainer output, chunk states,
+size, rows per group of lanes, backward schedule) drawn with them. The forward's trainer output, chunk states,
 prefill output and final state and the backward's six gradients are compared element by
 element with the oracle on the same inputs. The draw is fixed by its seed, so a failure
 names a case that reproduces.
@@ -17,7 +17,8 @@ import torch
 
 from bitwise_consistent_linear_amd import api
 from bitwise_consistent_linear_amd import workloads as W
-from gpu_util import (assert_bits, lanes, log, scan_threads, schedule, up, up_workload)
+from gpu_util import (assert_bits, lanes, log, rows_per_group, scan_threads, schedule, up,
+                      up_workload)
 from oracle import oracle as O
 
 SWEEP_SEED = 20261203
@@ -26,9 +27,11 @@ SWEEP_CASES = 96
 
 def draw_cases(seed=SWEEP_SEED, n=SWEEP_CASES):
     """n case tuples (name, lengths, Hk, Hv, d_k, d_v, chunk, bf16, with_s0, with_dsf, L,
-    threads, bwd schedule, data seed), sized so that the oracle's backward of the largest
-    stays near a second. Every fourth case is drawn where 512-thread scan workgroups are
-    admitted (16 lanes per row, bf16, d_v a multiple of 32) and asks for them."""
+    threads, bwd schedule, data seed, rows per group), sized so that the oracle's backward
+    of the largest stays near a second. Every fourth case is drawn where 512-thread scan
+    workgroups are admitted (16 lanes per row, bf16, d_v a multiple of 32) and asks for
+    them; every other case is run with two rows per group of lanes where it has 4 lanes per
+    row (the row-pair count takes no draw, so the other fields are as drawn before)."""
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -50,10 +53,11 @@ def draw_cases(seed=SWEEP_SEED, n=SWEEP_CASES):
         L = 16 if wide else int(rng.choice([16, 8, 4]))
         threads = 512 if wide else 256
         sched = str(rng.choice(["chunks", "sequences"]))
+        R = 2 if L == 4 and i % 2 == 0 else 1
         name = (f"s{i:02d}_dk{dk}_dv{dv}_c{chunk}_h{Hk}x{Hv // Hk}_{'bf16' if bf16 else 'f32'}"
-                f"_L{L}_t{threads}_{sched}")
+                f"_L{L}_t{threads}_r{R}_{sched}")
         cases.append((name, lengths, Hk, Hv, dk, dv, chunk, bf16, with_s0, with_dsf, L,
-                      threads, sched, 3000 + i))
+                      threads, sched, 3000 + i, R))
     return cases
 
 
@@ -70,7 +74,7 @@ def test_sweep_draw_is_fixed_and_admitted():
 
 
 def sweep_workload(case):
-    (name, lengths, Hk, Hv, dk, dv, chunk, bf16, with_s0, with_dsf, _L, _t, _s, seed) = case
+    (name, lengths, Hk, Hv, dk, dv, chunk, bf16, with_s0, with_dsf, _L, _t, _s, seed, _R) = case
     w = W.make_packed(name, lengths, Hk=Hk, Hv=Hv, d=dk, chunk=chunk, bf16=bf16, seed=seed)
     if dv != dk:  # v of width d_v from the same recipe
         w.v = W.make_packed(name, lengths, Hk=Hv, Hv=Hv, d=dv, chunk=chunk, bf16=bf16,
@@ -86,7 +90,7 @@ def sweep_workload(case):
 @pytest.mark.gpu
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_sweep_forward_and_backward_match_oracle(case):
-    name, L, threads, sched = case[0], case[10], case[11], case[12]
+    name, L, threads, sched, R = case[0], case[10], case[11], case[12], case[14]
     log(f"sweep: {case}")
     w, s0, do, dsf = sweep_workload(case)
     ro, rcs, rfs = O.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=w.chunk,
@@ -95,7 +99,7 @@ def test_sweep_forward_and_backward_match_oracle(case):
                      initial_state=s0, dstate_final=dsf)
     d = up_workload(w)
     ds0 = None if s0 is None else up(s0)
-    with lanes(L), scan_threads(threads), schedule(sched):
+    with lanes(L), scan_threads(threads), rows_per_group(R), schedule(sched):
         o, cs = api.trainer_fwd(d["cu"], d["q"], d["k"], d["v"], d["a"], d["b"],
                                 chunk=w.chunk, initial_state=ds0,
                                 total_chunks=w.total_chunks)

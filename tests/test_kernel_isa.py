@@ -26,9 +26,10 @@ def kernels(asm):
 
 def test_all_kernels_present(asm):
     names = kernels(asm)
-    # d_k x case x (dtype x (lanes per row, stage tokens) in (16, 32), (8, 32), (4, 16), and
-    # (16, 64) for bf16 in 256- and in 512-thread workgroups)
-    assert sum("cpr_scan_kernel" in n for n in names) == 4 * 2 * (2 * 3 + 2)
+    # d_k x case x (dtype x (lanes per row, stage tokens, rows per group) in (16, 32, 1),
+    # (8, 32, 1), (4, 16, 1), (4, 16, 2), and (16, 64, 1) for bf16 in 256- and in 512-thread
+    # workgroups)
+    assert sum("cpr_scan_kernel" in n for n in names) == 4 * 2 * (2 * 4 + 2)
     assert sum("cpr_decode_kernel" in n for n in names) == 4 * 3 * 2
     assert sum("cpr_bwd_plan_kernel" in n for n in names) == 1
     assert sum("cpr_bwd_state_kernel" in n for n in names) == 4 * 3 * 2
