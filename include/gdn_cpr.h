@@ -56,7 +56,9 @@
  * that keeps at most two wavefronts per SIMD). The environment variable
  * GDN_CPR_LANES_PER_ROW (16, 8 or 4) overrides the choice. With two wavefronts per SIMD at
  * 16 lanes, bf16 inputs and d_v a multiple of 32 a scan workgroup has 512 threads
- * (GDN_CPR_SCAN_THREADS=256 keeps 256), and the backward picks its schedule by the number
+ * (GDN_CPR_SCAN_THREADS=256 keeps 256); at 4 lanes, where rows fill two 32-row wavefronts
+ * on every SIMD, each group of 4 lanes holds two rows (GDN_CPR_ROWS_PER_GROUP=1 or 2
+ * overrides); and the backward picks its schedule by the number
  * of (sequence, head, row block) units (GDN_CPR_BWD_SCHEDULE=sequences or chunks
  * overrides). The contract makes every admitted choice give the same bits, which the
  * tests check.
