@@ -15,7 +15,8 @@
 // straight from the registers, each lane its contiguous slice of the row.
 //
 // Decode: one launch per step; each row's d_k floats are read from HBM, updated once and
-// written back (plus the resync checkpoint on C-token boundaries).
+// written back (plus the resync checkpoint on C-token boundaries). For d_k >= 32 a row sits
+// on 32 lanes (row_token_split), so that each lane moves 16 bytes of the row at d_k = 128.
 //
 // Scheduling: workgroups of the longest sequences are dispatched first (for up to 1024
 // sequences the rank of every sequence by length is computed in LDS), so that the long
@@ -448,9 +449,19 @@ void cpr_scan_kernel(const ScanArgs p) {
   }
 }
 
+// On 32 lanes per row each group of lanes holds two rows, g and g + 8 of a 16-row block, so
+// that a wave keeps as many bytes in flight as on 16 lanes (one 16-byte load per lane and
+// row, each load instruction covering two whole rows).
+template <int D, int L>
+constexpr int decode_rows_per_group() {
+  return L == 32 ? 2 : 1;
+}
+
 template <int D, int L, bool BF16>
 __global__ __launch_bounds__(kThreads) void cpr_decode_kernel(const DecodeArgs p) {
-  constexpr int ROWS = kThreads / L;
+  constexpr int R = decode_rows_per_group<D, L>();
+  constexpr int GR = kThreads / L;
+  constexpr int ROWS = R * GR;
   constexpr int M = D / L;
   const int tid = threadIdx.x, row = tid / L, lane = tid % L;
   const int Hv = p.num_v_heads, Hk = p.num_qk_heads, dv = p.d_v;
@@ -459,10 +470,8 @@ __global__ __launch_bounds__(kThreads) void cpr_decode_kernel(const DecodeArgs p
   block_work(blockIdx.x, p.num_seqs * Hv, rblocks, Hv / Hk, pair, rblock);
   const int n = pair / Hv;
   const int h = pair % Hv;
-  const int i = rblock * ROWS + row;
   const int pos = p.pos[n];
   if (pos < 0) return;  // idle slot: uniform over the workgroup
-  const bool valid = i < dv;
   const int hk = h / (Hv / Hk);
 
   float kr[M], qr[M];
@@ -471,21 +480,48 @@ __global__ __launch_bounds__(kThreads) void cpr_decode_kernel(const DecodeArgs p
   load_input<M, BF16>(p.q, qk_off, qr);
   const int64_t nh = (int64_t)n * Hv + h;
   const float a = p.a[nh], b = p.b[nh];
-  const float v_i = valid ? load1<BF16>(p.v, nh * dv + i) : 0.0f;
-  const int64_t row_off = (nh * dv + i) * D + lane * M;
-  float s[M];
-  if (valid) {
-    load_row<M>(p.state + row_off, s);
-  } else {
+  int i[R];
+  bool valid[R];
+  float v_i[R], s[R][M], oi[R];
+  int64_t row_off[R];
 #pragma unroll
-    for (int e = 0; e < M; ++e) s[e] = 0.0f;
+  for (int rr = 0; rr < R; ++rr) {
+    i[rr] = rblock * ROWS + row + GR * rr;
+    valid[rr] = i[rr] < dv;
+    row_off[rr] = (nh * dv + i[rr]) * D + lane * M;
+    if constexpr (L == 32) {
+      // Rows past d_v load (and compute on) the last row, so that every load is issued
+      // unconditionally and both rows' loads are in flight together (measured 187 against
+      // 210 us per step on the engine_decode workload with the loads behind branches);
+      // only valid rows store.
+      const int ic = valid[rr] ? i[rr] : dv - 1;
+      v_i[rr] = load1<BF16>(p.v, nh * dv + ic);
+      load_row<M>(p.state + (nh * dv + ic) * D + lane * M, s[rr]);
+    } else {
+      v_i[rr] = valid[rr] ? load1<BF16>(p.v, nh * dv + i[rr]) : 0.0f;
+      if (valid[rr]) {
+        load_row<M>(p.state + row_off[rr], s[rr]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < M; ++e) s[rr][e] = 0.0f;
+      }
+    }
   }
-  const float oi = row_token<D, L>(s, a, b, v_i, kr, qr);
-  if (valid) {
-    store_row<M>(p.state + row_off, s);
-    if (lane == 0) p.o[nh * dv + i] = oi;
-    if (p.resync_states && (((int64_t)pos + 1) & (p.chunk - 1)) == 0)
-      store_row<M>(p.resync_states + row_off, s);
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    if constexpr (L == 32)
+      oi[rr] = row_token_split<D>(s[rr], a, b, v_i[rr], kr, qr);
+    else
+      oi[rr] = row_token<D, L>(s[rr], a, b, v_i[rr], kr, qr);
+  }
+  const bool resync = p.resync_states && (((int64_t)pos + 1) & (p.chunk - 1)) == 0;
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    if (valid[rr]) {
+      store_row<M>(p.state + row_off[rr], s[rr]);
+      if (lane == 0) p.o[nh * dv + i[rr]] = oi[rr];
+      if (resync) store_row<M>(p.resync_states + row_off[rr], s[rr]);
+    }
   }
 }
 
@@ -545,6 +581,9 @@ hipError_t scan_d(const ScanArgs &a, int L, int TS, int NT, int R, hipStream_t s
 
 template <int D>
 hipError_t decode_d(const DecodeArgs &a, int L, hipStream_t st) {
+  if constexpr (D >= 32) {
+    if (L == 32) return decode_dl<D, 32>(a, st);
+  }
   switch (L) {
     case 16: return decode_dl<D, 16>(a, st);
     case 8: return decode_dl<D, 8>(a, st);
@@ -561,7 +600,7 @@ int64_t scan_grid(const ScanArgs &a, int L, int threads, int rows_per_group) {
 }
 
 int64_t decode_grid(const DecodeArgs &a, int L) {
-  const int64_t rows = kThreads / L;
+  const int64_t rows = (L == 32 ? 2 : 1) * (kThreads / L);
   return (int64_t)a.num_seqs * a.num_v_heads * ((a.d_v + rows - 1) / rows);
 }
 

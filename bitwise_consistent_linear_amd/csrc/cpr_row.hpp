@@ -1,8 +1,10 @@
 // Per-token update of one state row, spread over L lanes of a wavefront (gfx950).
 //
-// This is the only implementation of the recurrence's arithmetic on the GPU; the scan
-// kernel (trainer_fwd, prefill) and the decode kernel both call row_token, so the three
-// cases run the same sequence of binary32 operations and agree bit for bit.
+// The scan kernel (trainer_fwd, prefill) calls these steps, and the decode kernel calls
+// row_token, so the three cases run the same sequence of binary32 operations and agree bit
+// for bit. The wide decode kernel holds a row on 32 lanes (row_token_split below): the same
+// operations on the same operands in the same order, with each leaf's chain handed from
+// one lane to the next half-way.
 //
 // A row s of d_k = D binary32 values lives in the VGPRs of L consecutive lanes: lane l
 // holds elements [l*M, (l+1)*M) with M = D/L, i.e. P = 16/L whole leaves of W = D/16
@@ -27,6 +29,8 @@ constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
+constexpr int kDppQuadEven = 0xA0;    // quad_perm [0,0,2,2]: each lane reads its even lane
+constexpr int kDppQuadOdd = 0xF5;     // quad_perm [1,1,3,3]: each lane reads its odd lane
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_partner(float x) {
@@ -162,6 +166,56 @@ template <int D, int L>
 __device__ __forceinline__ void row_bwd_decay(float (&sh)[D / L], float a, const float (&xh)[D / L]) {
 #pragma unroll
   for (int e = 0; e < RowShape<D, L>::M; ++e) sh[e] = a * xh[e];
+}
+
+// ------------------------------------------------------------ a row on 32 lanes (decode)
+// Lane l of a 32-lane row holds elements [l*M, (l+1)*M), M = D/32: the first or second half
+// of leaf l/2 (leaf width 2M), so a lane's slice is 16 bytes at d_k = 128. A leaf's chain
+// starts in its even lane (rounded first product, fmaf for the rest of that half) and
+// continues in its odd lane from the even lane's partial, copied by DPP; the odd lane's
+// result, copied back, is the leaf in both lanes. The tree then pairs leaves 2m and 2m+1
+// (lanes two apart: quad_perm [2,3,0,1]), leaf pairs (the other half of each 8-lane group:
+// row_half_mirror), groups of four (the other half of the 16-lane row: row_mirror) and the
+// two halves of the 32-lane row (a lane swap between 16-lane rows): the natural pairing of
+// the contract's tree, every lane of the row ending with the same bits.
+__device__ __forceinline__ float swap16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D>
+__device__ __forceinline__ float contract_dot_split(const float (&x)[D / 32],
+                                                    const float (&y)[D / 32]) {
+  static_assert(D % 32 == 0, "a leaf spans two lanes");
+  constexpr int M = D / 32;
+  float part = x[0] * y[0];
+#pragma unroll
+  for (int e = 1; e < M; ++e) part = __builtin_fmaf(x[e], y[e], part);
+  float leaf = dpp_partner<kDppQuadEven>(part);  // odd lanes: continue the even lane's chain
+#pragma unroll
+  for (int e = 0; e < M; ++e) leaf = __builtin_fmaf(x[e], y[e], leaf);
+  float r = dpp_partner<kDppQuadOdd>(leaf);
+  r = r + dpp_partner<kDppQuadXor2>(r);
+  r = r + dpp_partner<kDppRowHalfMirror>(r);
+  r = r + dpp_partner<kDppRowMirror>(r);
+  return swap16_sum(r);
+}
+
+// row_token on a 32-lane row: decay, key dot, delta, fused rank-1 update, query readout.
+template <int D>
+__device__ __forceinline__ float row_token_split(float (&s)[D / 32], float a, float b,
+                                                 float v_i, const float (&k)[D / 32],
+                                                 const float (&q)[D / 32]) {
+  constexpr int M = D / 32;
+  float x[M];
+#pragma unroll
+  for (int e = 0; e < M; ++e) x[e] = a * s[e];
+  const float u = contract_dot_split<D>(x, k);
+  const float delta = row_delta(b, v_i, u);
+#pragma unroll
+  for (int e = 0; e < M; ++e) s[e] = __builtin_fmaf(delta, k[e], x[e]);
+  return contract_dot_split<D>(s, q);
 }
 
 }  // namespace gdn

@@ -52,9 +52,10 @@
  *
  * TUNING. How many lanes of a wavefront share one state row is chosen per call from the
  * number of rows: 16 when that gives at most two wavefronts per SIMD, 8 when 8 lanes give
- * at most one, 4 otherwise (decode: 16; the backward's reverse pass over dL/dS: the widest
- * that keeps at most two wavefronts per SIMD). The environment variable
- * GDN_CPR_LANES_PER_ROW (16, 8 or 4) overrides the choice. With two wavefronts per SIMD at
+ * at most one, 4 otherwise (decode: 32 for d_k >= 32, two rows per group of 32 lanes, else
+ * 16; the backward's reverse pass over dL/dS: the widest that keeps at most two wavefronts
+ * per SIMD). The environment variable GDN_CPR_LANES_PER_ROW (16, 8 or 4; 32 for decode
+ * only) overrides the choice. With two wavefronts per SIMD at
  * 16 lanes, bf16 inputs and d_v a multiple of 32 a scan workgroup has 512 threads
  * (GDN_CPR_SCAN_THREADS=256 keeps 256); at 4 lanes, where rows fill two 32-row wavefronts
  * on every SIMD, each group of 4 lanes holds two rows (GDN_CPR_ROWS_PER_GROUP=1 or 2

@@ -162,7 +162,7 @@ def test_small_cases_512_threads_match_oracle(case):
     assert_bits(fs, rfs, f"{case[0]} prefill final")
 
 
-@pytest.mark.parametrize("L", LANES)
+@pytest.mark.parametrize("L", LANES + (32,))
 def test_decode_matches_oracle_and_trainer(L):
     # equal-length batch: prefix by prefill, then decode steps across several boundaries
     w = W.make_packed("dec", [90] * 3, Hk=2, Hv=4, d=64, chunk=16, bf16=True, seed=77)
@@ -182,6 +182,33 @@ def test_decode_matches_oracle_and_trainer(L):
             assert_bits(o, ro_seq[:, 21 + s], f"decode o step {s}")
             if (21 + s + 1) % 16 == 0:
                 assert_bits(rs, rcs_seq[:, (21 + s + 1) // 16 - 1], f"resync step {s}")
+    assert_bits(state, rfs, "decode final state")
+
+
+@pytest.mark.parametrize("dk,dv,bf16", [(32, 32, False), (128, 40, True), (64, 64, False)])
+def test_decode_32_lanes_per_row(dk, dv, bf16):
+    # a row on 32 lanes (each leaf's chain handed from one lane to the next) for every d_k
+    # that admits it, binary32 and bf16 inputs, a d_v that ends part-way through a workgroup
+    w = W.make_packed("dec32", [40] * 2, Hk=1, Hv=2, d=dk, chunk=16, bf16=bf16, seed=79)
+    if dv != dk:
+        w.v = W.make_packed("dec32", [40] * 2, Hk=2, Hv=2, d=dv, chunk=16, bf16=bf16,
+                            seed=80).v
+    g = np.random.default_rng(9)
+    s0 = (0.25 * g.standard_normal((2, 2, dv, dk))).astype(np.float32)
+    log(f"decode 32 lanes per row: d_k={dk} d_v={dv} bf16={bf16}")
+    ro, rcs, rfs = O.scan(w.cu_seqlens, w.q, w.k, w.v, w.a, w.b, chunk=16, initial_state=s0,
+                          want_chunk_states=True, want_final_state=True)
+    pre, steps = W.split_for_decode(w, 5)
+    dp = up_workload(pre)
+    with lanes(32):
+        _, state = run_prefill(pre, dp, up(s0))
+        dsteps = up_steps(steps)
+        ro_seq = ro.reshape(2, 40, 2, dv)
+        rcs_seq = rcs.reshape(2, 2, 2, dv, dk)
+        for s, o, rs in decode_steps(dsteps, state, 16):
+            assert_bits(o, ro_seq[:, 5 + s], f"decode o step {s}")
+            if (5 + s + 1) % 16 == 0:
+                assert_bits(rs, rcs_seq[:, (5 + s + 1) // 16 - 1], f"resync step {s}")
     assert_bits(state, rfs, "decode final state")
 
 

@@ -30,7 +30,8 @@ def test_all_kernels_present(asm):
     # (8, 32, 1), (4, 16, 1), (4, 16, 2), and (16, 64, 1) for bf16 in 256- and in 512-thread
     # workgroups)
     assert sum("cpr_scan_kernel" in n for n in names) == 4 * 2 * (2 * 4 + 2)
-    assert sum("cpr_decode_kernel" in n for n in names) == 4 * 3 * 2
+    # d_k x (lanes per row 16, 8, 4) x dtype, and 32 lanes per row for d_k = 32, 64, 128
+    assert sum("cpr_decode_kernel" in n for n in names) == 4 * 3 * 2 + 3 * 2
     assert sum("cpr_bwd_plan_kernel" in n for n in names) == 1
     assert sum("cpr_bwd_state_kernel" in n for n in names) == 4 * 3 * 2
     # d_k, dtype, schedule, and (chunks longer than one 64-token segment, the general loops
