@@ -407,10 +407,14 @@ void cpr_scan_kernel(const ScanArgs p) {
     deposit(0);
   }
   __syncthreads();
-  for (int64_t st = 0; st < nstages; ++st) {
+  // Full stages in the loop; a sequence's last stage, if partial, after it. Keeping the
+  // partial stage's token loop out of the stage loop lets the state stay in one set of
+  // registers across stages (with both in the loop the compiler copied the state in and
+  // out of the full stage, 128 moves per stage at 4 lanes per row and two rows per group).
+  const int64_t nfull = Tn / TS;
+  for (int64_t st = 0; st < nfull; ++st) {
     const int buf = (int)(st & 1);
     const int64_t t0 = st * TS;
-    const int nt = (int)(Tn - t0 < TS ? Tn - t0 : TS);
     const bool more = st + 1 < nstages;
     if (more) {  // global loads in flight while this stage computes
       if (t0 + 2 * TS <= Tn)
@@ -418,27 +422,31 @@ void cpr_scan_kernel(const ScanArgs p) {
       else
         fetch(t0 + TS);
     }
-    if (nt == TS) {
-      if constexpr (L >= 8) {
-        float snap[SNAPS][M];
-        run_stage_pipelined(buf, snap);
-        if constexpr (INNER) {
+    if constexpr (L >= 8) {
+      float snap[SNAPS][M];
+      run_stage_pipelined(buf, snap);
+      if constexpr (INNER) {
 #pragma unroll
-          for (int m = 0; m + 1 < TS / 16; ++m) store_chunk_state(t0 + 16 * (m + 1), 0, snap[m]);
-        }
-      } else {
-#pragma unroll
-        for (int tt = 0; tt < TS; ++tt) run_token(buf, tt);
+        for (int m = 0; m + 1 < TS / 16; ++m) store_chunk_state(t0 + 16 * (m + 1), 0, snap[m]);
       }
-      store_chunk_states(t0 + TS);
     } else {
-#pragma unroll 1
-      for (int tt = 0; tt < nt; ++tt) {
-        run_token(buf, tt);
-        store_chunk_states(t0 + tt + 1);
-      }
+#pragma unroll
+      for (int tt = 0; tt < TS; ++tt) run_token(buf, tt);
     }
+    store_chunk_states(t0 + TS);
     if (more) deposit(buf ^ 1);
+    __syncthreads();
+    write_o(t0, TS, buf);
+  }
+  if (nfull < nstages) {  // the last stage, partial: its inputs were deposited already
+    const int buf = (int)(nfull & 1);
+    const int64_t t0 = nfull * TS;
+    const int nt = (int)(Tn - t0);
+#pragma unroll 1
+    for (int tt = 0; tt < nt; ++tt) {
+      run_token(buf, tt);
+      store_chunk_states(t0 + tt + 1);
+    }
     __syncthreads();
     write_o(t0, nt, buf);
   }
@@ -452,14 +460,11 @@ void cpr_scan_kernel(const ScanArgs p) {
 // On 32 lanes per row each group of lanes holds two rows, g and g + 8 of a 16-row block, so
 // that a wave keeps as many bytes in flight as on 16 lanes (one 16-byte load per lane and
 // row, each load instruction covering two whole rows).
-template <int D, int L>
-constexpr int decode_rows_per_group() {
-  return L == 32 ? 2 : 1;
-}
+constexpr int decode_rows_per_group(int L) { return L == 32 ? 2 : 1; }
 
 template <int D, int L, bool BF16>
 __global__ __launch_bounds__(kThreads) void cpr_decode_kernel(const DecodeArgs p) {
-  constexpr int R = decode_rows_per_group<D, L>();
+  constexpr int R = decode_rows_per_group(L);
   constexpr int GR = kThreads / L;
   constexpr int ROWS = R * GR;
   constexpr int M = D / L;
@@ -600,7 +605,7 @@ int64_t scan_grid(const ScanArgs &a, int L, int threads, int rows_per_group) {
 }
 
 int64_t decode_grid(const DecodeArgs &a, int L) {
-  const int64_t rows = (L == 32 ? 2 : 1) * (kThreads / L);
+  const int64_t rows = decode_rows_per_group(L) * (kThreads / L);
   return (int64_t)a.num_seqs * a.num_v_heads * ((a.d_v + rows - 1) / rows);
 }
 
