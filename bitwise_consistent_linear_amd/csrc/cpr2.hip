@@ -511,12 +511,22 @@ __global__ __launch_bounds__(kThreads) void cpr2_cache_kernel(const Cpr2Args p, 
   const int Hk = p.num_qk_heads, Hv = p.num_v_heads, dk = p.d_k, dv = p.d_v, C = p.chunk;
   const int64_t row = (int64_t)n * C + pos % C;
   using T = typename std::conditional<BF16, uint16_t, float>::type;
-  for (int e = threadIdx.x; e < Hk * dk; e += kThreads)
-    static_cast<T *>(p.cache_k)[row * Hk * dk + e] =
-        static_cast<const T *>(k)[(int64_t)n * Hk * dk + e];
-  for (int e = threadIdx.x; e < Hv * dv; e += kThreads)
-    static_cast<T *>(p.cache_v)[row * Hv * dv + e] =
-        static_cast<const T *>(v)[(int64_t)n * Hv * dv + e];
+  // 16 bytes per lane where both ends of a copy are 16-byte aligned (the usual case: whole
+  // rows of a contiguous tensor), element by element otherwise
+  auto copy = [&](void *dst_base, const void *src_base, int count) {
+    T *dst = static_cast<T *>(dst_base) + row * count;
+    const T *src = static_cast<const T *>(src_base) + (int64_t)n * count;
+    constexpr int V = 16 / sizeof(T);
+    if ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) % 16 == 0 &&
+        count % V == 0) {
+      for (int e = threadIdx.x; e < count / V; e += kThreads)
+        reinterpret_cast<uint4 *>(dst)[e] = reinterpret_cast<const uint4 *>(src)[e];
+    } else {
+      for (int e = threadIdx.x; e < count; e += kThreads) dst[e] = src[e];
+    }
+  };
+  copy(p.cache_k, k, Hk * dk);
+  copy(p.cache_v, v, Hv * dv);
   for (int e = threadIdx.x; e < Hv; e += kThreads) {
     p.cache_a[row * Hv + e] = a[(int64_t)n * Hv + e];
     p.cache_b[row * Hv + e] = b[(int64_t)n * Hv + e];
